@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant multi-sequence decode step on one MI355X.
+
+Headline (one JSON line on stdout): q8_0 narrow-batch GEMV throughput in GB/s
+over the 8B-class decode projections -- 32 layers of QKV 4096->6144, O
+4096->4096, gate|up 4096->2x14336 (one fused matrix), down 14336->4096, q8_0
+weights with fp16 scales uniform[1e-3, 1e-2], fp32 N(0,1) activations
+quantized per token -- at n_tok = 4.  A step is one sweep: per layer, quantize
+the projection input, then the GEMV, for all four projections (7.42 GB of
+weights, far beyond the 256 MB Infinity Cache).  The timed steps replay a HIP
+graph of the sweep, so the host's launch rate does not limit the GPU.  Inputs
+are resident in HBM before timing starts.
+
+Also reported: the same sweep at n_tok = 1..4, the dominant kernel's roofline
+(per-launch HIP-event durations of every GEMV in an eager pass of the same
+sweep), the aggregate tokens/s of the full synthetic decode step for 1..4
+sequences (plus the serial one-sequence-at-a-time baseline), and the CPU
+oracle's GEMV throughput on a bounded sample of the same matrices.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "q8_0 narrow-batch GEMV GB/s (%HBM peak) n_tok 1-4; aggregate decode tok/s"
+SHAPES = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
+N_LAYERS = 32
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(N, K, n_tok):
+    """Algorithmic bytes of one launch: weights once, q8 activations, fp32 outputs."""
+    return N * (K // 32) * 34 + n_tok * (K + 4 * (K // 32)) + 4 * n_tok * N
+
+
+class Sweep:
+    def __init__(self, sd, torch, seed, max_tok):
+        from sequence_decode_amd import synth
+        self.sd, self.torch = sd, torch
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.w = [{name: synth.torch_q8_0_weights(g, N, K, "cuda") for name, N, K in SHAPES}
+                  for _ in range(N_LAYERS)]
+        self.x = torch.randn((max_tok, 14336), dtype=torch.float32, device="cuda", generator=g)
+        self.xq = torch.empty((max_tok, 14336), dtype=torch.int8, device="cuda")
+        self.xd = torch.empty((max_tok, 14336 // 32), dtype=torch.float32, device="cuda")
+        self.y = {name: torch.empty((max_tok, N), dtype=torch.float32, device="cuda")
+                  for name, N, K in SHAPES}
+        self.weight_bytes = sum(N * (K // 32) * 34 for _, N, K in SHAPES) * N_LAYERS
+
+    def step(self, n_tok, events=None):
+        sd, lib = self.sd, self.sd._lib.load()
+        import ctypes
+        st = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        P = ctypes.c_void_p
+        xq, xd = self.xq, self.xd
+        for L in self.w:
+            for name, N, K in SHAPES:
+                rc = lib.sd_quantize_q8_act(P(self.x.data_ptr()), 14336, n_tok, K, P(xq.data_ptr()),
+                                            P(xd.data_ptr()), st)
+                if rc:
+                    raise sd.SdError("sd_quantize_q8_act", rc)
+                y = self.y[name]
+                if events is not None:
+                    e0 = self.torch.cuda.Event(enable_timing=True)
+                    e1 = self.torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                rc = lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()),
+                                             P(xd.data_ptr()), n_tok, None, P(y.data_ptr()), N, st)
+                if rc:
+                    raise sd.SdError("sd_qgemv_q8_0_batch", rc)
+                if events is not None:
+                    e1.record()
+                    events.append((name, N, K, e0, e1))
+
+    def bytes_per_step(self, n_tok):
+        return sum(gemv_bytes(N, K, n_tok) for _, N, K in SHAPES) * N_LAYERS
+
+
+def time_graph(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        fn()
+        g.capture_end()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del g
+    return dt / steps
+
+
+def roofline_pass(torch, sweep, n_tok, reps):
+    ev = []
+    for _ in range(reps):
+        sweep.step(n_tok, events=ev)
+    torch.cuda.synchronize()
+    tot_ms = 0.0
+    tot_bytes = 0
+    per = {}
+    for name, N, K, e0, e1 in ev:
+        ms = e0.elapsed_time(e1)
+        tot_ms += ms
+        b = gemv_bytes(N, K, n_tok)
+        tot_bytes += b
+        d = per.setdefault(name, [0.0, 0, 0])
+        d[0] += ms
+        d[1] += b
+        d[2] += 1
+    return tot_bytes, tot_ms, len(ev), per
+
+
+def cpu_baseline(torch, sweep, n_tok, budget_s):
+    import numpy as np
+    import oracle
+    xq = sweep.xq[:n_tok].cpu().numpy()
+    xd = sweep.xd[:n_tok].cpu().numpy()
+    done_bytes, t_used, layers = 0, 0.0, 0
+    x = sweep.x[:n_tok].cpu().numpy()
+    for L in sweep.w:
+        for name, N, K in SHAPES:
+            w = L[name].cpu().numpy()
+            q, d = oracle.quantize_q8_act(x[:, :K])
+            t0 = time.perf_counter()
+            oracle.qgemv_q8_0(w, N, K, q, d)
+            t_used += time.perf_counter() - t0
+            done_bytes += gemv_bytes(N, K, n_tok)
+        layers += 1
+        if t_used >= budget_s:
+            break
+    del xq, xd
+    return {"value": round(done_bytes / t_used / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{layers} of 32 layers (4 projections each) at n_tok={n_tok}, "
+                      f"{done_bytes / 1e9:.2f} GB of weights, {t_used:.1f} s"}
+
+
+def decode_bench(torch, steps, warmup):
+    """Aggregate tok/s of the full step (sd_decode_step) for 1..4 sequences."""
+    from sequence_decode_amd.step import DecodeModel, SeqCache, StepRunner
+    dims = dict(n_layers=32, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=14336,
+                vocab=151936, eps=1e-6, theta=1e6)
+    model = DecodeModel.random_device(11, dims)
+    ragged = [2050, 3072, 16384, 32768]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    span = warmup + steps + 1
+    caches = [SeqCache.random_device(g, 32, ctx + span, 8, 128) for ctx in ragged]
+    out = {"model": "random-init dense 32-layer, hidden 4096, 32/8 heads, ffn 14336, "
+                    "vocab 151936, q8_0 weights, fp16 KV",
+           "weight_bytes": model.weight_bytes}
+    res = {}
+    for label, ctxs in (("ragged", ragged), ("ctx2050", [2050] * 4)):
+        for n in (1, 2, 3, 4):
+            r = StepRunner(model, caches[:n], max_ctx=max(ctxs[:n]) + span)
+            r.tokens.copy_(torch.arange(n, dtype=torch.int32) + 7)
+            r.set_positions([c - 1 for c in ctxs[:n]])
+            for _ in range(warmup):
+                r.step()
+                r.advance()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                r.step()
+                r.advance()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / steps
+            res[f"{label}_n{n}"] = {"tok_s": round(n / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
+            log(f"decode {label} n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
+    # serial baseline: the four ragged sequences one at a time (one-token steps back to back)
+    runners = [StepRunner(model, [caches[s]], max_ctx=ragged[s] + span) for s in range(4)]
+    for s in range(4):
+        runners[s].set_positions([ragged[s] - 1])
+    for _ in range(2):
+        for s in range(4):
+            runners[s].step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for s in range(4):
+            runners[s].step()
+            runners[s].advance()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    res["serial_ragged_n4"] = {"tok_s": round(4 / dt, 2), "ms_per_round": round(dt * 1e3, 3)}
+    log(f"decode serial 4 sequences: {4 / dt:.1f} tok/s")
+    out["results"] = res
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--n-tok", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode step here is built and measured on a "
+              "single MI355X; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sequence_decode_amd as sd
+    sd.load()
+    torch.cuda.set_device(0)
+    log("generating 7.42 GB of q8_0 projection weights on the device")
+    sweep = Sweep(sd, torch, seed=1, max_tok=16)
+    torch.cuda.synchronize()
+
+    per_n = {}
+    for n in (1, 2, 3, 4):
+        dt = time_graph(torch, lambda: sweep.step(n), max(3, args.steps // 2), 2)
+        gbs = sweep.bytes_per_step(n) / dt / 1e9
+        per_n[str(n)] = {"GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                         "ms_per_step": round(dt * 1e3, 4)}
+        log(f"sweep n_tok={n}: {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s), "
+            f"{dt * 1e3:.3f} ms")
+
+    n = args.n_tok
+    dt = time_graph(torch, lambda: sweep.step(n), args.steps, args.warmup)
+    value = sweep.bytes_per_step(n) / dt / 1e9
+
+    tb, tms, launches, per = roofline_pass(torch, sweep, n, reps=2)
+    achieved = tb / (tms / 1e3) / 1e9
+    per_shape = {k: {"GB_s": round(v[1] / (v[0] / 1e3) / 1e9, 1),
+                     "avg_us": round(v[0] / v[2] * 1e3, 3)} for k, v in per.items()}
+    log(f"GEMV kernel (event-timed, {launches} launches): {achieved:.1f} GB/s; {per_shape}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "8B-class q8_0 decode projections, 32 layers x (QKV 6144x4096, "
+                               "O 4096x4096, gate|up 28672x4096, down 4096x14336)",
+                   "n_tok": n, "layers": N_LAYERS, "weight_bytes": sweep.weight_bytes,
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "per_n_tok": per_n,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_qgemv_q8_0", "launches": launches,
+                     "avg_launch_us": round(tms / launches * 1e3, 3), "per_shape": per_shape},
+    }
+    line["decode_step"] = None
+    if not args.no_decode:
+        line["decode_step"] = decode_bench(torch, steps=max(8, args.steps), warmup=args.warmup)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(torch, sweep, n, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

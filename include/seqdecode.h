@@ -1,0 +1,291 @@
+/*
+ * seqdecode.h -- C ABI of the exact, batch-invariant multi-sequence decode step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point enqueues HIP kernels on the caller's stream and returns
+ * without synchronizing.  Pointers are DEVICE pointers unless marked [host].
+ * The caller owns every buffer; the library allocates no device memory and
+ * keeps no state between calls, so concurrent calls on different streams are
+ * independent.
+ *
+ * Errors: arguments are validated on the host before any HIP call.  On failure
+ * a negative sd_status is returned, nothing is launched and no output is
+ * written.  SD_EHIP reports a launch error from the HIP runtime.
+ *
+ * Batch invariance: for every entry point, the bits of the output for token
+ * (or sequence) t depend only on t's own inputs, never on how many other rows
+ * are in the call or where t sits among them.  This is the property the
+ * "feat(qwen4exp): exact 4-slot concurrent serving" page demands in "How it
+ * stays exact" (a batch uses the same kernels and arithmetic as a single row),
+ * and that ds4 pull request 604 does not reach ("Correctness notes and
+ * limitations": its fused pass differs from serial decode by reduction order).
+ *
+ * Page citations below name the page and the section on it.
+ */
+#ifndef SEQDECODE_H
+#define SEQDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sd_stream_t; /* a hipStream_t; NULL = legacy default stream */
+
+typedef enum sd_status {
+  SD_OK = 0,
+  SD_EINVAL = -1,       /* a size, count or pointer is out of range or NULL */
+  SD_EUNSUPPORTED = -2, /* a shape this build does not implement */
+  SD_EALIGN = -3,       /* a pointer or stride breaks the stated alignment */
+  SD_EWORKSPACE = -4,   /* the workspace is smaller than the query returned */
+  SD_EHIP = -5          /* the HIP runtime rejected a launch */
+} sd_status;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* sd_status_string(int status);
+
+/* ABI revision of this header; bumps on any signature change. */
+#define SD_ABI_VERSION 1
+int sd_abi_version(void);
+
+/* Largest batch of token rows a GEMV call takes (speculative-verify width, see
+ * "#1209 Speed up concurrent generation, fix QFUSE, and improve prefill
+ * monitoring", "What changed and why" item 1: 8/12/16-row capacities). */
+#define SD_MAX_TOKENS 16
+/* Largest number of sequences one attention call takes: ds4 pull request 604,
+ * "Commit walkthrough / CUDA kernels" (per-sequence views passed by value,
+ * max 4); "feat(qwen4exp): exact 4-slot concurrent serving", "What" (more than
+ * four is refused). */
+#define SD_MAX_SEQS 4
+/* Keys per attention chunk.  Fixed, so a sequence's split depends on its own
+ * length only. */
+#define SD_ATTN_CHUNK 256
+
+/* ------------------------------------------------------------------ q8 data
+ * q8_0 weight matrix: N rows, each of K/32 consecutive 34-byte blocks; a block
+ * is a little-endian fp16 scale d_w followed by 32 int8 weights (the 32-weight
+ * block of ds4 pull request 604, "Commit walkthrough / CUDA kernels").
+ * q8 activations: per token, K int8 codes (row stride K) and K/32 fp32 block
+ * scales (row stride K/32).
+ */
+
+/*
+ * sd_quantize_q8_act -- fp32 rows -> q8 activation blocks.
+ * For each token t < n_tok and block b < K/32: amax = max|x|, d = amax/127 in
+ * fp32 (IEEE division), code = roundf(x/d) (fp32 division, ties away from
+ * zero) clamped to [-127, 127]; all codes 0 when d == 0.  This is the division
+ * and rounding convention every fused producer in this library also uses (the
+ * QFUSE lesson of "#1209 ...", "What changed and why" item 2).
+ *   x   [n_tok][ldx] fp32, 4-byte aligned; ldx >= K.
+ *   xq  [n_tok][K] int8, 16-byte aligned.   xd [n_tok][K/32] fp32.
+ * Requires 1 <= n_tok <= SD_MAX_TOKENS, K > 0, K % 32 == 0.  Inputs must be
+ * finite (non-finite inputs give unspecified codes).
+ */
+int sd_quantize_q8_act(const float* x, int64_t ldx, int n_tok, int64_t K,
+                       int8_t* xq, float* xd, sd_stream_t stream);
+
+/*
+ * sd_qgemv_q8_0_batch -- narrow-batch q8_0 matrix-vector product (ds4 pull
+ * request 604, "Commit walkthrough / CUDA kernels": each 32-weight block is
+ * read once and dotted against every token row).
+ *   y[t][n] = (residual ? residual[t][n] : 0) + sum_b s_b,
+ *   s_b = fl32(fl32(d_w[n][b] * xd[t][b]) * (float) sum_i w[n][b][i]*xq[t][b*32+i])
+ * The block sums are exact int32; the fp32 sum over b uses one fixed order
+ * that depends on K only, so y[t] is bitwise the same for any n_tok and any
+ * row order.
+ *   w         N*(K/32)*34 bytes, 16-byte aligned.
+ *   xq, xd    q8 activations of n_tok tokens (layout above); xq 16-byte aligned.
+ *   residual  NULL or [n_tok][ldy] fp32; may equal y (in-place accumulate).
+ *   y         [n_tok][ldy] fp32, ldy >= N.
+ * Requires N >= 1, K % 256 == 0 (rows then start 16-byte aligned),
+ * 1 <= n_tok <= SD_MAX_TOKENS, and n_tok * K * 1.25 bytes <= 144 KiB
+ * (activations staged in LDS); otherwise SD_EUNSUPPORTED / SD_EINVAL.
+ */
+int sd_qgemv_q8_0_batch(const void* w, int64_t N, int64_t K,
+                        const int8_t* xq, const float* xd, int n_tok,
+                        const float* residual, float* y, int64_t ldy,
+                        sd_stream_t stream);
+
+/* ------------------------------------------------------------------ RoPE
+ * sd_rope_posvec -- rotary embedding with one position per token (ds4 pull
+ * request 604, "Commit walkthrough / CUDA kernels": pos-vector RoPE; token t
+ * gives bitwise what a single-token call at pos[t] gives).
+ * In place on x[t][h][:] (token stride ld_tok, head stride ld_head, in
+ * elements).  The last n_rot dimensions of each head are rotated: with
+ * off = head_dim - n_rot and half = n_rot/2, the pair (off+i, off+i+half) turns
+ * by pos[t] * theta^(-2i/n_rot).  Angle, sine and cosine are computed in fp64
+ * and rounded to fp32; the rotation is fp32.
+ *   pos [n_tok] int32 >= 0 (device).
+ * Requires 1 <= n_tok <= 4096, n_heads >= 1, n_rot even, 2 <= n_rot <= head_dim
+ * <= 512, theta > 0.
+ */
+int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
+                   int64_t ld_tok, int64_t ld_head, const int32_t* pos,
+                   double theta, int n_rot, sd_stream_t stream);
+
+/* --------------------------------------------------- per-sequence KV views
+ * One sequence's fp16 key and value caches (bit patterns), element (j, g, d) at
+ * base[j*ld_tok + g*ld_head + d] (elements).  The struct array is [host] memory;
+ * kernels receive the views by value in their arguments (ds4 pull request 604,
+ * "Commit walkthrough / CUDA kernels").  ctx_len counts every key in use,
+ * including the current token's (its position is ctx_len - 1).
+ */
+typedef struct sd_seqview {
+  uint16_t* k;
+  uint16_t* v;
+  int32_t ctx_len;
+  int32_t capacity;
+  int64_t ld_tok;
+  int64_t ld_head;
+} sd_seqview;
+
+/*
+ * sd_kv_append_f16 -- write the current token's key and value rows.
+ * For sequence s: row ctx_len_s - 1 of views[s] receives fp16(k_new[s]) and
+ * fp16(v_new[s]) (round to nearest even); no other row is touched (ds4 pull
+ * request 604, "2. Single-GPU decode batches don't scale": the append runs per
+ * sequence).
+ *   k_new, v_new  [n_seq][H_kv][D] fp32 at sequence stride ld_new (elements).
+ *   views         [host] n_seq views; 4-byte aligned bases, even strides.
+ * Requires 1 <= n_seq <= SD_MAX_SEQS, 1 <= ctx_len <= capacity, D even.
+ */
+int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
+                     const sd_seqview* views, int n_seq, int H_kv, int D,
+                     sd_stream_t stream);
+
+/*
+ * sd_decode_attn_workspace_bytes -- workspace size sd_decode_attn_multiseq
+ * needs for these views (0 on invalid arguments).
+ */
+size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_q, int D);
+
+/*
+ * sd_decode_attn_multiseq -- one query token per sequence over that sequence's
+ * own cache, all sequences in one launch (ds4 pull request 604, "Commit
+ * walkthrough / CUDA kernels": multi-sequence decode attention).
+ * For sequence s and query head h (KV head g = h / (H_q/H_kv)):
+ *   out[s][h] = sum_j softmax_j(scale * q[s][h] . k_j) v_j,  j < ctx_len_s.
+ * fp32 throughout (online softmax over fixed SD_ATTN_CHUNK-key chunks, merged
+ * in chunk order), so a sequence's bits do not depend on the others.
+ *   q    [n_seq][H_q][D] fp32 at sequence stride ld_q (elements), 16-byte aligned.
+ *   out  [n_seq][H_q][D] fp32 contiguous, 16-byte aligned.
+ *   ws   workspace of at least sd_decode_attn_workspace_bytes(), 16-byte aligned.
+ *   views [host]: 16-byte aligned bases, ld_tok and ld_head multiples of 8.
+ * Requires 1 <= n_seq <= SD_MAX_SEQS, D == 128, H_q % H_kv == 0,
+ * H_q / H_kv == 4 (grouped-query attention with four query heads per KV head),
+ * 1 <= ctx_len <= capacity.
+ */
+int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
+                            int n_seq, int H_q, int H_kv, int D, float scale,
+                            float* out, void* ws, size_t ws_bytes, sd_stream_t stream);
+
+/* ------------------------------------------------------------ step glue
+ * Pieces of the fused decode step (ds4 pull request 604, "2. Single-GPU
+ * decode batches don't scale" and "Commit walkthrough / Graph driver").
+ */
+
+/*
+ * sd_rmsnorm_q8 -- y = x / sqrt(mean(x^2) + eps) * gamma per row (fp32, fixed
+ * reduction order), quantized to q8 activation blocks exactly as
+ * sd_quantize_q8_act would quantize y.
+ *   x [n_tok][ldx] fp32; gamma [D] fp32; xq [n_tok][D]; xd [n_tok][D/32];
+ *   y NULL or [n_tok][D] fp32 (the normalized row before quantization).
+ * Requires 1 <= n_tok <= SD_MAX_TOKENS, D % 32 == 0, 32 <= D <= 32768.
+ */
+int sd_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D, const float* gamma,
+                  float eps, int8_t* xq, float* xd, float* y, sd_stream_t stream);
+
+/*
+ * sd_swiglu_q8 -- m = silu(g) * u with g = gu[t][0..F), u = gu[t][F..2F),
+ * silu(g) = g / (1 + exp(-g)) in fp32, quantized to q8 blocks (as above).
+ *   gu [n_tok][ldgu] fp32, ldgu >= 2F; xq [n_tok][F]; xd [n_tok][F/32];
+ *   y NULL or [n_tok][F] fp32.
+ * Requires 1 <= n_tok <= SD_MAX_TOKENS, F % 32 == 0.
+ */
+int sd_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F,
+                 int8_t* xq, float* xd, float* y, sd_stream_t stream);
+
+/*
+ * sd_embed_f16 -- x[t][:] = fp32(table[tokens[t]][:]) (exact widening).
+ *   table [V][H] fp16 bits; tokens [n_tok] int32 in [0, V) (device; out-of-range
+ *   ids are clamped to V-1); x [n_tok][H] fp32.
+ */
+int sd_embed_f16(const uint16_t* table, int64_t V, int64_t H, const int32_t* tokens,
+                 int n_tok, float* x, sd_stream_t stream);
+
+/*
+ * sd_argmax_rows -- greedy next token per row: the lowest index among equal
+ * maxima of logits[t][0..V).  NaN never wins.
+ *   logits [n_tok][ld] fp32; out [n_tok] int32.
+ */
+int sd_argmax_rows(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
+                   sd_stream_t stream);
+
+/* ------------------------------------------------------- the decode step */
+
+/* One decoder layer's weights (device pointers). */
+typedef struct sd_layer_weights {
+  const void* w_qkv;      /* q8_0 [(H_q + 2 H_kv) D][hidden]: q rows, k rows, v rows */
+  const void* w_o;        /* q8_0 [hidden][H_q D] */
+  const void* w_gate_up;  /* q8_0 [2 ffn][hidden]: gate rows, then up rows */
+  const void* w_down;     /* q8_0 [hidden][ffn] */
+  const float* attn_norm; /* [hidden] */
+  const float* ffn_norm;  /* [hidden] */
+} sd_layer_weights;
+
+/* A dense decoder model (shapes and pointers). */
+typedef struct sd_model {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rms_eps;
+  double rope_theta;
+  const uint16_t* tok_embd;        /* fp16 bits [vocab][hidden] */
+  const float* out_norm;           /* [hidden] */
+  const void* w_lm_head;           /* q8_0 [vocab][hidden] */
+  const sd_layer_weights* layers;  /* [host] n_layers entries */
+} sd_model;
+
+/* One sequence's state for a step: caches [n_layers][capacity][H_kv][D] fp16. */
+typedef struct sd_step_seq {
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t capacity;
+  int32_t pos;        /* position of this step's token; ctx_len = pos + 1 */
+} sd_step_seq;
+
+/* Inputs and outputs of one step. */
+typedef struct sd_step_io {
+  int32_t n_seq;
+  const sd_step_seq* seqs;   /* [host] n_seq entries */
+  const int32_t* tokens;     /* [n_seq] input token per sequence */
+  const int32_t* positions;  /* [n_seq] equal to seqs[s].pos */
+  float* logits;             /* [n_seq][vocab] */
+  int32_t* next_tokens;      /* [n_seq] greedy argmax of logits */
+  void* ws;                  /* workspace, 256-byte aligned */
+  size_t ws_bytes;
+} sd_step_io;
+
+/* Workspace bytes sd_decode_step needs for n_seq sequences whose contexts
+ * are at most max_ctx keys (0 on invalid arguments). */
+size_t sd_decode_step_workspace_bytes(const sd_model* m, int n_seq, int max_ctx);
+
+/*
+ * sd_decode_step -- one batched decode step for n_seq sequences: embedding,
+ * n_layers x (rmsnorm, QKV projection, pos-vector RoPE, KV append, multi-
+ * sequence attention, O projection + residual, rmsnorm, gate/up projection,
+ * SwiGLU, down projection + residual), final rmsnorm, LM head, argmax.  The
+ * projections run once for all sequences (ds4 pull request 604, "2. Single-GPU
+ * decode batches don't scale").  Every sequence's logits and token are bitwise
+ * those of a step with that sequence alone.
+ * Requires 1 <= n_seq <= SD_MAX_SEQS, head_dim == 128, n_heads == 4*n_kv_heads,
+ * hidden % 256 == 0, ffn % 256 == 0, n_heads*head_dim % 256 == 0,
+ * 0 <= pos < capacity.
+ */
+int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEQDECODE_H */

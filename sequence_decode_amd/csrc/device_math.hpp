@@ -1,0 +1,77 @@
+// device_math.hpp -- device helpers with a fixed operation order.
+//
+// Every floating-point operation that decides output bits goes through one of
+// the helpers below, each a single IEEE operation that the compiler may not
+// contract into a fused multiply-add (the pragma holds whatever the build
+// flags say).  A row is therefore rounded the same way in every template
+// instantiation, whatever the batch size.  fp32 division and square root are
+// the correctly rounded ones (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+__device__ __forceinline__ float fadd(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+__device__ __forceinline__ float fsub(float a, float b) {
+#pragma clang fp contract(off)
+  return a - b;
+}
+__device__ __forceinline__ float fmul(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float fdiv(float a, float b) {
+#pragma clang fp contract(off)
+  return a / b;
+}
+__device__ __forceinline__ float ffma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4), aligned(16)));
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
+  return (float)h;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Sum over the 64 lanes of a wave with a fixed butterfly (xor 32, 16, ..., 1).
+// Floating-point addition is commutative, so every lane ends with the same
+// bits, and the tree depends on nothing but the lane index.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fadd(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Maximum over a contiguous group of `width` lanes (exact and order-free).
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = width / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// q8 activation code of x for block scale d (the library-wide convention):
+// IEEE fp32 division, round half away from zero, clamp to [-127, 127].
+__device__ __forceinline__ int q8_code(float x, float d) {
+  if (d == 0.0f) return 0;
+  float r = roundf(fdiv(x, d));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ float q8_scale(float amax) { return fdiv(amax, 127.0f); }
+
+}  // namespace sd

@@ -1,0 +1,176 @@
+// glue.hip -- activation quantizer and the small per-token kernels of the step.
+//
+// The quantizer convention (fp32 d = amax/127, codes = roundf(x/d) clamped to
+// +-127) is shared by every producer here, as "#1209 Speed up concurrent
+// generation, fix QFUSE, and improve prefill monitoring" ("What changed and
+// why", item 2) requires of a fused quantizer: it must reproduce the consuming
+// quantizer's division and rounding exactly.  Blocks of 32 values map to 32
+// consecutive lanes, so the block maximum is a 5-step lane reduction.
+#include <math.h>
+
+#include "device_math.hpp"
+#include "internal.hpp"
+
+namespace sd {
+
+namespace {
+
+// Quantizes one value per lane; lanes 32k..32k+31 hold one block.  Every lane
+// of the wave must call this (the maximum uses cross-lane moves).
+__device__ __forceinline__ void quantize_lane(float v, bool valid, int8_t* q_out, float* d_out,
+                                              int lane32) {
+  const float amax = group_max<32>(valid ? fabsf(v) : 0.0f);
+  const float d = q8_scale(amax);
+  if (valid) {
+    *q_out = (int8_t)q8_code(v, d);
+    if (lane32 == 0) *d_out = d;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x, int64_t ldx,
+                                                     int n_tok, int64_t K, int8_t* __restrict__ xq,
+                                                     float* __restrict__ xd) {
+  const int64_t nb = K / 32;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t blk = gid >> 5;
+  const int lane32 = threadIdx.x & 31;
+  const bool valid = blk < (int64_t)n_tok * nb;
+  const int64_t t = valid ? blk / nb : 0;
+  const int64_t b = valid ? blk - t * nb : 0;
+  const float v = valid ? x[t * ldx + b * 32 + lane32] : 0.0f;
+  quantize_lane(v, valid, xq + t * K + b * 32 + lane32, xd + t * nb + b, lane32);
+}
+
+// One workgroup per token row.  The sum of squares is accumulated per thread
+// over a fixed stride, then combined by fixed wave and workgroup trees.
+__global__ __launch_bounds__(256) void k_rmsnorm_q8(const float* __restrict__ x, int64_t ldx,
+                                                    int64_t D, const float* __restrict__ gamma,
+                                                    float eps, int8_t* __restrict__ xq,
+                                                    float* __restrict__ xd, float* y) {
+  __shared__ float part[4];
+  const int t = blockIdx.x;
+  const float* xr = x + (int64_t)t * ldx;
+  float ss = 0.0f;
+  for (int64_t i = threadIdx.x; i < D; i += 256) {
+    const float v = xr[i];
+    ss = fadd(ss, fmul(v, v));
+  }
+  ss = wave_sum_fixed(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float total = fadd(fadd(part[0], part[1]), fadd(part[2], part[3]));
+  const float r = fdiv(1.0f, sqrtf(fadd(fdiv(total, (float)D), eps)));
+  const int64_t nb = D / 32;
+  for (int64_t base = 0; base < D; base += 256) {
+    const int64_t i = base + threadIdx.x;
+    const bool valid = i < D;
+    const float v = valid ? fmul(fmul(xr[i], r), gamma[i]) : 0.0f;
+    if (valid && y) y[(int64_t)t * D + i] = v;
+    quantize_lane(v, valid, xq + (int64_t)t * D + i, xd + (int64_t)t * nb + (i >> 5),
+                  threadIdx.x & 31);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu, int64_t ldgu,
+                                                   int n_tok, int64_t F, int8_t* __restrict__ xq,
+                                                   float* __restrict__ xd, float* y) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = gid < (int64_t)n_tok * F;
+  const int64_t t = valid ? gid / F : 0;
+  const int64_t i = valid ? gid - t * F : 0;
+  float m = 0.0f;
+  if (valid) {
+    const float g = gu[t * ldgu + i];
+    const float u = gu[t * ldgu + F + i];
+    const float silu = fdiv(g, fadd(1.0f, expf(-g)));
+    m = fmul(silu, u);
+    if (y) y[t * F + i] = m;
+  }
+  quantize_lane(m, valid, xq + t * F + i, xd + t * (F / 32) + (i >> 5), threadIdx.x & 31);
+}
+
+__global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ table, int64_t V,
+                                               int64_t H, const int32_t* __restrict__ tokens,
+                                               float* __restrict__ x) {
+  const int t = blockIdx.y;
+  int64_t tok = tokens[t];
+  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < H; i += (int64_t)gridDim.x * 256)
+    x[(int64_t)t * H + i] = f16_bits_to_f32(table[tok * H + i]);
+}
+
+// (value, index) selection: larger value wins, equal values go to the lower
+// index, NaN never wins.  It is a total order on candidates, so any reduction
+// tree gives the same winner.
+__device__ __forceinline__ void better(float& v, int32_t& i, float ov, int32_t oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int64_t ld,
+                                                int64_t V, int32_t* __restrict__ out) {
+  __shared__ float sv[4];
+  __shared__ int32_t si[4];
+  const int t = blockIdx.x;
+  const float* row = logits + (int64_t)t * ld;
+  float bv = -INFINITY;
+  int32_t bi = (int32_t)V;
+  for (int64_t j = threadIdx.x; j < V; j += 256) better(bv, bi, row[j], (int32_t)j);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int32_t oi = __shfl_xor(bi, m, 64);
+    better(bv, bi, ov, oi);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = bv;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = sv[0];
+    int32_t i = si[0];
+    for (int w = 1; w < 4; ++w) better(v, i, sv[w], si[w]);
+    out[t] = i >= V ? 0 : i;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K, int8_t* xq,
+                              float* xd, hipStream_t st) {
+  const int64_t threads = (int64_t)n_tok * K;  // one lane per value
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_quantize_q8, dim3((unsigned)grid), dim3(256), 0, st, x, ldx, n_tok, K, xq, xd);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D, const float* gamma,
+                             float eps, int8_t* xq, float* xd, float* y, hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm_q8, dim3(n_tok), dim3(256), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F, int8_t* xq,
+                            float* xd, float* y, hipStream_t st) {
+  const int64_t grid = ((int64_t)n_tok * F + 255) / 256;
+  hipLaunchKernelGGL(k_swiglu_q8, dim3((unsigned)grid), dim3(256), 0, st, gu, ldgu, n_tok, F, xq, xd, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const uint16_t* table, int64_t V, int64_t H, const int32_t* tokens, int n_tok,
+                        float* x, hipStream_t st) {
+  const int64_t gx = (H + 255) / 256 < 64 ? (H + 255) / 256 : 64;
+  hipLaunchKernelGGL(k_embed, dim3((unsigned)gx, n_tok), dim3(256), 0, st, table, V, H, tokens, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax, dim3(n_tok), dim3(256), 0, st, logits, ld, V, out);
+  return hipGetLastError();
+}
+
+}  // namespace sd

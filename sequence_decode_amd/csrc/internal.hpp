@@ -1,0 +1,90 @@
+// internal.hpp -- declarations shared by the HIP kernels and the C-ABI layer.
+// Not part of the public interface (include/seqdecode.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "seqdecode.h"
+
+namespace sd {
+
+// ---------------------------------------------------------------- constants
+constexpr int kBlock = 32;          // weights / codes per q8 block
+constexpr int kBlockBytes = 34;     // fp16 scale + 32 int8
+constexpr int kPairBytes = 68;      // two consecutive blocks; a pair starts 4-byte aligned
+constexpr int kPairDw = 17;         // dwords per pair
+constexpr int kActDw = 20;          // dwords per pair in the LDS activation layout
+constexpr int kGemvThreads = 256;   // four wave64 per workgroup
+constexpr int kGemvLdsMax = 144 * 1024;
+constexpr int kAttnChunk = SD_ATTN_CHUNK;
+constexpr int kAttnHeadDim = 128;
+constexpr int kAttnGroup = 4;       // query heads per KV head handled by one workgroup
+constexpr int kAttnPartialFloats = 132;  // m, l, 2 pad, o[128]
+
+// Per-sequence view as passed by value to the attention / append kernels.
+struct SeqArg {
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* k_w;
+  uint16_t* v_w;
+  int64_t ld_tok;
+  int64_t ld_head;
+  int32_t ctx_len;
+  int32_t n_chunks;
+  int32_t unit_begin;     // first workgroup index of this sequence
+  int32_t partial_begin;  // first partial slot of this sequence (per head: n_chunks slots)
+};
+
+struct SeqArgs {
+  SeqArg s[SD_MAX_SEQS];
+  int32_t n_seq;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already validated.
+hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
+                              int8_t* xq, float* xd, hipStream_t st);
+
+// GEMV launch geometry for (N, K, n_tok): lds bytes and slice layout.
+struct GemvPlan {
+  int pairs;         // K / 64
+  int slice_pairs;   // pairs staged per LDS slice (multiple of 64, or all)
+  int n_slices;
+  size_t lds_bytes;
+  int rows_per_wave;
+  int grid;
+};
+bool plan_qgemv(int64_t N, int64_t K, int n_tok, GemvPlan* plan);
+hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
+                        int n_tok, const float* residual, float* y, int64_t ldy, hipStream_t st);
+
+hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok,
+                              int64_t ld_head, const int32_t* pos, double theta, int n_rot,
+                              hipStream_t st);
+hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_new,
+                            const SeqArgs& seqs, int H_kv, int D, hipStream_t st);
+// Fused step helper: rotates q (n_heads) and k (n_kv) rows of qkv in place and
+// writes rotated k and v into each sequence's cache row pos = ctx_len - 1.
+hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads, int n_kv, int head_dim,
+                               const int32_t* pos, double theta, const SeqArgs& seqs,
+                               hipStream_t st);
+
+// Fills per-sequence chunk bookkeeping; returns workspace floats needed.
+size_t attn_layout(SeqArgs* seqs, int H_q, int H_kv);
+hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_q, int H_kv,
+                       float scale, float* out, float* partials, int8_t* oq, float* od,
+                       hipStream_t st);
+
+hipError_t launch_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D,
+                             const float* gamma, float eps, int8_t* xq, float* xd, float* y,
+                             hipStream_t st);
+hipError_t launch_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F, int8_t* xq,
+                            float* xd, float* y, hipStream_t st);
+hipError_t launch_embed(const uint16_t* table, int64_t V, int64_t H, const int32_t* tokens,
+                        int n_tok, float* x, hipStream_t st);
+hipError_t launch_argmax(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
+                         hipStream_t st);
+
+}  // namespace sd

@@ -1,0 +1,139 @@
+// rope_kv.hip -- pos-vector RoPE and the per-sequence KV-cache append.
+//
+// RoPE with one position per token: ds4 pull request 604, "Commit walkthrough
+// / CUDA kernels" (decode tokens of different sequences sit at arbitrary
+// positions; the per-element math is that of the single-token kernel, so token
+// t equals a single-token launch at pos[t] bitwise).  Here every element's
+// result depends on (x pair, pos[t], i, theta, n_rot) only, so the property
+// holds by construction.  The angle pos * theta^(-2i/n_rot) and its sine and
+// cosine are taken in fp64: at positions near 32K an fp32 angle would already
+// be off by ~1e-3 rad.  The rotation itself is four fp32 products and two
+// sums, unfused.
+//
+// KV append: ds4 pull request 604, "2. Single-GPU decode batches don't scale"
+// (the append runs per sequence with the single-token helpers); each sequence
+// writes its own row ctx_len - 1.
+#include <math.h>
+
+#include "device_math.hpp"
+#include "internal.hpp"
+
+namespace sd {
+
+namespace {
+
+__device__ __forceinline__ void rope_angle(int pos, int i, int n_rot, double theta, float* c,
+                                           float* s) {
+  const double inv_freq = pow(theta, (double)(-2 * i) / (double)n_rot);
+  const double a = (double)pos * inv_freq;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+__device__ __forceinline__ void rotate(float x0, float x1, float c, float s, float* y0, float* y1) {
+  *y0 = fsub(fmul(x0, c), fmul(x1, s));
+  *y1 = fadd(fmul(x0, s), fmul(x1, c));
+}
+
+// Grid (n_tok * n_heads); threads loop over the n_rot/2 pairs of one head.
+__global__ __launch_bounds__(128) void k_rope_posvec(float* x, int n_heads, int head_dim,
+                                                     int64_t ld_tok, int64_t ld_head,
+                                                     const int32_t* __restrict__ pos,
+                                                     double theta, int n_rot) {
+  const int t = blockIdx.x / n_heads;
+  const int h = blockIdx.x - t * n_heads;
+  const int half = n_rot / 2;
+  const int p = pos[t];
+  float* v = x + (int64_t)t * ld_tok + (int64_t)h * ld_head + (head_dim - n_rot);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    float c, s, y0, y1;
+    rope_angle(p, i, n_rot, theta, &c, &s);
+    rotate(v[i], v[i + half], c, s, &y0, &y1);
+    v[i] = y0;
+    v[i + half] = y1;
+  }
+}
+
+// Grid (n_seq, H_kv); one thread per element pair of a head.
+__global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ k_new,
+                                                   const float* __restrict__ v_new,
+                                                   int64_t ld_new, SeqArgs seqs, int H_kv, int D) {
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const SeqArg& a = seqs.s[s];
+  const int64_t row = (int64_t)(a.ctx_len - 1) * a.ld_tok + (int64_t)g * a.ld_head;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const int64_t src = (int64_t)s * ld_new + (int64_t)g * D + d;
+    a.k_w[row + d] = f32_to_f16_bits(k_new[src]);
+    a.v_w[row + d] = f32_to_f16_bits(v_new[src]);
+  }
+}
+
+// Fused step helper.  Workgroup (t, h) for h < n_heads rotates query head h of
+// token t in place; for n_heads <= h < n_heads + n_kv it rotates key head
+// g = h - n_heads and writes it, with value head g, into sequence t's cache.
+__global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads,
+                                                     int n_kv, int head_dim,
+                                                     const int32_t* __restrict__ pos,
+                                                     double theta, SeqArgs seqs) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int half = head_dim / 2;
+  const int p = pos[t];
+  float* row = qkv + (int64_t)t * ld_qkv;
+  if (h < n_heads) {
+    float* v = row + (int64_t)h * head_dim;
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+      float c, s, y0, y1;
+      rope_angle(p, i, head_dim, theta, &c, &s);
+      rotate(v[i], v[i + half], c, s, &y0, &y1);
+      v[i] = y0;
+      v[i + half] = y1;
+    }
+  } else {
+    const int g = h - n_heads;
+    const float* kh = row + (int64_t)(n_heads + g) * head_dim;
+    const float* vh = row + (int64_t)(n_heads + n_kv + g) * head_dim;
+    const SeqArg& a = seqs.s[t];
+    const int64_t dst = (int64_t)(a.ctx_len - 1) * a.ld_tok + (int64_t)g * a.ld_head;
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+      float c, s, y0, y1;
+      rope_angle(p, i, head_dim, theta, &c, &s);
+      rotate(kh[i], kh[i + half], c, s, &y0, &y1);
+      a.k_w[dst + i] = f32_to_f16_bits(y0);
+      a.k_w[dst + i + half] = f32_to_f16_bits(y1);
+      a.v_w[dst + i] = f32_to_f16_bits(vh[i]);
+      a.v_w[dst + i + half] = f32_to_f16_bits(vh[i + half]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok,
+                              int64_t ld_head, const int32_t* pos, double theta, int n_rot,
+                              hipStream_t st) {
+  const int threads = n_rot / 2 < 128 ? ((n_rot / 2 + 63) / 64) * 64 : 128;
+  hipLaunchKernelGGL(k_rope_posvec, dim3(n_tok * n_heads), dim3(threads), 0, st, x, n_heads,
+                     head_dim, ld_tok, ld_head, pos, theta, n_rot);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_new,
+                            const SeqArgs& seqs, int H_kv, int D, hipStream_t st) {
+  hipLaunchKernelGGL(k_kv_append, dim3(seqs.n_seq, H_kv), dim3(128), 0, st, k_new, v_new, ld_new,
+                     seqs, H_kv, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads, int n_kv, int head_dim,
+                               const int32_t* pos, double theta, const SeqArgs& seqs,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_rope_kv_step, dim3(seqs.n_seq, n_heads + n_kv), dim3(64), 0, st, qkv,
+                     ld_qkv, n_heads, n_kv, head_dim, pos, theta, seqs);
+  return hipGetLastError();
+}
+
+}  // namespace sd

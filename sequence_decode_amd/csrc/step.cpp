@@ -1,0 +1,147 @@
+// step.cpp -- sd_decode_step: one fused batched decode step, enqueued from C++.
+//
+// Structure: ds4 pull request 604, "2. Single-GPU decode batches don't scale"
+// and "Commit walkthrough / Graph driver": the dense projections run once on a
+// shared batch workspace with one row per sequence, so the weights cross HBM
+// once per step; RoPE and the KV append run per sequence at each sequence's own
+// position; attention is one multi-sequence launch; the feed-forward block and
+// the output head run on the batch; the logits land one row per sequence.
+// Every kernel here is row-independent with a fixed reduction order, so a
+// sequence's logits are bitwise those of a step that holds it alone (the
+// exactness of "feat(qwen4exp): exact 4-slot concurrent serving", "How it
+// stays exact").  The ~10 launches per layer are issued from here, not from
+// Python, so the host keeps ahead of the GPU.
+#include <math.h>
+
+#include "internal.hpp"
+
+using namespace sd;
+
+namespace {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct StepLayout {
+  size_t x, aq, ad, qkv, attn_o, gu, part, total;
+};
+
+bool model_ok(const sd_model* m) {
+  if (!m || !m->layers || !m->tok_embd || !m->out_norm || !m->w_lm_head) return false;
+  if (m->n_layers < 1 || m->hidden < 256 || m->vocab < 1 || m->ffn < 256) return false;
+  if (m->head_dim != kAttnHeadDim || m->n_kv_heads < 1 || m->n_heads != kAttnGroup * m->n_kv_heads)
+    return false;
+  if (m->hidden % 256 != 0 || m->ffn % 256 != 0 || (m->n_heads * m->head_dim) % 256 != 0) return false;
+  if (m->hidden > 32768 || m->ffn > 32768) return false;
+  if (!(m->rms_eps >= 0.0f) || !(m->rope_theta > 0.0)) return false;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const sd_layer_weights& L = m->layers[l];
+    if (!L.w_qkv || !L.w_o || !L.w_gate_up || !L.w_down || !L.attn_norm || !L.ffn_norm) return false;
+  }
+  return true;
+}
+
+StepLayout layout(const sd_model* m, int n, int max_ctx) {
+  const size_t qkv_rows = (size_t)(m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+  size_t maxk = (size_t)m->hidden;
+  if ((size_t)m->ffn > maxk) maxk = m->ffn;
+  if ((size_t)m->n_heads * m->head_dim > maxk) maxk = (size_t)m->n_heads * m->head_dim;
+  const size_t chunks = (size_t)(max_ctx + kAttnChunk - 1) / kAttnChunk;
+  StepLayout L;
+  size_t off = 0;
+  L.x = off;      off = align_up(off + (size_t)n * m->hidden * 4, 256);
+  L.aq = off;     off = align_up(off + (size_t)n * maxk, 256);
+  L.ad = off;     off = align_up(off + (size_t)n * (maxk / 32) * 4, 256);
+  L.qkv = off;    off = align_up(off + (size_t)n * qkv_rows * 4, 256);
+  L.attn_o = off; off = align_up(off + (size_t)n * m->n_heads * m->head_dim * 4, 256);
+  L.gu = off;     off = align_up(off + (size_t)n * 2 * m->ffn * 4, 256);
+  L.part = off;   off = align_up(off + (size_t)n * chunks * m->n_heads * kAttnPartialFloats * 4, 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sd_decode_step_workspace_bytes(const sd_model* m, int n_seq, int max_ctx) {
+  if (!model_ok(m) || n_seq < 1 || n_seq > SD_MAX_SEQS || max_ctx < 1) return 0;
+  return layout(m, n_seq, max_ctx).total;
+}
+
+int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) {
+  if (!model_ok(m)) return SD_EUNSUPPORTED;
+  if (!io || !io->seqs || !io->tokens || !io->positions || !io->logits || !io->next_tokens || !io->ws)
+    return SD_EINVAL;
+  const int n = io->n_seq;
+  if (n < 1 || n > SD_MAX_SEQS) return SD_EINVAL;
+  int max_ctx = 1;
+  for (int s = 0; s < n; ++s) {
+    const sd_step_seq& q = io->seqs[s];
+    if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || q.pos >= q.capacity) return SD_EINVAL;
+    if (((uintptr_t)q.k_cache % 16) || ((uintptr_t)q.v_cache % 16)) return SD_EALIGN;
+    if (q.pos + 1 > max_ctx) max_ctx = q.pos + 1;
+  }
+  if ((uintptr_t)io->ws % 256 || (uintptr_t)io->logits % 4 || (uintptr_t)io->tokens % 4 ||
+      (uintptr_t)io->positions % 4 || (uintptr_t)io->next_tokens % 4)
+    return SD_EALIGN;
+  const StepLayout W = layout(m, n, max_ctx);
+  if (io->ws_bytes < W.total) return SD_EWORKSPACE;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(io->ws);
+  float* x = reinterpret_cast<float*>(ws + W.x);
+  int8_t* aq = reinterpret_cast<int8_t*>(ws + W.aq);
+  float* ad = reinterpret_cast<float*>(ws + W.ad);
+  float* qkv = reinterpret_cast<float*>(ws + W.qkv);
+  float* attn_o = reinterpret_cast<float*>(ws + W.attn_o);
+  float* gu = reinterpret_cast<float*>(ws + W.gu);
+  float* part = reinterpret_cast<float*>(ws + W.part);
+
+  const int H = m->hidden, Hq = m->n_heads, Hkv = m->n_kv_heads, D = m->head_dim, F = m->ffn;
+  const int64_t QKV = (int64_t)(Hq + 2 * Hkv) * D;
+  const int64_t HqD = (int64_t)Hq * D;
+  const float scale = 1.0f / sqrtf((float)D);
+  const int64_t layer_elems_per_tok = (int64_t)Hkv * D;
+
+  SeqArgs sa{};
+  sa.n_seq = n;
+  for (int s = 0; s < n; ++s) {
+    sa.s[s].ld_tok = layer_elems_per_tok;
+    sa.s[s].ld_head = D;
+    sa.s[s].ctx_len = io->seqs[s].pos + 1;
+  }
+  attn_layout(&sa, Hq, Hkv);
+
+#define SD_TRY(call)                         \
+  do {                                       \
+    if ((call) != hipSuccess) return SD_EHIP; \
+  } while (0)
+
+  SD_TRY(launch_embed(m->tok_embd, m->vocab, H, io->tokens, n, x, st));
+  for (int l = 0; l < m->n_layers; ++l) {
+    const sd_layer_weights& L = m->layers[l];
+    for (int s = 0; s < n; ++s) {
+      const int64_t off = (int64_t)l * io->seqs[s].capacity * layer_elems_per_tok;
+      sa.s[s].k = io->seqs[s].k_cache + off;
+      sa.s[s].v = io->seqs[s].v_cache + off;
+      sa.s[s].k_w = io->seqs[s].k_cache + off;
+      sa.s[s].v_w = io->seqs[s].v_cache + off;
+    }
+    SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
+    SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
+    SD_TRY(launch_rope_kv_step(qkv, QKV, Hq, Hkv, D, io->positions, m->rope_theta, sa, st));
+    SD_TRY(launch_attn(qkv, QKV, sa, Hq, Hkv, scale, attn_o, part, aq, ad, st));
+    SD_TRY(launch_qgemv(L.w_o, H, HqD, aq, ad, n, x, x, H, st));
+    SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));
+    SD_TRY(launch_qgemv(L.w_gate_up, 2 * (int64_t)F, H, aq, ad, n, nullptr, gu, 2 * (int64_t)F, st));
+    SD_TRY(launch_swiglu_q8(gu, 2 * (int64_t)F, n, F, aq, ad, nullptr, st));
+    SD_TRY(launch_qgemv(L.w_down, H, F, aq, ad, n, x, x, H, st));
+  }
+  SD_TRY(launch_rmsnorm_q8(x, H, n, H, m->out_norm, m->rms_eps, aq, ad, nullptr, st));
+  SD_TRY(launch_qgemv(m->w_lm_head, m->vocab, H, aq, ad, n, nullptr, io->logits, m->vocab, st));
+  SD_TRY(launch_argmax(io->logits, m->vocab, n, m->vocab, io->next_tokens, st));
+#undef SD_TRY
+  return SD_OK;
+}
+
+}  // extern "C"

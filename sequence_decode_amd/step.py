@@ -1,0 +1,147 @@
+"""Device-side synthetic model and the sd_decode_step binding.
+
+Holds the model's device tensors and the ctypes structs that point at them
+(torch allocates; the library computes).  Weights either come from host arrays
+(the seeded generator's output, for tests) or are drawn on the device (large
+benchmark models).
+"""
+import ctypes
+
+import numpy as np
+
+from . import _lib, synth
+from . import _check, _stream
+
+
+class DecodeModel:
+    """A dense decoder in the library's layout (see sd_model in seqdecode.h)."""
+
+    def __init__(self, dims, layers, tok_embd, out_norm, w_lm):
+        import torch
+        self.dims = dict(dims)
+        self.layers = layers          # list of dicts of device tensors
+        self.tok_embd = tok_embd      # float16 [vocab][hidden] (fp16 bits)
+        self.out_norm = out_norm
+        self.w_lm = w_lm
+        d = self.dims
+        self._lw = (_lib.LayerWeights * d["n_layers"])()
+        for i, L in enumerate(layers):
+            self._lw[i] = _lib.LayerWeights(L["w_qkv"].data_ptr(), L["w_o"].data_ptr(),
+                                            L["w_gu"].data_ptr(), L["w_down"].data_ptr(),
+                                            L["attn_norm"].data_ptr(), L["ffn_norm"].data_ptr())
+        self.struct = _lib.Model(d["n_layers"], d["hidden"], d["n_heads"], d["n_kv_heads"],
+                                 d["head_dim"], d["ffn"], d["vocab"], float(d["eps"]),
+                                 float(d["theta"]), tok_embd.data_ptr(), out_norm.data_ptr(),
+                                 w_lm.data_ptr(), ctypes.cast(self._lw, ctypes.c_void_p))
+        self.device = tok_embd.device
+        del torch
+
+    @property
+    def weight_bytes(self) -> int:
+        n = sum(t.numel() for L in self.layers for k, t in L.items() if k.startswith("w_"))
+        return n + self.w_lm.numel()
+
+    @classmethod
+    def from_host(cls, h: dict, device="cuda"):
+        import torch
+
+        def dev(a, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return t.to(device) if dtype is None else t.view(dtype).to(device)
+
+        layers = []
+        for L in h["layers"]:
+            layers.append({k: dev(v) for k, v in L.items()})
+        dims = {k: h[k] for k in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim",
+                                  "ffn", "vocab", "eps", "theta")}
+        return cls(dims, layers, dev(h["tok_embd_bits"], torch.float16), dev(h["out_norm"]),
+                   dev(h["w_lm"]))
+
+    @classmethod
+    def random_device(cls, seed: int, dims: dict, device="cuda"):
+        """Same distributions as synth.model_host, drawn by torch on the device."""
+        import torch
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        H, Hq, Hkv, D, F, V = (dims[k] for k in ("hidden", "n_heads", "n_kv_heads", "head_dim",
+                                                  "ffn", "vocab"))
+        qkv_rows = (Hq + 2 * Hkv) * D
+
+        def w(N, K):
+            lo, hi = synth.unit_gain_scale_range(K)
+            return synth.torch_q8_0_weights(g, N, K, device, lo, hi)
+
+        def gamma(n):
+            return torch.rand(n, device=device, generator=g) + 0.5
+
+        layers = []
+        for _ in range(dims["n_layers"]):
+            layers.append({"w_qkv": w(qkv_rows, H), "w_o": w(H, Hq * D), "w_gu": w(2 * F, H),
+                           "w_down": w(H, F), "attn_norm": gamma(H), "ffn_norm": gamma(H)})
+        tok = synth.torch_normal_f16(g, (V, H), device)
+        return cls(dims, layers, tok, gamma(H), w(V, H))
+
+
+class SeqCache:
+    """One sequence's caches, fp16 [n_layers][capacity][H_kv][D]."""
+
+    def __init__(self, k, v):
+        self.k, self.v = k, v
+        self.capacity = k.shape[1]
+
+    @classmethod
+    def from_host(cls, k_bits, v_bits, device="cuda"):
+        import torch
+        return cls(torch.from_numpy(k_bits).view(torch.float16).to(device),
+                   torch.from_numpy(v_bits).view(torch.float16).to(device))
+
+    @classmethod
+    def random_device(cls, gen, n_layers, capacity, H_kv, D, device="cuda"):
+        return cls(synth.torch_normal_f16(gen, (n_layers, capacity, H_kv, D), device),
+                   synth.torch_normal_f16(gen, (n_layers, capacity, H_kv, D), device))
+
+
+class StepRunner:
+    """Preallocated inputs/outputs/workspace for repeated sd_decode_step calls."""
+
+    def __init__(self, model: DecodeModel, caches, max_ctx: int):
+        import torch
+        self.model = model
+        self.caches = list(caches)
+        n = len(self.caches)
+        V = model.dims["vocab"]
+        dev = model.device
+        need = _lib.load().sd_decode_step_workspace_bytes(ctypes.byref(model.struct), n, max_ctx)
+        if need == 0:
+            raise ValueError("model or batch not supported by sd_decode_step")
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.logits = torch.empty((n, V), dtype=torch.float32, device=dev)
+        self.next_tokens = torch.empty(n, dtype=torch.int32, device=dev)
+        self.tokens = torch.zeros(n, dtype=torch.int32, device=dev)
+        self.positions = torch.zeros(n, dtype=torch.int32, device=dev)
+        self._seqs = (_lib.StepSeq * n)()
+        for s, c in enumerate(self.caches):
+            self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0)
+        self.io = _lib.StepIO(n, ctypes.cast(self._seqs, ctypes.c_void_p), self.tokens.data_ptr(),
+                              self.positions.data_ptr(), self.logits.data_ptr(),
+                              self.next_tokens.data_ptr(), self.ws.data_ptr(), need)
+
+    def set_positions(self, pos):
+        """Sets every sequence's position (host structs and device copy)."""
+        import torch
+        for s, p in enumerate(pos):
+            self._seqs[s].pos = int(p)
+        self.positions.copy_(torch.tensor(list(pos), dtype=torch.int32))
+
+    def advance(self):
+        """Moves every sequence one position on and feeds the greedy tokens back,
+        without a host round trip (both updates are enqueued on the stream)."""
+        for s in range(len(self.caches)):
+            self._seqs[s].pos += 1
+        self.positions.add_(1)
+        self.tokens.copy_(self.next_tokens)
+
+    def step(self, stream=None):
+        """Enqueues one step reading self.tokens / positions (already on device)."""
+        _check("sd_decode_step", _lib.load().sd_decode_step(
+            ctypes.byref(self.model.struct), ctypes.byref(self.io), _stream(stream)))

@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host (CPU only: rejected calls make no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sequence_decode_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seqdecode.h")
+
+SD_OK, SD_EINVAL, SD_EUNSUPPORTED, SD_EALIGN, SD_EWORKSPACE = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+ODD = ctypes.c_void_p(0x10002)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libseqdecode.so not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(L):
+    assert L.sd_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.sd_status_string(code).startswith(b"SD_")
+    assert L.sd_status_string(7) == b"unknown sd_status"
+
+
+def test_gemv_rejections(L):
+    g = L.sd_qgemv_q8_0_batch
+    assert g(None, 64, 256, FAKE, FAKE, 1, None, FAKE, 64, None) == SD_EINVAL
+    assert g(FAKE, 64, 256, FAKE, FAKE, 0, None, FAKE, 64, None) == SD_EINVAL
+    assert g(FAKE, 64, 256, FAKE, FAKE, 17, None, FAKE, 64, None) == SD_EINVAL
+    assert g(FAKE, 64, 128, FAKE, FAKE, 1, None, FAKE, 64, None) == SD_EUNSUPPORTED
+    assert g(FAKE, 64, 4000, FAKE, FAKE, 1, None, FAKE, 64, None) == SD_EUNSUPPORTED
+    assert g(FAKE, 64, 256, FAKE, FAKE, 1, None, FAKE, 63, None) == SD_EINVAL
+    assert g(ODD, 64, 256, FAKE, FAKE, 1, None, FAKE, 64, None) == SD_EALIGN
+    assert g(FAKE, 64, 256, ODD, FAKE, 1, None, FAKE, 64, None) == SD_EALIGN
+    assert g(FAKE, 0, 14336, FAKE, FAKE, 16, None, FAKE, 64, None) == SD_EINVAL
+
+
+def test_quantize_rejections(L):
+    q = L.sd_quantize_q8_act
+    assert q(FAKE, 64, 1, 48, FAKE, FAKE, None) == SD_EUNSUPPORTED
+    assert q(FAKE, 16, 1, 32, FAKE, FAKE, None) == SD_EINVAL
+    assert q(FAKE, 64, 17, 64, FAKE, FAKE, None) == SD_EINVAL
+    assert q(FAKE, 64, 1, 64, ODD, FAKE, None) == SD_EALIGN
+
+
+def _view(ctx, cap, k=FAKE, ld_tok=1024, ld_head=128):
+    return _lib.SeqView(k.value, FAKE.value, ctx, cap, ld_tok, ld_head)
+
+
+def test_attention_rejections(L):
+    a = L.sd_decode_attn_multiseq
+    views5 = (_lib.SeqView * 5)(*[_view(10, 16) for _ in range(5)])
+    assert a(FAKE, 4096, views5, 5, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
+    v1 = (_lib.SeqView * 1)(_view(10, 16))
+    assert a(FAKE, 4096, v1, 0, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
+    assert a(FAKE, 4096, v1, 1, 32, 8, 64, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EUNSUPPORTED
+    assert a(FAKE, 4096, v1, 1, 32, 16, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EUNSUPPORTED
+    assert a(FAKE, 4096, v1, 1, 30, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
+    over = (_lib.SeqView * 1)(_view(17, 16))
+    assert a(FAKE, 4096, over, 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
+    zero = (_lib.SeqView * 1)(_view(0, 16))
+    assert a(FAKE, 4096, zero, 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
+    mis = (_lib.SeqView * 1)(_view(10, 16, k=ctypes.c_void_p(0x10008)))
+    assert a(FAKE, 4096, mis, 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EALIGN
+    need = L.sd_decode_attn_workspace_bytes(v1, 1, 32, 128)
+    assert need == 1 * 32 * 132 * 4      # one chunk per head for ctx 10
+    assert a(FAKE, 4096, v1, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
+    v2 = (_lib.SeqView * 2)(_view(2050, 4096), _view(32768, 32768))
+    assert L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128) == (9 + 128) * 32 * 132 * 4
+
+
+def test_rope_kv_and_glue_rejections(L):
+    r = L.sd_rope_posvec
+    assert r(FAKE, 4, 32, 128, 4096, 128, FAKE, 1e6, 127, None) == SD_EINVAL
+    assert r(FAKE, 4, 32, 128, 4096, 128, FAKE, 1e6, 130, None) == SD_EINVAL
+    assert r(FAKE, 4, 32, 128, 4096, 128, FAKE, -1.0, 128, None) == SD_EINVAL
+    assert r(ODD, 4, 32, 128, 4096, 128, FAKE, 1e6, 128, None) == SD_EALIGN
+    v1 = (_lib.SeqView * 1)(_view(3, 2))
+    assert L.sd_kv_append_f16(FAKE, FAKE, 1024, v1, 1, 8, 128, None) == SD_EINVAL
+    assert L.sd_rmsnorm_q8(FAKE, 100, 1, 100, FAKE, 1e-6, FAKE, FAKE, None, None) == SD_EUNSUPPORTED
+    assert L.sd_rmsnorm_q8(FAKE, 128, 1, 128, FAKE, -1.0, FAKE, FAKE, None, None) == SD_EINVAL
+    assert L.sd_swiglu_q8(FAKE, 100, 1, 64, FAKE, FAKE, None, None) == SD_EINVAL
+    assert L.sd_argmax_rows(FAKE, 10, 1, 11, FAKE, None) == SD_EINVAL
+    assert L.sd_embed_f16(FAKE, 0, 16, FAKE, 1, FAKE, None) == SD_EINVAL
+
+
+def test_step_rejections(L):
+    lw = (_lib.LayerWeights * 1)(_lib.LayerWeights(*([FAKE.value] * 6)))
+    m = _lib.Model(1, 4096, 32, 8, 128, 14336, 1000, 1e-6, 1e6, FAKE.value, FAKE.value,
+                   FAKE.value, ctypes.cast(lw, ctypes.c_void_p))
+    need = L.sd_decode_step_workspace_bytes(ctypes.byref(m), 4, 32768)
+    assert need > 0
+    assert L.sd_decode_step_workspace_bytes(ctypes.byref(m), 5, 32768) == 0
+    bad = _lib.Model(1, 4096, 32, 8, 64, 14336, 1000, 1e-6, 1e6, FAKE.value, FAKE.value,
+                     FAKE.value, ctypes.cast(lw, ctypes.c_void_p))
+    assert L.sd_decode_step_workspace_bytes(ctypes.byref(bad), 1, 16) == 0
+    seqs = (_lib.StepSeq * 1)(_lib.StepSeq(FAKE.value, FAKE.value, 16, 16))   # pos == capacity
+    io = _lib.StepIO(1, ctypes.cast(seqs, ctypes.c_void_p), FAKE.value, FAKE.value, FAKE.value,
+                     FAKE.value, 0x100000, 1 << 30)
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EINVAL
+    assert L.sd_decode_step(ctypes.byref(bad), ctypes.byref(io), None) == SD_EUNSUPPORTED
+    seqs[0].pos = 3
+    io.ws_bytes = 16
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EWORKSPACE

@@ -1,0 +1,149 @@
+"""The fused decode step on the GPU: bitwise batch invariance (the hard gate)
+and end-to-end agreement with the oracle's step.
+
+Batch invariance, bitwise: each sequence's logits, next token and cache rows
+are those of a step holding it alone, for 1..4 sequences, any order, over a
+64-step soak that feeds tokens back, and across a cancel/reset/reuse of one
+slot.  Against the oracle: requantization between layers makes the end-to-end
+result discontinuous (one activation code can flip when an input moves by an
+ulp), so the check is normwise (logits within 1e-3 relative) and on tokens
+whose top-2 margin is clear.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import step as ostep
+from helpers import bits, dev, host, say
+from sequence_decode_amd import synth
+from sequence_decode_amd.step import DecodeModel, SeqCache, StepRunner
+
+pytestmark = pytest.mark.gpu
+
+DIMS = dict(n_layers=2, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128, ffn=768, vocab=1000)
+CAP = 320
+
+
+@pytest.fixture(scope="module")
+def model_host():
+    return synth.model_host(3000, **DIMS)
+
+
+@pytest.fixture(scope="module")
+def model(sd, model_host):
+    return DecodeModel.from_host(model_host)
+
+
+def _caches_host(n, seed=3001):
+    g = synth.rng(seed)
+    return [synth.prefilled_cache(g, DIMS["n_layers"], CAP, DIMS["n_kv_heads"], DIMS["head_dim"])
+            for _ in range(n)]
+
+
+def _run(model, caches_h, tokens, pos):
+    """One GPU step on fresh device copies; returns logits, tokens, device caches."""
+    caches = [SeqCache.from_host(k, v) for k, v in caches_h]
+    r = StepRunner(model, caches, max_ctx=CAP)
+    r.tokens.copy_(dev(np.asarray(tokens, np.int32)))
+    r.set_positions(pos)
+    r.step()
+    return host(r.logits), host(r.next_tokens), [(host(c.k), host(c.v)) for c in caches]
+
+
+def test_step_batched_equals_solo(sd, model):
+    say("step batched == solo")
+    ch = _caches_host(4)
+    toks, pos = [11, 222, 333, 999], [0, 130, 256, 319]
+    lg, nt, cs = _run(model, ch, toks, pos)
+    for s in range(4):
+        l1, n1, c1 = _run(model, [ch[s]], [toks[s]], [pos[s]])
+        assert np.array_equal(bits(l1[0]), bits(lg[s])), s
+        assert n1[0] == nt[s]
+        assert np.array_equal(c1[0][0], cs[s][0]) and np.array_equal(c1[0][1], cs[s][1])
+    perm = [2, 0, 3, 1]
+    lp, npm, _ = _run(model, [ch[i] for i in perm], [toks[i] for i in perm], [pos[i] for i in perm])
+    assert np.array_equal(bits(lp), bits(lg[perm])) and np.array_equal(npm, nt[perm])
+    for n in (2, 3):
+        ln, nn, _ = _run(model, ch[:n], toks[:n], pos[:n])
+        assert np.array_equal(bits(ln), bits(lg[:n]))
+
+
+def test_step_soak_64_steps_and_slot_reuse(sd, model):
+    """Four sequences decode 64 steps batched; every step equals the solo runs.
+    At step 20 slot 1 is cancelled, reset to a new sequence and reused."""
+    import torch
+    say("step soak 64")
+    ch = _caches_host(5, seed=3100)
+    start = [3, 40, 100, 250]
+    first = [5, 6, 7, 8]
+    steps = 64
+    # batched run with a reset of slot 1 at step 20 (new cache = ch[4], new start 0)
+    caches = [SeqCache.from_host(*ch[s]) for s in range(4)]
+    r = StepRunner(model, caches, max_ctx=CAP)
+    pos = list(start)
+    tok = list(first)
+    hist = [[] for _ in range(4)]
+    for i in range(steps):
+        if i == 20:
+            fresh = SeqCache.from_host(*ch[4])
+            caches[1].k.copy_(fresh.k)
+            caches[1].v.copy_(fresh.v)
+            pos[1], tok[1] = 0, 42
+        r.tokens.copy_(torch.tensor(tok, dtype=torch.int32))
+        r.set_positions(pos)
+        r.step()
+        lg = host(r.logits)
+        nt = host(r.next_tokens)
+        for s in range(4):
+            hist[s].append((lg[s].copy(), int(nt[s])))
+        tok = [int(t) for t in nt]
+        pos = [p + 1 for p in pos]
+    # solo reference runs
+    def solo(cache_h, p0, t0, n_steps):
+        c = SeqCache.from_host(*cache_h)
+        rr = StepRunner(model, [c], max_ctx=CAP)
+        out, p, t = [], p0, t0
+        for _ in range(n_steps):
+            rr.tokens.copy_(torch.tensor([t], dtype=torch.int32))
+            rr.set_positions([p])
+            rr.step()
+            l1 = host(rr.logits)[0].copy()
+            t = int(host(rr.next_tokens)[0])
+            out.append((l1, t))
+            p += 1
+        return out
+    for s in (0, 2, 3):
+        ref = solo(ch[s], start[s], first[s], steps)
+        for i in range(steps):
+            assert np.array_equal(bits(ref[i][0]), bits(hist[s][i][0])), (s, i)
+            assert ref[i][1] == hist[s][i][1]
+    ref1a = solo(ch[1], start[1], first[1], 20)
+    for i in range(20):
+        assert np.array_equal(bits(ref1a[i][0]), bits(hist[1][i][0]))
+    ref1b = solo(ch[4], 0, 42, steps - 20)
+    for i in range(steps - 20):
+        assert np.array_equal(bits(ref1b[i][0]), bits(hist[1][20 + i][0]))
+
+
+def test_step_matches_oracle_end_to_end(sd, model, model_host):
+    say("step vs oracle")
+    h = model_host
+    m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
+                    h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
+                    h["w_lm"], h["layers"])
+    ch = _caches_host(4, seed=3200)
+    toks, pos = [1, 2, 500, 998], [7, 64, 255, 300]
+    lg, nt, cs = _run(model, ch, toks, pos)
+    ocache = [(k.copy(), v.copy()) for k, v in ch]
+    olg, ont = ostep.decode_step(m, ocache, toks, pos)
+    rel = np.linalg.norm(lg - olg) / np.linalg.norm(olg)
+    say(f"  logits normwise relative error vs oracle: {rel:.3e}")
+    assert rel <= 1e-3
+    for s in range(4):
+        top = np.sort(olg[s])[-2:]
+        if top[1] - top[0] > 1e-3 * abs(top[1]):
+            assert nt[s] == ont[s]
+        for L in range(DIMS["n_layers"]):
+            gk = cs[s][0][L, pos[s]].view(np.float16).astype(np.float32)
+            ok = ocache[s][0][L, pos[s]].view(np.float16).astype(np.float32)
+            assert np.max(np.abs(gk - ok)) <= 2e-2 * max(1.0, np.max(np.abs(ok)))

@@ -5,9 +5,11 @@ Headline (one JSON line on stdout): q8_0 narrow-batch GEMV throughput in GB/s
 over the 8B-class decode projections -- 32 layers of QKV 4096->6144, O
 4096->4096, gate|up 4096->2x14336 (one fused matrix), down 14336->4096, q8_0
 weights with fp16 scales uniform[1e-3, 1e-2], fp32 N(0,1) activations
-quantized per token -- at n_tok = 4.  A step is one sweep: per layer, quantize
-the projection input, then the GEMV, for all four projections (7.42 GB of
-weights, far beyond the 256 MB Infinity Cache).  The timed steps replay a HIP
+quantized per token -- at n_tok = 4.  A step is one sweep over one batch of
+n_tok synthetic activation rows: quantize them (once for the 4096-wide input
+of QKV, O and gate|up, once for the 14336-wide input of down), then the 128
+GEMVs of the 32 layers (7.42 GB of weights, far beyond the 256 MB Infinity
+Cache).  The timed steps replay a HIP
 graph of the sweep, so the host's launch rate does not limit the GPU.  Inputs
 are resident in HBM before timing starts.
 
@@ -50,8 +52,9 @@ class Sweep:
         self.w = [{name: synth.torch_q8_0_weights(g, N, K, "cuda") for name, N, K in SHAPES}
                   for _ in range(N_LAYERS)]
         self.x = torch.randn((max_tok, 14336), dtype=torch.float32, device="cuda", generator=g)
-        self.xq = torch.empty((max_tok, 14336), dtype=torch.int8, device="cuda")
-        self.xd = torch.empty((max_tok, 14336 // 32), dtype=torch.float32, device="cuda")
+        self.xq = {K: torch.empty((max_tok, K), dtype=torch.int8, device="cuda") for K in (4096, 14336)}
+        self.xd = {K: torch.empty((max_tok, K // 32), dtype=torch.float32, device="cuda")
+                   for K in (4096, 14336)}
         self.y = {name: torch.empty((max_tok, N), dtype=torch.float32, device="cuda")
                   for name, N, K in SHAPES}
         self.weight_bytes = sum(N * (K // 32) * 34 for _, N, K in SHAPES) * N_LAYERS
@@ -61,13 +64,14 @@ class Sweep:
         import ctypes
         st = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
         P = ctypes.c_void_p
-        xq, xd = self.xq, self.xd
+        for K in (4096, 14336):
+            rc = lib.sd_quantize_q8_act(P(self.x.data_ptr()), 14336, n_tok, K,
+                                        P(self.xq[K].data_ptr()), P(self.xd[K].data_ptr()), st)
+            if rc:
+                raise sd.SdError("sd_quantize_q8_act", rc)
         for L in self.w:
             for name, N, K in SHAPES:
-                rc = lib.sd_quantize_q8_act(P(self.x.data_ptr()), 14336, n_tok, K, P(xq.data_ptr()),
-                                            P(xd.data_ptr()), st)
-                if rc:
-                    raise sd.SdError("sd_quantize_q8_act", rc)
+                xq, xd = self.xq[K], self.xd[K]
                 y = self.y[name]
                 if events is not None:
                     e0 = self.torch.cuda.Event(enable_timing=True)
@@ -130,8 +134,6 @@ def roofline_pass(torch, sweep, n_tok, reps):
 def cpu_baseline(torch, sweep, n_tok, budget_s):
     import numpy as np
     import oracle
-    xq = sweep.xq[:n_tok].cpu().numpy()
-    xd = sweep.xd[:n_tok].cpu().numpy()
     done_bytes, t_used, layers = 0, 0.0, 0
     x = sweep.x[:n_tok].cpu().numpy()
     for L in sweep.w:
@@ -145,7 +147,6 @@ def cpu_baseline(torch, sweep, n_tok, budget_s):
         layers += 1
         if t_used >= budget_s:
             break
-    del xq, xd
     return {"value": round(done_bytes / t_used / 1e9, 3), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{layers} of 32 layers (4 projections each) at n_tok={n_tok}, "

@@ -46,12 +46,33 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Sum over the 64 lanes of a wave with a fixed butterfly (xor 32, 16, ..., 1).
-// Floating-point addition is commutative, so every lane ends with the same
+template <int ctrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl,
+                                                               0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wave with a fixed tree: partners at lane distance
+// 1 and 2 (DPP quad permutations), then the mirrored lane within 8 and within
+// 16 (DPP row mirrors), then lanes 16 and 32 apart (v_permlane16/32_swap,
+// which return the lower and the upper partner in fixed operand order).  Every
+// level adds two equal-shaped subtree sums, so all 64 lanes end with the same
 // bits, and the tree depends on nothing but the lane index.
 __device__ __forceinline__ float wave_sum_fixed(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fadd(v, __shfl_xor(v, m, 64));
+  v = fadd(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = fadd(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = fadd(v, dpp_mov<0x141>(v));  // row_half_mirror: 7 - lane within 8
+  v = fadd(v, dpp_mov<0x140>(v));  // row_mirror: 15 - lane within 16
+  {
+    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    v = fadd(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  }
+  {
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    v = fadd(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  }
   return v;
 }
 

@@ -50,10 +50,14 @@ hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
 // GEMV launch geometry for (N, K, n_tok): lds bytes and slice layout.
 struct GemvPlan {
   int pairs;         // K / 64
+  int chunks;        // pairs / 64 rounded up: the unit of the fixed reduction order
+  bool use_reg;      // activations held in registers (1..4 tokens, <= 4 chunks)
+  int sp;            // waves per row in the register kernel (1, 2 or 4)
   int slice_pairs;   // pairs staged per LDS slice (multiple of 64, or all)
   int n_slices;
   size_t lds_bytes;
   int rows_per_wave;
+  int n_blocks;      // row blocks of rows_per_wave rows
   int grid;
 };
 bool plan_qgemv(int64_t N, int64_t K, int n_tok, GemvPlan* plan);

@@ -38,6 +38,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per GEMV launch from the committed rocprofv3 --pmc summary, if
+    it was taken on the kernel source that is built now (else None)."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "qgemv_q8_0_sweep_ntok1-4.md")
+    src = os.path.join(ROOT, "sequence_decode_amd", "csrc", "qgemv.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_launch: ", "kernel_source_sha256: ")))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != sha:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def gemv_bytes(N, K, n_tok):
     """Algorithmic bytes of one launch: weights once, q8 activations, fp32 outputs."""
     return N * (K // 32) * 34 + n_tok * (K + 4 * (K // 32)) + 4 * n_tok * N
@@ -59,7 +76,7 @@ class Sweep:
                   for name, N, K in SHAPES}
         self.weight_bytes = sum(N * (K // 32) * 34 for _, N, K in SHAPES) * N_LAYERS
 
-    def step(self, n_tok, events=None):
+    def step(self, n_tok):
         sd, lib = self.sd, self.sd._lib.load()
         import ctypes
         st = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
@@ -73,17 +90,10 @@ class Sweep:
             for name, N, K in SHAPES:
                 xq, xd = self.xq[K], self.xd[K]
                 y = self.y[name]
-                if events is not None:
-                    e0 = self.torch.cuda.Event(enable_timing=True)
-                    e1 = self.torch.cuda.Event(enable_timing=True)
-                    e0.record()
                 rc = lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()),
                                              P(xd.data_ptr()), n_tok, None, P(y.data_ptr()), N, st)
                 if rc:
                     raise sd.SdError("sd_qgemv_q8_0_batch", rc)
-                if events is not None:
-                    e1.record()
-                    events.append((name, N, K, e0, e1))
 
     def bytes_per_step(self, n_tok):
         return sum(gemv_bytes(N, K, n_tok) for _, N, K in SHAPES) * N_LAYERS
@@ -112,23 +122,40 @@ def time_graph(torch, fn, steps, warmup):
 
 
 def roofline_pass(torch, sweep, n_tok, reps):
-    ev = []
-    for _ in range(reps):
-        sweep.step(n_tok, events=ev)
-    torch.cuda.synchronize()
-    tot_ms = 0.0
-    tot_bytes = 0
+    """Average duration of the GEMV kernel per shape: HIP events on the launch
+    stream around `reps` rounds of the shape's 32 matrices launched back to back
+    (nothing else in between), so each average is one kernel's duration plus
+    the dispatch gap to the next launch of the same kernel."""
+    import ctypes
+    lib = sweep.sd._lib.load()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
     per = {}
-    for name, N, K, e0, e1 in ev:
+    tot_bytes, tot_ms, launches = 0, 0.0, 0
+    for name, N, K in SHAPES:
+        xq, xd, y = sweep.xq[K], sweep.xd[K], sweep.y[name]
+        def run():
+            for L in sweep.w:
+                lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()), P(xd.data_ptr()),
+                                        n_tok, None, P(y.data_ptr()), N, st)
+        run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        tot_ms += ms
-        b = gemv_bytes(N, K, n_tok)
+        n = reps * len(sweep.w)
+        b = gemv_bytes(N, K, n_tok) * n
+        per[name] = {"GB_s": round(b / (ms / 1e3) / 1e9, 1), "avg_us": round(ms / n * 1e3, 3),
+                     "bytes_per_launch": gemv_bytes(N, K, n_tok), "launches": n}
         tot_bytes += b
-        d = per.setdefault(name, [0.0, 0, 0])
-        d[0] += ms
-        d[1] += b
-        d[2] += 1
-    return tot_bytes, tot_ms, len(ev), per
+        tot_ms += ms
+        launches += n
+    return tot_bytes, tot_ms, launches, per
 
 
 def cpu_baseline(torch, sweep, n_tok, budget_s):
@@ -178,13 +205,18 @@ def decode_bench(torch, steps, warmup):
                 r.advance()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
+            host = 0.0
             for _ in range(steps):
+                h0 = time.perf_counter()
                 r.step()
+                host += time.perf_counter() - h0
                 r.advance()
             torch.cuda.synchronize()
             dt = (time.perf_counter() - t0) / steps
-            res[f"{label}_n{n}"] = {"tok_s": round(n / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
-            log(f"decode {label} n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
+            res[f"{label}_n{n}"] = {"tok_s": round(n / dt, 2), "ms_per_step": round(dt * 1e3, 3),
+                                    "host_enqueue_ms": round(host / steps * 1e3, 3)}
+            log(f"decode {label} n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step, "
+                f"host enqueue {host / steps * 1e3:.3f} ms)")
     # serial baseline: the four ragged sequences one at a time (one-token steps back to back)
     runners = [StepRunner(model, [caches[s]], max_ctx=ragged[s] + span) for s in range(4)]
     for s in range(4):
@@ -215,6 +247,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="only the decode-step tok/s")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode step here is built and measured on a "
@@ -225,6 +260,16 @@ def main():
     import sequence_decode_amd as sd
     sd.load()
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps(decode_bench(torch, steps=max(8, args.steps), warmup=args.warmup)), flush=True)
+        return
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+        del a, b
     log("generating 7.42 GB of q8_0 projection weights on the device")
     sweep = Sweep(sd, torch, seed=1, max_tok=16)
     torch.cuda.synchronize()
@@ -242,10 +287,8 @@ def main():
     dt = time_graph(torch, lambda: sweep.step(n), args.steps, args.warmup)
     value = sweep.bytes_per_step(n) / dt / 1e9
 
-    tb, tms, launches, per = roofline_pass(torch, sweep, n, reps=2)
+    tb, tms, launches, per_shape = roofline_pass(torch, sweep, n, reps=4)
     achieved = tb / (tms / 1e3) / 1e9
-    per_shape = {k: {"GB_s": round(v[1] / (v[0] / 1e3) / 1e9, 1),
-                     "avg_us": round(v[0] / v[2] * 1e3, 3)} for k, v in per.items()}
     log(f"GEMV kernel (event-timed, {launches} launches): {achieved:.1f} GB/s; {per_shape}")
 
     line = {
@@ -259,8 +302,10 @@ def main():
                    "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "per_n_tok": per_n,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_qgemv_q8_0", "launches": launches,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": round(tb / launches),
+                     "kernel": f"k_qgemv_q8_0_dma<{n},SP,1>", "launches": launches,
                      "avg_launch_us": round(tms / launches * 1e3, 3), "per_shape": per_shape},
     }
     line["decode_step"] = None

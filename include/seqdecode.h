@@ -62,6 +62,8 @@ int sd_abi_version(void);
 /* Keys per attention chunk.  Fixed, so a sequence's split depends on its own
  * length only. */
 #define SD_ATTN_CHUNK 256
+/* Longest context one attention call takes (2048 chunks). */
+#define SD_MAX_CTX (2048 * SD_ATTN_CHUNK)
 
 /* ------------------------------------------------------------------ q8 data
  * q8_0 weight matrix: N rows, each of K/32 consecutive 34-byte blocks; a block
@@ -99,9 +101,9 @@ int sd_quantize_q8_act(const float* x, int64_t ldx, int n_tok, int64_t K,
  *   xq, xd    q8 activations of n_tok tokens (layout above); xq 16-byte aligned.
  *   residual  NULL or [n_tok][ldy] fp32; may equal y (in-place accumulate).
  *   y         [n_tok][ldy] fp32, ldy >= N.
- * Requires N >= 1, K % 256 == 0 (rows then start 16-byte aligned),
- * 1 <= n_tok <= SD_MAX_TOKENS, and n_tok * K * 1.25 bytes <= 144 KiB
- * (activations staged in LDS); otherwise SD_EUNSUPPORTED / SD_EINVAL.
+ * Requires 1 <= N <= 2^30, K % 256 == 0 (rows then start 16-byte aligned),
+ * K <= 2^24, 1 <= n_tok <= SD_MAX_TOKENS; otherwise SD_EUNSUPPORTED /
+ * SD_EINVAL.
  */
 int sd_qgemv_q8_0_batch(const void* w, int64_t N, int64_t K,
                         const int8_t* xq, const float* xd, int n_tok,
@@ -175,7 +177,7 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  *   views [host]: 16-byte aligned bases, ld_tok and ld_head multiples of 8.
  * Requires 1 <= n_seq <= SD_MAX_SEQS, D == 128, H_q % H_kv == 0,
  * H_q / H_kv == 4 (grouped-query attention with four query heads per KV head),
- * 1 <= ctx_len <= capacity.
+ * 1 <= ctx_len <= capacity, ctx_len <= SD_MAX_CTX (else SD_EUNSUPPORTED).
  */
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
                             int n_seq, int H_q, int H_kv, int D, float scale,
@@ -215,13 +217,17 @@ int sd_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F,
 int sd_embed_f16(const uint16_t* table, int64_t V, int64_t H, const int32_t* tokens,
                  int n_tok, float* x, sd_stream_t stream);
 
+/* Workspace bytes sd_argmax_rows needs (0 on invalid arguments). */
+size_t sd_argmax_workspace_bytes(int n_tok, int64_t V);
+
 /*
  * sd_argmax_rows -- greedy next token per row: the lowest index among equal
- * maxima of logits[t][0..V).  NaN never wins.
- *   logits [n_tok][ld] fp32; out [n_tok] int32.
+ * maxima of logits[t][0..V).  NaN never wins.  (Selection is exact, so the
+ * result does not depend on how the row is split across workgroups.)
+ *   logits [n_tok][ld] fp32; out [n_tok] int32; ws >= sd_argmax_workspace_bytes.
  */
 int sd_argmax_rows(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
-                   sd_stream_t stream);
+                   void* ws, size_t ws_bytes, sd_stream_t stream);
 
 /* ------------------------------------------------------- the decode step */
 

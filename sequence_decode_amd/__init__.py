@@ -184,6 +184,8 @@ def argmax_rows(logits, stream=None):
     _need(logits, torch.float32, "logits")
     n_tok, V = logits.shape
     out = torch.empty(n_tok, dtype=torch.int32, device=logits.device)
+    need = _lib.load().sd_argmax_workspace_bytes(n_tok, V)
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=logits.device)
     _check("sd_argmax_rows", _lib.load().sd_argmax_rows(
-        _p(logits), V, n_tok, V, _p(out), _stream(stream)))
+        _p(logits), V, n_tok, V, _p(out), _p(ws), ws.numel(), _stream(stream)))
     return out

@@ -21,7 +21,8 @@ SIGNATURES = {
     "sd_rmsnorm_q8": ([P, i64, i32, i64, P, f32, P, P, P, P], i32),
     "sd_swiglu_q8": ([P, i64, i32, i64, P, P, P, P], i32),
     "sd_embed_f16": ([P, i64, i64, P, i32, P, P], i32),
-    "sd_argmax_rows": ([P, i64, i32, i64, P, P], i32),
+    "sd_argmax_workspace_bytes": ([i32, i64], sz),
+    "sd_argmax_rows": ([P, i64, i32, i64, P, P, sz, P], i32),
     "sd_decode_step_workspace_bytes": ([P, i32, i32], sz),
     "sd_decode_step": ([P, P, P], i32),
 }

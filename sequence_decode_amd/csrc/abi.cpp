@@ -40,6 +40,7 @@ int check_views(const sd_seqview* views, int n_seq, int D, bool attn) {
     const sd_seqview& v = views[s];
     if (!v.k || !v.v) return SD_EINVAL;
     if (v.capacity < 1 || v.ctx_len < 1 || v.ctx_len > v.capacity) return SD_EINVAL;
+    if (attn && v.ctx_len > SD_MAX_CTX) return SD_EUNSUPPORTED;
     if (v.ld_head < D || v.ld_tok < D) return SD_EINVAL;
     const size_t al = attn ? 16 : 4;
     if (!aligned(v.k, al) || !aligned(v.v, al)) return SD_EALIGN;
@@ -174,12 +175,18 @@ int sd_embed_f16(const uint16_t* table, int64_t V, int64_t H, const int32_t* tok
   return from_hip(launch_embed(table, V, H, tokens, n_tok, x, hs(stream)));
 }
 
-int sd_argmax_rows(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
-                   sd_stream_t stream) {
-  if (!logits || !out || n_tok < 1 || n_tok > 65535 || V < 1 || V > INT32_MAX - 1 || ld < V)
+size_t sd_argmax_workspace_bytes(int n_tok, int64_t V) {
+  if (n_tok < 1 || n_tok > 65535 || V < 1 || V > INT32_MAX - 1) return 0;
+  return argmax_ws_bytes(n_tok, V);
+}
+
+int sd_argmax_rows(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out, void* ws,
+                   size_t ws_bytes, sd_stream_t stream) {
+  if (!logits || !out || !ws || n_tok < 1 || n_tok > 65535 || V < 1 || V > INT32_MAX - 1 || ld < V)
     return SD_EINVAL;
-  if (!aligned(logits, 4) || !aligned(out, 4)) return SD_EALIGN;
-  return from_hip(launch_argmax(logits, ld, n_tok, V, out, hs(stream)));
+  if (!aligned(logits, 4) || !aligned(out, 4) || !aligned(ws, 4)) return SD_EALIGN;
+  if (ws_bytes < argmax_ws_bytes(n_tok, V)) return SD_EWORKSPACE;
+  return from_hip(launch_argmax(logits, ld, n_tok, V, out, ws, hs(stream)));
 }
 
 }  // extern "C"

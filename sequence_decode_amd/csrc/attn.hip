@@ -17,8 +17,8 @@
 //   fp32 FMAs directly (v_fma_mix), with no conversion pass.
 // * Two passes over the chunk (scores, then values) with the chunk maximum in
 //   between, so no running rescale; partial (m, l, o[128]) per head and chunk.
-// * A second kernel merges the partials of each (sequence, head) in chunk
-//   order.  Every sum has a fixed shape, so a sequence's output bits do not
+// * A second kernel merges the partials of each (sequence, head) with fixed
+//   reduction shapes.  Every sum has a fixed shape, so a sequence's output bits do not
 //   depend on the other sequences in the call.
 #include <math.h>
 
@@ -85,16 +85,31 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   }
   const uint16_t* kbase = A.k + (int64_t)g * A.ld_head + 8 * dg;
   const uint16_t* vbase = A.v + (int64_t)g * A.ld_head + 8 * dg;
+  constexpr int STEPS = C / 16;  // keys of one lane: wave * 64 + step * 4 + kslot
+
+  // All key and value rows of this lane are requested before any arithmetic, so
+  // the workgroup waits for one memory latency rather than one per step.
+  u32x4a kk[STEPS], vv[STEPS];
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    const int jl = wave * 64 + step * 4 + kslot;
+    kk[step] = u32x4a{0u, 0u, 0u, 0u};
+    if (jl < nk) kk[step] = *reinterpret_cast<const u32x4a*>(kbase + (int64_t)(j0 + jl) * A.ld_tok);
+  }
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    const int jl = wave * 64 + step * 4 + kslot;
+    vv[step] = u32x4a{0u, 0u, 0u, 0u};
+    if (jl < nk) vv[step] = *reinterpret_cast<const u32x4a*>(vbase + (int64_t)(j0 + jl) * A.ld_tok);
+  }
 
   // ---- pass 1: scores
-#pragma unroll 4
-  for (int step = 0; step < C / 16; ++step) {
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
     const int jl = wave * 64 + step * 4 + kslot;
     const bool valid = jl < nk;
-    u32x4a kk = {0u, 0u, 0u, 0u};
-    if (valid) kk = *reinterpret_cast<const u32x4a*>(kbase + (int64_t)(j0 + jl) * A.ld_tok);
     float kf[8];
-    unpack8(kk, kf);
+    unpack8(kk[step], kf);
     float pz[kAttnGroup];
 #pragma unroll
     for (int hh = 0; hh < kAttnGroup; ++hh) {
@@ -104,9 +119,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       pz[hh] = acc;
     }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-      for (int hh = 0; hh < kAttnGroup; ++hh) pz[hh] = fadd(pz[hh], __shfl_xor(pz[hh], m, 64));
+    for (int hh = 0; hh < kAttnGroup; ++hh) pz[hh] = row16_sum_fixed(pz[hh]);
     if (dg == 0) {
       f32x4 z;
       z.x = valid ? fmul(pz[0], scale) : -INFINITY;
@@ -154,13 +167,12 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   for (int hh = 0; hh < kAttnGroup; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[hh][e] = 0.0f;
-#pragma unroll 4
-  for (int step = 0; step < C / 16; ++step) {
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
     const int jl = wave * 64 + step * 4 + kslot;
     if (jl < nk) {
-      const u32x4a vv = *reinterpret_cast<const u32x4a*>(vbase + (int64_t)(j0 + jl) * A.ld_tok);
       float vf[8];
-      unpack8(vv, vf);
+      unpack8(vv[step], vf);
       const f32x4 pw = s_z[jl];
       const float pr[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
@@ -172,12 +184,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
   for (int hh = 0; hh < kAttnGroup; ++hh)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = o[hh][e];
-      v = fadd(v, __shfl_xor(v, 16, 64));
-      v = fadd(v, __shfl_xor(v, 32, 64));
-      o[hh][e] = v;
-    }
+    for (int e = 0; e < 8; ++e) o[hh][e] = cross_row_sum_fixed(o[hh][e]);
   if (kslot == 0)
 #pragma unroll
     for (int hh = 0; hh < kAttnGroup; ++hh)
@@ -199,34 +206,77 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   }
 }
 
-// Grid (n_seq * H_q); thread d of the head dimension.  Merges the chunks of
-// one (sequence, head) in chunk order; optionally also emits the q8 blocks of
-// the output row (the quantized input of the output projection).
-__global__ __launch_bounds__(128) void k_attn_combine(SeqArgs seqs, int H_q,
+// Grid (n_seq * H_q), 256 threads.  Merges the chunk partials of one
+// (sequence, head): M = max_c m_c; w_c = exp(m_c - M); L = sum_c l_c w_c by a
+// fixed tree over chunk index; O[d] = sum_c o_c[d] w_c with chunks split into
+// two interleaved halves (threads 0..127 take even chunks, 128..255 odd ones,
+// each in chunk order) that are then added.  Every shape depends only on the
+// sequence's chunk count.  Optionally also emits the q8 blocks of the output
+// row (the quantized input of the output projection).
+constexpr int kMaxChunks = SD_MAX_CTX / SD_ATTN_CHUNK;
+
+__global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
                                                       const float* __restrict__ part,
                                                       float* __restrict__ out, int8_t* oq, float* od) {
+  __shared__ float s_w[kMaxChunks];
+  __shared__ float s_red[256];
+  __shared__ float s_o[HD];
   const int s = blockIdx.x / H_q;
   const int h = blockIdx.x - s * H_q;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const SeqArg& A = seqs.s[s];
-  const float* base = part + ((int64_t)A.partial_begin + (int64_t)h * A.n_chunks) * PF;
-  float M = -INFINITY;
-  for (int c = 0; c < A.n_chunks; ++c) M = fmaxf(M, base[(int64_t)c * PF]);
-  float L = 0.0f, O = 0.0f;
-  for (int c = 0; c < A.n_chunks; ++c) {
-    const float* pc = base + (int64_t)c * PF;
-    const float e = expf(fsub(pc[0], M));
-    L = fadd(L, fmul(pc[1], e));
-    O = fadd(O, fmul(pc[4 + d], e));
+  const int nc = A.n_chunks;
+  const float* base = part + ((int64_t)A.partial_begin + (int64_t)h * nc) * PF;
+
+  // maximum of the chunk maxima (exact, order-free)
+  float mx = -INFINITY;
+  for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, base[(int64_t)c * PF]);
+  mx = group_max<64>(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  // weights, and L by a fixed tree: thread partials over c = tid, tid+256, ...
+  float lp = 0.0f;
+  for (int c = tid; c < nc; c += 256) {
+    const float w = expf(fsub(base[(int64_t)c * PF], M));
+    s_w[c] = w;
+    lp = fadd(lp, fmul(base[(int64_t)c * PF + 1], w));
   }
-  const float v = fdiv(O, L);
-  const int64_t idx = ((int64_t)s * H_q + h) * HD + d;
-  out[idx] = v;
-  if (oq) {
-    const float amax = group_max<32>(fabsf(v));
-    const float dd = q8_scale(amax);
-    oq[idx] = (int8_t)q8_code(v, dd);
-    if ((d & 31) == 0) od[idx >> 5] = dd;
+  lp = wave_sum_fixed(lp);
+  if ((tid & 63) == 0) s_red[tid >> 6] = lp;
+  __syncthreads();
+  const float L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
+  // values: two interleaved halves of the chunks, each in chunk order
+  const int d = tid & (HD - 1);
+  const int half = tid >> 7;
+  float O = 0.0f;
+  {
+    int c = half;
+    for (; c + 6 < nc; c += 8) {
+      const float a0 = base[(int64_t)c * PF + 4 + d];
+      const float a1 = base[(int64_t)(c + 2) * PF + 4 + d];
+      const float a2 = base[(int64_t)(c + 4) * PF + 4 + d];
+      const float a3 = base[(int64_t)(c + 6) * PF + 4 + d];
+      O = fadd(O, fmul(a0, s_w[c]));
+      O = fadd(O, fmul(a1, s_w[c + 2]));
+      O = fadd(O, fmul(a2, s_w[c + 4]));
+      O = fadd(O, fmul(a3, s_w[c + 6]));
+    }
+    for (; c < nc; c += 2) O = fadd(O, fmul(base[(int64_t)c * PF + 4 + d], s_w[c]));
+  }
+  if (half == 1) s_o[d] = O;
+  __syncthreads();
+  if (half == 0) {
+    const float v = fdiv(fadd(O, s_o[d]), L);
+    const int64_t idx = ((int64_t)s * H_q + h) * HD + d;
+    out[idx] = v;
+    if (oq) {
+      const float amax = group_max<32>(fabsf(v));
+      const float dd = q8_scale(amax);
+      oq[idx] = (int8_t)q8_code(v, dd);
+      if ((d & 31) == 0) od[idx >> 5] = dd;
+    }
   }
 }
 
@@ -254,7 +304,7 @@ hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_
   hipLaunchKernelGGL(k_attn_chunk, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(seqs.n_seq * H_q), dim3(HD), 0, st, seqs, H_q, partials,
+  hipLaunchKernelGGL(k_attn_combine, dim3(seqs.n_seq * H_q), dim3(256), 0, st, seqs, H_q, partials,
                      out, oq, od);
   return hipGetLastError();
 }

@@ -58,11 +58,16 @@ __device__ __forceinline__ float dpp_mov(float v) {
 // which return the lower and the upper partner in fixed operand order).  Every
 // level adds two equal-shaped subtree sums, so all 64 lanes end with the same
 // bits, and the tree depends on nothing but the lane index.
-__device__ __forceinline__ float wave_sum_fixed(float v) {
+__device__ __forceinline__ float row16_sum_fixed(float v) {
   v = fadd(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
   v = fadd(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
   v = fadd(v, dpp_mov<0x141>(v));  // row_half_mirror: 7 - lane within 8
   v = fadd(v, dpp_mov<0x140>(v));  // row_mirror: 15 - lane within 16
+  return v;
+}
+
+// Sum of the four 16-lane rows (lanes l, l^16, l^32, l^48): the last two levels.
+__device__ __forceinline__ float cross_row_sum_fixed(float v) {
   {
     auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
                                               __builtin_bit_cast(uint32_t, v), false, false);
@@ -75,6 +80,8 @@ __device__ __forceinline__ float wave_sum_fixed(float v) {
   }
   return v;
 }
+
+__device__ __forceinline__ float wave_sum_fixed(float v) { return cross_row_sum_fixed(row16_sum_fixed(v)); }
 
 // Maximum over a contiguous group of `width` lanes (exact and order-free).
 template <int width>

@@ -41,33 +41,47 @@ __global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x
   quantize_lane(v, valid, xq + t * K + b * 32 + lane32, xd + t * nb + b, lane32);
 }
 
-// One workgroup per token row.  The sum of squares is accumulated per thread
-// over a fixed stride, then combined by fixed wave and workgroup trees.
-__global__ __launch_bounds__(256) void k_rmsnorm_q8(const float* __restrict__ x, int64_t ldx,
-                                                    int64_t D, const float* __restrict__ gamma,
-                                                    float eps, int8_t* __restrict__ xq,
-                                                    float* __restrict__ xd, float* y) {
-  __shared__ float part[4];
+// One workgroup of 1024 threads per token row, the row held in registers
+// (EPT values per thread, element j*1024 + tid).  The sum of squares runs per
+// thread in j order, then over the 64 lanes of a wave (fixed tree), then over
+// the 16 waves in wave order.
+template <int EPT>
+__global__ __launch_bounds__(1024) void k_rmsnorm_q8(const float* __restrict__ x, int64_t ldx,
+                                                     int64_t D, const float* __restrict__ gamma,
+                                                     float eps, int8_t* __restrict__ xq,
+                                                     float* __restrict__ xd, float* y) {
+  __shared__ float part[16];
   const int t = blockIdx.x;
+  const int tid = threadIdx.x;
   const float* xr = x + (int64_t)t * ldx;
-  float ss = 0.0f;
-  for (int64_t i = threadIdx.x; i < D; i += 256) {
-    const float v = xr[i];
-    ss = fadd(ss, fmul(v, v));
+  constexpr bool kGammaEarly = EPT <= 16;  // registers for gamma too (no spills up to 16)
+  float v[EPT], gm[kGammaEarly ? EPT : 1];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int64_t i = (int64_t)j * 1024 + tid;
+    v[j] = i < D ? xr[i] : 0.0f;
+    if (kGammaEarly) gm[kGammaEarly ? j : 0] = i < D ? gamma[i] : 0.0f;
   }
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) ss = fadd(ss, fmul(v[j], v[j]));
   ss = wave_sum_fixed(ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
-  const float total = fadd(fadd(part[0], part[1]), fadd(part[2], part[3]));
+  float total = part[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) total = fadd(total, part[w]);
   const float r = fdiv(1.0f, sqrtf(fadd(fdiv(total, (float)D), eps)));
   const int64_t nb = D / 32;
-  for (int64_t base = 0; base < D; base += 256) {
-    const int64_t i = base + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int64_t i = (int64_t)j * 1024 + tid;
+    if ((int64_t)j * 1024 >= D) break;  // uniform: D is a multiple of 32, blocks stay whole
     const bool valid = i < D;
-    const float v = valid ? fmul(fmul(xr[i], r), gamma[i]) : 0.0f;
-    if (valid && y) y[(int64_t)t * D + i] = v;
-    quantize_lane(v, valid, xq + (int64_t)t * D + i, xd + (int64_t)t * nb + (i >> 5),
-                  threadIdx.x & 31);
+    const float gj = kGammaEarly ? gm[kGammaEarly ? j : 0] : (valid ? gamma[i] : 0.0f);
+    const float o = valid ? fmul(fmul(v[j], r), gj) : 0.0f;
+    if (valid && y) y[(int64_t)t * D + i] = o;
+    quantize_lane(o, valid, xq + (int64_t)t * D + i, xd + (int64_t)t * nb + (i >> 5), tid & 31);
   }
 }
 
@@ -109,15 +123,11 @@ __device__ __forceinline__ void better(float& v, int32_t& i, float ov, int32_t o
   }
 }
 
-__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int64_t ld,
-                                                int64_t V, int32_t* __restrict__ out) {
-  __shared__ float sv[4];
-  __shared__ int32_t si[4];
-  const int t = blockIdx.x;
-  const float* row = logits + (int64_t)t * ld;
-  float bv = -INFINITY;
-  int32_t bi = (int32_t)V;
-  for (int64_t j = threadIdx.x; j < V; j += 256) better(bv, bi, row[j], (int32_t)j);
+// Pass 1: workgroup (t, slice) takes kArgSlice logits of row t; every thread
+// issues all its loads first, then selects; the workgroup's winner goes to ws.
+constexpr int kArgSlice = 8192;
+
+__device__ __forceinline__ void block_best(float& bv, int32_t& bi, float* sv, int32_t* si) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     const float ov = __shfl_xor(bv, m, 64);
@@ -129,12 +139,53 @@ __global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits
     si[threadIdx.x >> 6] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float v = sv[0];
-    int32_t i = si[0];
-    for (int w = 1; w < 4; ++w) better(v, i, sv[w], si[w]);
-    out[t] = i >= V ? 0 : i;
+  bv = sv[0];
+  bi = si[0];
+  for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
+}
+
+__global__ __launch_bounds__(256) void k_argmax_slices(const float* __restrict__ logits, int64_t ld,
+                                                       int64_t V, float* __restrict__ wv,
+                                                       int32_t* __restrict__ wi) {
+  __shared__ float sv[4];
+  __shared__ int32_t si[4];
+  const int t = blockIdx.y;
+  const int64_t base = (int64_t)blockIdx.x * kArgSlice;
+  const float* row = logits + (int64_t)t * ld;
+  constexpr int PER = kArgSlice / 256;  // 32 values per thread
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t i = base + (int64_t)j * 256 + threadIdx.x;
+    v[j] = i < V ? row[i] : -INFINITY;
   }
+  float bv = -INFINITY;
+  int32_t bi = (int32_t)V;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t i = base + (int64_t)j * 256 + threadIdx.x;
+    if (i < V) better(bv, bi, v[j], (int32_t)i);
+  }
+  block_best(bv, bi, sv, si);
+  if (threadIdx.x == 0) {
+    wv[(int64_t)t * gridDim.x + blockIdx.x] = bv;
+    wi[(int64_t)t * gridDim.x + blockIdx.x] = bi;
+  }
+}
+
+// Pass 2: one workgroup per row reduces the slice winners.
+__global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ wv,
+                                                      const int32_t* __restrict__ wi, int n_slices,
+                                                      int64_t V, int32_t* __restrict__ out) {
+  __shared__ float sv[4];
+  __shared__ int32_t si[4];
+  const int t = blockIdx.x;
+  float bv = -INFINITY;
+  int32_t bi = (int32_t)V;
+  for (int j = threadIdx.x; j < n_slices; j += 256)
+    better(bv, bi, wv[(int64_t)t * n_slices + j], wi[(int64_t)t * n_slices + j]);
+  block_best(bv, bi, sv, si);
+  if (threadIdx.x == 0) out[t] = bi >= V ? 0 : bi;
 }
 
 }  // namespace
@@ -149,7 +200,14 @@ hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
 
 hipError_t launch_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D, const float* gamma,
                              float eps, int8_t* xq, float* xd, float* y, hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm_q8, dim3(n_tok), dim3(256), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+  if (D <= 4096)
+    hipLaunchKernelGGL(k_rmsnorm_q8<4>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+  else if (D <= 8192)
+    hipLaunchKernelGGL(k_rmsnorm_q8<8>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+  else if (D <= 16384)
+    hipLaunchKernelGGL(k_rmsnorm_q8<16>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_q8<32>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
   return hipGetLastError();
 }
 
@@ -167,9 +225,21 @@ hipError_t launch_embed(const uint16_t* table, int64_t V, int64_t H, const int32
   return hipGetLastError();
 }
 
+size_t argmax_ws_bytes(int n_tok, int64_t V) {
+  const int64_t slices = (V + kArgSlice - 1) / kArgSlice;
+  return (size_t)n_tok * slices * 8;
+}
+
 hipError_t launch_argmax(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(n_tok), dim3(256), 0, st, logits, ld, V, out);
+                         void* ws, hipStream_t st) {
+  const int64_t slices = (V + kArgSlice - 1) / kArgSlice;
+  float* wv = static_cast<float*>(ws);
+  int32_t* wi = reinterpret_cast<int32_t*>(wv + (int64_t)n_tok * slices);
+  hipLaunchKernelGGL(k_argmax_slices, dim3((unsigned)slices, n_tok), dim3(256), 0, st, logits, ld, V,
+                     wv, wi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_argmax_final, dim3(n_tok), dim3(256), 0, st, wv, wi, (int)slices, V, out);
   return hipGetLastError();
 }
 

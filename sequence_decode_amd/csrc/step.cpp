@@ -22,7 +22,7 @@ namespace {
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct StepLayout {
-  size_t x, aq, ad, qkv, attn_o, gu, part, total;
+  size_t x, aq, ad, qkv, attn_o, gu, part, arg, total;
 };
 
 bool model_ok(const sd_model* m) {
@@ -55,6 +55,7 @@ StepLayout layout(const sd_model* m, int n, int max_ctx) {
   L.attn_o = off; off = align_up(off + (size_t)n * m->n_heads * m->head_dim * 4, 256);
   L.gu = off;     off = align_up(off + (size_t)n * 2 * m->ffn * 4, 256);
   L.part = off;   off = align_up(off + (size_t)n * chunks * m->n_heads * kAttnPartialFloats * 4, 256);
+  L.arg = off;    off = align_up(off + argmax_ws_bytes(n, m->vocab), 256);
   L.total = off;
   return L;
 }
@@ -78,6 +79,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   for (int s = 0; s < n; ++s) {
     const sd_step_seq& q = io->seqs[s];
     if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || q.pos >= q.capacity) return SD_EINVAL;
+    if (q.pos + 1 > SD_MAX_CTX) return SD_EUNSUPPORTED;
     if (((uintptr_t)q.k_cache % 16) || ((uintptr_t)q.v_cache % 16)) return SD_EALIGN;
     if (q.pos + 1 > max_ctx) max_ctx = q.pos + 1;
   }
@@ -139,7 +141,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   }
   SD_TRY(launch_rmsnorm_q8(x, H, n, H, m->out_norm, m->rms_eps, aq, ad, nullptr, st));
   SD_TRY(launch_qgemv(m->w_lm_head, m->vocab, H, aq, ad, n, nullptr, io->logits, m->vocab, st));
-  SD_TRY(launch_argmax(io->logits, m->vocab, n, m->vocab, io->next_tokens, st));
+  SD_TRY(launch_argmax(io->logits, m->vocab, n, m->vocab, io->next_tokens, ws + W.arg, st));
 #undef SD_TRY
   return SD_OK;
 }

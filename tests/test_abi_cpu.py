@@ -103,7 +103,9 @@ def test_rope_kv_and_glue_rejections(L):
     assert L.sd_rmsnorm_q8(FAKE, 100, 1, 100, FAKE, 1e-6, FAKE, FAKE, None, None) == SD_EUNSUPPORTED
     assert L.sd_rmsnorm_q8(FAKE, 128, 1, 128, FAKE, -1.0, FAKE, FAKE, None, None) == SD_EINVAL
     assert L.sd_swiglu_q8(FAKE, 100, 1, 64, FAKE, FAKE, None, None) == SD_EINVAL
-    assert L.sd_argmax_rows(FAKE, 10, 1, 11, FAKE, None) == SD_EINVAL
+    assert L.sd_argmax_rows(FAKE, 10, 1, 11, FAKE, FAKE, 64, None) == SD_EINVAL
+    assert L.sd_argmax_workspace_bytes(4, 151936) == 4 * 19 * 8
+    assert L.sd_argmax_rows(FAKE, 151936, 4, 151936, FAKE, FAKE, 4 * 19 * 8 - 1, None) == SD_EWORKSPACE
     assert L.sd_embed_f16(FAKE, 0, 16, FAKE, 1, FAKE, None) == SD_EINVAL
 
 

@@ -11,12 +11,12 @@
 //   the grid is the sum of all sequences' units, which fills 256 CUs even for
 //   four sequences (a sequence-per-workgroup split would give 32 units).
 // * A workgroup loads each key and value row of its chunk once for the four
-//   query heads that share the KV head.  Lane = 16 * key_slot + dim_group: a
-//   wave reads four 256-byte key rows per instruction (16 B per lane), and each
-//   lane keeps its 8 query dims of the 4 heads in registers.  fp16 K/V enter
-//   fp32 FMAs directly (v_fma_mix), with no conversion pass.
-// * Two passes over the chunk (scores, then values) with the chunk maximum in
-//   between, so no running rescale; partial (m, l, o[128]) per head and chunk.
+//   query heads that share the KV head; every load is issued before any
+//   arithmetic.  Scores come from MFMA (fp16 keys as stored, the fp32 query as
+//   an exact fp16 hi + lo pair), the weighted value sum from v_fma_mix (fp16
+//   values straight into fp32 FMAs).
+// * Each wave keeps its own softmax partial over its 64 keys, and the four
+//   merge in wave order: partial (m, l, o[128]) per head and chunk.
 // * A second kernel merges the partials of each (sequence, head) with fixed
 //   reduction shapes.  Every sum has a fixed shape, so a sequence's output bits do not
 //   depend on the other sequences in the call.
@@ -52,11 +52,33 @@ __device__ __forceinline__ int find_seq(const SeqArgs& a, int u) {
   return s;
 }
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float cross_row_max(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
+}
+
+// One workgroup = (sequence, KV head g, chunk of C keys); wave w owns keys
+// w*64 .. w*64+63 of the chunk.
+//  * Scores by MFMA (v_mfma_f32_16x16x32_f16): A = 16 keys x 32 dims of K (fp16
+//    as stored), B = 32 dims x 16 columns of q^T (the 4 heads of the group, the
+//    other 12 columns zero).  q is fp32; it enters as q_hi + q_lo (two fp16
+//    parts, q - q_hi - q_lo ~ 2^-22 |q|), so each fp16 x fp16 product is exact
+//    and the score keeps fp32 accuracy.
+//  * Each wave forms its own softmax partial (max, sum of weights, weighted
+//    value sum) over its 64 keys; the weighted values use v_fma_mix (fp16 V
+//    straight into fp32 FMAs).  The 4 wave partials merge in wave order.
 __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q, int64_t ld_q,
                                                     SeqArgs seqs, int H_q, float scale,
                                                     float* __restrict__ part) {
-  __shared__ f32x4 s_z[C];            // scores, then weights: [key][head of the group]
-  __shared__ float s_red[2][4][4];    // [max|sum][wave][head]
+  __shared__ __attribute__((aligned(16))) float s_p[4][64][kAttnGroup];  // [wave][key][head]
+  __shared__ float s_m[4][kAttnGroup], s_l[4][kAttnGroup];
   __shared__ float s_o[4][kAttnGroup * HD];
 
   const int s = find_seq(seqs, blockIdx.x);
@@ -70,110 +92,108 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int col = lane & 15;   // MFMA column / row-in-tile index
+  const int kg = lane >> 4;    // MFMA k-group (8 of the 32 dims)
+
+  // ---- K tiles (A operands), issued first: tile t = keys wave*64 + 16t + col
+  const uint16_t* kbase = A.k + (int64_t)g * A.ld_head;
+  u32x4a ka[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int jl = wave * 64 + 16 * t + col;
+    const uint16_t* kr = kbase + (int64_t)(j0 + jl) * A.ld_tok + 8 * kg;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      ka[t][kk] = u32x4a{0u, 0u, 0u, 0u};
+      if (jl < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+    }
+  }
+  // ---- V rows for the weighted sum: lane = 16 * kslot + dg, key wave*64 + 4*step + kslot
   const int kslot = lane >> 4;
   const int dg = lane & 15;
-
-  // query dims 8*dg .. 8*dg+7 of the four heads of group g
-  float qv[kAttnGroup][8];
-#pragma unroll
-  for (int hh = 0; hh < kAttnGroup; ++hh) {
-    const f32x4* qp = reinterpret_cast<const f32x4*>(q + (int64_t)s * ld_q +
-                                                     (int64_t)(g * kAttnGroup + hh) * HD + 8 * dg);
-    const f32x4 a = qp[0], b = qp[1];
-    qv[hh][0] = a.x; qv[hh][1] = a.y; qv[hh][2] = a.z; qv[hh][3] = a.w;
-    qv[hh][4] = b.x; qv[hh][5] = b.y; qv[hh][6] = b.z; qv[hh][7] = b.w;
-  }
-  const uint16_t* kbase = A.k + (int64_t)g * A.ld_head + 8 * dg;
   const uint16_t* vbase = A.v + (int64_t)g * A.ld_head + 8 * dg;
-  constexpr int STEPS = C / 16;  // keys of one lane: wave * 64 + step * 4 + kslot
-
-  // All key and value rows of this lane are requested before any arithmetic, so
-  // the workgroup waits for one memory latency rather than one per step.
-  u32x4a kk[STEPS], vv[STEPS];
+  u32x4a vv[16];
 #pragma unroll
-  for (int step = 0; step < STEPS; ++step) {
-    const int jl = wave * 64 + step * 4 + kslot;
-    kk[step] = u32x4a{0u, 0u, 0u, 0u};
-    if (jl < nk) kk[step] = *reinterpret_cast<const u32x4a*>(kbase + (int64_t)(j0 + jl) * A.ld_tok);
-  }
-#pragma unroll
-  for (int step = 0; step < STEPS; ++step) {
+  for (int step = 0; step < 16; ++step) {
     const int jl = wave * 64 + step * 4 + kslot;
     vv[step] = u32x4a{0u, 0u, 0u, 0u};
     if (jl < nk) vv[step] = *reinterpret_cast<const u32x4a*>(vbase + (int64_t)(j0 + jl) * A.ld_tok);
   }
-
-  // ---- pass 1: scores
+  // ---- q^T (B operands) as fp16 hi + lo: column col = head of the group (< 4)
+  h8 bhi[4], blo[4];
 #pragma unroll
-  for (int step = 0; step < STEPS; ++step) {
-    const int jl = wave * 64 + step * 4 + kslot;
-    const bool valid = jl < nk;
-    float kf[8];
-    unpack8(kk[step], kf);
-    float pz[kAttnGroup];
+  for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int hh = 0; hh < kAttnGroup; ++hh) {
-      float acc = fmul(qv[hh][0], kf[0]);
-#pragma unroll
-      for (int e = 1; e < 8; ++e) acc = ffma(qv[hh][e], kf[e], acc);
-      pz[hh] = acc;
+    for (int j = 0; j < 8; ++j) {
+      bhi[kk][j] = (_Float16)0.0f;
+      blo[kk][j] = (_Float16)0.0f;
     }
+    if (col < kAttnGroup) {
+      const f32x4* qp = reinterpret_cast<const f32x4*>(
+          q + (int64_t)s * ld_q + (int64_t)(g * kAttnGroup + col) * HD + 32 * kk + 8 * kg);
+      const f32x4 a = qp[0], b = qp[1];
+      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int hh = 0; hh < kAttnGroup; ++hh) pz[hh] = row16_sum_fixed(pz[hh]);
-    if (dg == 0) {
-      f32x4 z;
-      z.x = valid ? fmul(pz[0], scale) : -INFINITY;
-      z.y = valid ? fmul(pz[1], scale) : -INFINITY;
-      z.z = valid ? fmul(pz[2], scale) : -INFINITY;
-      z.w = valid ? fmul(pz[3], scale) : -INFINITY;
-      s_z[jl] = z;
+      for (int j = 0; j < 8; ++j) {
+        const _Float16 hi = (_Float16)x[j];
+        bhi[kk][j] = hi;
+        blo[kk][j] = (_Float16)fsub(x[j], (float)hi);
+      }
     }
   }
+  // ---- scores: D[key][head] per 16-key tile; lane holds keys 16t + 4*kg + r of head col
+  float z[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const h8 av = __builtin_bit_cast(h8, ka[t][kk]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int jl = wave * 64 + 16 * t + 4 * kg + r;
+      z[t][r] = jl < nk ? fmul(acc[r], scale) : -INFINITY;
+    }
+  }
+  // ---- this wave's softmax partial, per head (lanes with col < 4 carry heads)
+  float mw = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
+  mw = cross_row_max(mw);
+  float lw = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pz = z[t][r] == -INFINITY ? 0.0f : expf(fsub(z[t][r], mw));
+      lw = fadd(lw, pz);
+      if (col < kAttnGroup) s_p[wave][16 * t + 4 * kg + r][col] = pz;
+    }
+  lw = cross_row_sum_fixed(lw);
+  if (lane < kAttnGroup) {
+    s_m[wave][lane] = mw;
+    s_l[wave][lane] = lw;
+  }
   __syncthreads();
 
-  // ---- chunk maximum and weights (thread tid owns key tid)
-  f32x4 z = s_z[tid];
-  float mx[4] = {z.x, z.y, z.z, z.w};
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) mx[hh] = group_max<64>(mx[hh]);
-  if (lane == 0)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) s_red[0][wave][hh] = mx[hh];
-  __syncthreads();
-  float m[4], p[4], l[4];
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    m[hh] = fmaxf(fmaxf(s_red[0][0][hh], s_red[0][1][hh]), fmaxf(s_red[0][2][hh], s_red[0][3][hh]));
-  }
-  p[0] = expf(fsub(z.x, m[0]));
-  p[1] = expf(fsub(z.y, m[1]));
-  p[2] = expf(fsub(z.z, m[2]));
-  p[3] = expf(fsub(z.w, m[3]));
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) l[hh] = wave_sum_fixed(p[hh]);
-  if (lane == 0)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) s_red[1][wave][hh] = l[hh];
-  {
-    f32x4 pw;
-    pw.x = p[0]; pw.y = p[1]; pw.z = p[2]; pw.w = p[3];
-    s_z[tid] = pw;
-  }
-  __syncthreads();
-
-  // ---- pass 2: weighted values
+  // ---- weighted values of this wave's keys
   float o[kAttnGroup][8];
 #pragma unroll
   for (int hh = 0; hh < kAttnGroup; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[hh][e] = 0.0f;
 #pragma unroll
-  for (int step = 0; step < STEPS; ++step) {
-    const int jl = wave * 64 + step * 4 + kslot;
-    if (jl < nk) {
+  for (int step = 0; step < 16; ++step) {
+    const int kl = step * 4 + kslot;
+    if (wave * 64 + kl < nk) {
       float vf[8];
       unpack8(vv[step], vf);
-      const f32x4 pw = s_z[jl];
+      const f32x4 pw = *reinterpret_cast<const f32x4*>(&s_p[wave][kl][0]);
       const float pr[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
       for (int hh = 0; hh < kAttnGroup; ++hh)
@@ -192,16 +212,24 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       for (int e = 0; e < 8; ++e) s_o[wave][hh * HD + 8 * dg + e] = o[hh][e];
   __syncthreads();
 
+  // ---- merge the four wave partials in wave order
   for (int idx = tid; idx < kAttnGroup * HD; idx += 256) {
     const int hh = idx / HD;
     const int d = idx - hh * HD;
-    const float v = fadd(fadd(s_o[0][idx], s_o[1][idx]), fadd(s_o[2][idx], s_o[3][idx]));
+    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+    float O = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float e = s_m[w][hh] == -INFINITY ? 0.0f : expf(fsub(s_m[w][hh], M));
+      O = fadd(O, fmul(s_o[w][idx], e));
+      L = fadd(L, fmul(s_l[w][hh], e));
+    }
     const int h = g * kAttnGroup + hh;
     float* dst = part + ((int64_t)A.partial_begin + (int64_t)h * A.n_chunks + c) * PF;
-    dst[4 + d] = v;
+    dst[4 + d] = O;
     if (d == 0) {
-      dst[0] = m[hh];
-      dst[1] = fadd(fadd(s_red[1][0][hh], s_red[1][1][hh]), fadd(s_red[1][2][hh], s_red[1][3][hh]));
+      dst[0] = M;
+      dst[1] = L;
     }
   }
 }

@@ -33,17 +33,6 @@ constexpr int C = kAttnChunk;
 constexpr int HD = kAttnHeadDim;
 constexpr int PF = kAttnPartialFloats;
 
-__device__ __forceinline__ void unpack8(const u32x4a& k, float* f) {
-  f[0] = f16_bits_to_f32(k.x);
-  f[1] = f16_bits_to_f32(k.x >> 16);
-  f[2] = f16_bits_to_f32(k.y);
-  f[3] = f16_bits_to_f32(k.y >> 16);
-  f[4] = f16_bits_to_f32(k.z);
-  f[5] = f16_bits_to_f32(k.z >> 16);
-  f[6] = f16_bits_to_f32(k.w);
-  f[7] = f16_bits_to_f32(k.w >> 16);
-}
-
 __device__ __forceinline__ int find_seq(const SeqArgs& a, int u) {
   int s = 0;
 #pragma unroll
@@ -53,7 +42,10 @@ __device__ __forceinline__ int find_seq(const SeqArgs& a, int u) {
 }
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) s4* lds_s4_ptr;
 
 __device__ __forceinline__ float cross_row_max(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
@@ -64,22 +56,42 @@ __device__ __forceinline__ float cross_row_max(float v) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
 }
 
+// fp32 x as the fp16 pair (hi, lo) with hi + lo = x to about 2^-22 |x|.
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)fsub(x, (float)hi);
+}
+
+// Byte layout of one wave's V rows in LDS: row r (64 keys, 256 B each) keeps
+// its eight 32-byte segments at positions seg ^ vswz(r).  The permutation makes
+// the transposed reads below conflict-free: the 32 lanes of a half-wave read
+// eight rows whose swizzles differ, so their 32-byte pieces land on disjoint
+// banks.
+constexpr int kRowBytes = HD * 2;
+constexpr int kWaveKeys = 64;
+constexpr int kWaveVBytes = kWaveKeys * kRowBytes;
+__device__ __forceinline__ int vswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
 // One workgroup = (sequence, KV head g, chunk of C keys); wave w owns keys
-// w*64 .. w*64+63 of the chunk.
-//  * Scores by MFMA (v_mfma_f32_16x16x32_f16): A = 16 keys x 32 dims of K (fp16
-//    as stored), B = 32 dims x 16 columns of q^T (the 4 heads of the group, the
-//    other 12 columns zero).  q is fp32; it enters as q_hi + q_lo (two fp16
-//    parts, q - q_hi - q_lo ~ 2^-22 |q|), so each fp16 x fp16 product is exact
-//    and the score keeps fp32 accuracy.
-//  * Each wave forms its own softmax partial (max, sum of weights, weighted
-//    value sum) over its 64 keys; the weighted values use v_fma_mix (fp16 V
-//    straight into fp32 FMAs).  The 4 wave partials merge in wave order.
+// 64w .. 64w+63 of the chunk.  Both contractions run on v_mfma_f32_16x16x32_f16
+// with the four query heads of the group as the first 4 of 16 columns:
+//  * scores S^T = K q^T: A = 16 keys x 32 dims of K (fp16 as stored), B = q^T as
+//    the exact fp16 pair hi + lo of the fp32 query.  Tile t = (key block b =
+//    t/2, half = t%2) puts key 32b + 8(m/4) + 4 half + m%4 in row m, so that a
+//    lane's score slots are already the key slots of the P^T operand below.
+//  * the chunk's softmax uses one maximum per head, shared by the four waves
+//    through LDS, so the wave partials add without rescaling.
+//  * weighted values O^T = V^T P^T: A = 16 dims x 32 keys of V^T, read from the
+//    LDS copy of the wave's V rows with ds_read_b64_tr_b16 (each 16-lane group
+//    gathers 4 keys x 4 dims per read), B = the weights as fp16 hi + lo.
+// The four wave partials are added in wave order.  Keys past the end of the
+// sequence get weight 0; their V rows are clamped to the last key, so every
+// product that enters a sum is finite.
 __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q, int64_t ld_q,
                                                     SeqArgs seqs, int H_q, float scale,
                                                     float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float s_p[4][64][kAttnGroup];  // [wave][key][head]
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v[4 * kWaveVBytes];  // V rows, then O partials
   __shared__ float s_m[4][kAttnGroup], s_l[4][kAttnGroup];
-  __shared__ float s_o[4][kAttnGroup * HD];
 
   const int s = find_seq(seqs, blockIdx.x);
   const SeqArg& A = seqs.s[s];
@@ -92,56 +104,69 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 15;   // MFMA column / row-in-tile index
-  const int kg = lane >> 4;    // MFMA k-group (8 of the 32 dims)
+  const int col = lane & 15;  // MFMA row (A loads) / column (B, D)
+  const int kg = lane >> 4;   // MFMA k-group
+  const int wk = wave * kWaveKeys;
 
-  // ---- K tiles (A operands), issued first: tile t = keys wave*64 + 16t + col
-  const uint16_t* kbase = A.k + (int64_t)g * A.ld_head;
+  // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
+  const int jk = wk + 8 * (col >> 2) + (col & 3);
+  const uint16_t* kr = A.k + (int64_t)g * A.ld_head + (int64_t)(j0 + jk) * A.ld_tok + 8 * kg;
   u32x4a ka[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int jl = wave * 64 + 16 * t + col;
-    const uint16_t* kr = kbase + (int64_t)(j0 + jl) * A.ld_tok + 8 * kg;
+    const int dj = 32 * (t >> 1) + 4 * (t & 1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       ka[t][kk] = u32x4a{0u, 0u, 0u, 0u};
-      if (jl < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+      if (jk + dj < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + dj * A.ld_tok + 32 * kk);
     }
   }
-  // ---- V rows for the weighted sum: lane = 16 * kslot + dg, key wave*64 + 4*step + kslot
-  const int kslot = lane >> 4;
-  const int dg = lane & 15;
-  const uint16_t* vbase = A.v + (int64_t)g * A.ld_head + 8 * dg;
-  u32x4a vv[16];
-#pragma unroll
-  for (int step = 0; step < 16; ++step) {
-    const int jl = wave * 64 + step * 4 + kslot;
-    vv[step] = u32x4a{0u, 0u, 0u, 0u};
-    if (jl < nk) vv[step] = *reinterpret_cast<const u32x4a*>(vbase + (int64_t)(j0 + jl) * A.ld_tok);
-  }
-  // ---- q^T (B operands) as fp16 hi + lo: column col = head of the group (< 4)
-  h8 bhi[4], blo[4];
+  // ---- q (score B operands): column col < 4 = head g*4 + col, dims 32kk + 8kg ..
+  f32x4 qv[4][2];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bhi[kk][j] = (_Float16)0.0f;
-      blo[kk][j] = (_Float16)0.0f;
-    }
+    qv[kk][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    qv[kk][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (col < kAttnGroup) {
       const f32x4* qp = reinterpret_cast<const f32x4*>(
           q + (int64_t)s * ld_q + (int64_t)(g * kAttnGroup + col) * HD + 32 * kk + 8 * kg);
-      const f32x4 a = qp[0], b = qp[1];
-      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 hi = (_Float16)x[j];
-        bhi[kk][j] = hi;
-        blo[kk][j] = (_Float16)fsub(x[j], (float)hi);
-      }
+      qv[kk][0] = qp[0];
+      qv[kk][1] = qp[1];
     }
   }
-  // ---- scores: D[key][head] per 16-key tile; lane holds keys 16t + 4*kg + r of head col
+  // ---- V rows of this wave -> LDS by DMA: instruction i fills rows 4i .. 4i+3;
+  // lane l writes row 4i + l/16 at 16-byte position l%16, which holds the row's
+  // 16-byte piece (l%16) ^ 2 vswz(row).
+  uint8_t* vw = s_v + wave * kWaveVBytes;
+  {
+    const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
+    const int jv = wk + (lane >> 4);
+    const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + jv) * A.ld_tok);
+    const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + nk - 1) * A.ld_tok);
+    const int64_t step4 = 4 * A.ld_tok * 2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int piece = (lane & 15) ^ (2 * vswz(r));
+      const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+    }
+  }
+
+  // ---- scores
+  h8 bhi[4], blo[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const float x[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
+                        qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      _Float16 hi, lo;
+      split_f16(x[j], hi, lo);
+      bhi[kk][j] = hi;
+      blo[kk][j] = lo;
+    }
+  }
   float z[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -152,83 +177,92 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], acc, 0, 0, 0);
     }
+    // D slot r of this lane = row 4kg + r = key wk + 32(t/2) + 8kg + 4(t%2) + r, head col
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int jl = wave * 64 + 16 * t + 4 * kg + r;
-      z[t][r] = jl < nk ? fmul(acc[r], scale) : -INFINITY;
+      const int jl = wk + 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
+      z[t][r] = (jl < nk && col < kAttnGroup) ? fmul(acc[r], scale) : -INFINITY;
     }
   }
-  // ---- this wave's softmax partial, per head (lanes with col < 4 carry heads)
-  float mw = -INFINITY;
+  // ---- the chunk maximum per head, shared by the four waves
+  {
+    float mw = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
-  mw = cross_row_max(mw);
+      for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
+    mw = cross_row_max(mw);
+    if (lane < kAttnGroup) s_m[wave][lane] = mw;
+  }
+  __syncthreads();
+  const int hc = col & (kAttnGroup - 1);
+  const float M = fmaxf(fmaxf(s_m[0][hc], s_m[1][hc]), fmaxf(s_m[2][hc], s_m[3][hc]));
+  // ---- weights, their sum, and the P^T operands (block b: slot j = tile 2b + j/4, slot j%4)
+  h8 phi[2], plo[2];
   float lw = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pz = z[t][r] == -INFINITY ? 0.0f : expf(fsub(z[t][r], mw));
+      const float pz = z[t][r] == -INFINITY ? 0.0f : expf(fsub(z[t][r], M));
       lw = fadd(lw, pz);
-      if (col < kAttnGroup) s_p[wave][16 * t + 4 * kg + r][col] = pz;
+      _Float16 hi, lo;
+      split_f16(pz, hi, lo);
+      phi[t >> 1][4 * (t & 1) + r] = hi;
+      plo[t >> 1][4 * (t & 1) + r] = lo;
     }
   lw = cross_row_sum_fixed(lw);
-  if (lane < kAttnGroup) {
-    s_m[wave][lane] = mw;
-    s_l[wave][lane] = lw;
-  }
-  __syncthreads();
+  if (lane < kAttnGroup) s_l[wave][lane] = lw;
 
-  // ---- weighted values of this wave's keys
-  float o[kAttnGroup][8];
+  // ---- weighted values: this wave's V rows have landed in LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // lane (col, kg) reads row 32b + 8kg + 4h + col/4, dims 16dt + 4(col%4) .. +3
+  const int vg = vswz(8 * kg + (col >> 2));
+  const int rbase = (8 * kg + (col >> 2)) * kRowBytes + 8 * (col & 3);
+  f32x4v o[8];
 #pragma unroll
-  for (int hh = 0; hh < kAttnGroup; ++hh)
+  for (int dt = 0; dt < 8; ++dt) {
+    o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    const int a0 = rbase + ((dt ^ vg) << 5);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.0f;
-#pragma unroll
-  for (int step = 0; step < 16; ++step) {
-    const int kl = step * 4 + kslot;
-    if (wave * 64 + kl < nk) {
-      float vf[8];
-      unpack8(vv[step], vf);
-      const f32x4 pw = *reinterpret_cast<const f32x4*>(&s_p[wave][kl][0]);
-      const float pr[4] = {pw.x, pw.y, pw.z, pw.w};
-#pragma unroll
-      for (int hh = 0; hh < kAttnGroup; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = ffma(pr[hh], vf[e], o[hh][e]);
+    for (int b = 0; b < 2; ++b) {
+      const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes));
+      const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes + 4 * kRowBytes));
+      const h8 av = __builtin_bit_cast(h8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[b], o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);
     }
   }
+  // D slot r of lane (col, kg) = dim 16dt + 4kg + r of head col; the wave's own
+  // V region (now read) takes its partial O[head][dim]
+  float* so = reinterpret_cast<float*>(vw);
+  if (col < kAttnGroup)
 #pragma unroll
-  for (int hh = 0; hh < kAttnGroup; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = cross_row_sum_fixed(o[hh][e]);
-  if (kslot == 0)
-#pragma unroll
-    for (int hh = 0; hh < kAttnGroup; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][hh * HD + 8 * dg + e] = o[hh][e];
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<f32x4*>(so + col * HD + 16 * dt + 4 * kg) =
+          f32x4{o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
   __syncthreads();
 
-  // ---- merge the four wave partials in wave order
-  for (int idx = tid; idx < kAttnGroup * HD; idx += 256) {
+  // ---- sum of the four wave partials, in wave order
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int idx = tid + 256 * rep;
     const int hh = idx / HD;
     const int d = idx - hh * HD;
-    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
     float O = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float e = s_m[w][hh] == -INFINITY ? 0.0f : expf(fsub(s_m[w][hh], M));
-      O = fadd(O, fmul(s_o[w][idx], e));
-      L = fadd(L, fmul(s_l[w][hh], e));
+      O = fadd(O, reinterpret_cast<const float*>(s_v + w * kWaveVBytes)[idx]);
+      L = fadd(L, s_l[w][hh]);
     }
+    const float Mh = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
     const int h = g * kAttnGroup + hh;
     float* dst = part + ((int64_t)A.partial_begin + (int64_t)h * A.n_chunks + c) * PF;
     dst[4 + d] = O;
     if (d == 0) {
-      dst[0] = M;
+      dst[0] = Mh;
       dst[1] = L;
     }
   }

@@ -110,6 +110,29 @@ int sd_qgemv_q8_0_batch(const void* w, int64_t N, int64_t K,
                         const float* residual, float* y, int64_t ldy,
                         sd_stream_t stream);
 
+/*
+ * sd_qgemv_q8_0_batch_path -- sd_qgemv_q8_0_batch with the kernel chosen by
+ * the caller, for the wide verify batches of "#1209 Speed up concurrent
+ * generation, fix QFUSE, and improve prefill monitoring", "What changed and
+ * why" item 1 (several proposed tokens per sequence checked together, with
+ * 8/12/16-row capacities).
+ *   path  SD_GEMV_AUTO   the kernel sd_qgemv_q8_0_batch uses (the narrow
+ *                        kernel up to 8 tokens and K <= 16384, else MFMA);
+ *         SD_GEMV_NARROW v_dot4 kernels (one lane per block pair);
+ *         SD_GEMV_MFMA   matrix-core kernel (v_mfma_i32_16x16x64_i8 on tiles
+ *                        of 16 rows x 16 tokens).
+ * All paths compute the same cells in the same fixed order, so y is bitwise
+ * identical whichever path runs, for any n_tok.  Other arguments, layouts and
+ * errors as sd_qgemv_q8_0_batch; an unknown path gives SD_EINVAL.
+ */
+#define SD_GEMV_AUTO 0
+#define SD_GEMV_NARROW 1
+#define SD_GEMV_MFMA 2
+int sd_qgemv_q8_0_batch_path(const void* w, int64_t N, int64_t K,
+                             const int8_t* xq, const float* xd, int n_tok,
+                             const float* residual, float* y, int64_t ldy,
+                             int path, sd_stream_t stream);
+
 /* ------------------------------------------------------------------ RoPE
  * sd_rope_posvec -- rotary embedding with one position per token (ds4 pull
  * request 604, "Commit walkthrough / CUDA kernels": pos-vector RoPE; token t

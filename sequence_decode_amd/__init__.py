@@ -14,12 +14,13 @@ __all__ = [
     "SdError", "load", "abi_version", "quantize_q8_act", "qgemv_q8_0_batch", "rope_posvec",
     "kv_append_f16", "seqview", "decode_attn_workspace_bytes", "decode_attn_multiseq",
     "rmsnorm_q8", "swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
-    "ATTN_CHUNK",
+    "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA",
 ]
 
 MAX_TOKENS = 16
 MAX_SEQS = 4
 ATTN_CHUNK = 256
+GEMV_AUTO, GEMV_NARROW, GEMV_MFMA = 0, 1, 2
 
 
 class SdError(RuntimeError):
@@ -74,8 +75,10 @@ def quantize_q8_act(x, xq=None, xd=None, stream=None):
     return xq, xd
 
 
-def qgemv_q8_0_batch(w, N, K, xq, xd, residual=None, out=None, stream=None):
-    """q8_0 GEMV for n_tok = xq.shape[0] rows -> y fp32 [n_tok][N]."""
+def qgemv_q8_0_batch(w, N, K, xq, xd, residual=None, out=None, stream=None, path=None):
+    """q8_0 GEMV for n_tok = xq.shape[0] rows -> y fp32 [n_tok][N].  path=None
+    calls sd_qgemv_q8_0_batch; GEMV_AUTO / GEMV_NARROW / GEMV_MFMA call
+    sd_qgemv_q8_0_batch_path with that kernel choice."""
     import torch
     _need(w, torch.uint8, "w")
     _need(xq, torch.int8, "xq")
@@ -84,8 +87,13 @@ def qgemv_q8_0_batch(w, N, K, xq, xd, residual=None, out=None, stream=None):
     y = torch.empty((n_tok, N), dtype=torch.float32, device=xq.device) if out is None else out
     if residual is not None:
         _need(residual, torch.float32, "residual")
-    _check("sd_qgemv_q8_0_batch", _lib.load().sd_qgemv_q8_0_batch(
-        _p(w), N, K, _p(xq), _p(xd), n_tok, _p(residual), _p(y), y.shape[1], _stream(stream)))
+    if path is None:
+        _check("sd_qgemv_q8_0_batch", _lib.load().sd_qgemv_q8_0_batch(
+            _p(w), N, K, _p(xq), _p(xd), n_tok, _p(residual), _p(y), y.shape[1], _stream(stream)))
+    else:
+        _check("sd_qgemv_q8_0_batch_path", _lib.load().sd_qgemv_q8_0_batch_path(
+            _p(w), N, K, _p(xq), _p(xd), n_tok, _p(residual), _p(y), y.shape[1], int(path),
+            _stream(stream)))
     return y
 
 

@@ -14,6 +14,7 @@ SIGNATURES = {
     "sd_abi_version": ([], i32),
     "sd_quantize_q8_act": ([P, i64, i32, i64, P, P, P], i32),
     "sd_qgemv_q8_0_batch": ([P, i64, i64, P, P, i32, P, P, i64, P], i32),
+    "sd_qgemv_q8_0_batch_path": ([P, i64, i64, P, P, i32, P, P, i64, i32, P], i32),
     "sd_rope_posvec": ([P, i32, i32, i32, i64, i64, P, f64, i32, P], i32),
     "sd_kv_append_f16": ([P, P, i64, P, i32, i32, i32, P], i32),
     "sd_decode_attn_workspace_bytes": ([P, i32, i32, i32], sz),

@@ -23,14 +23,15 @@ inline int from_hip(hipError_t e) { return e == hipSuccess ? SD_OK : SD_EHIP; }
 inline hipStream_t hs(sd_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 int check_gemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd, int n_tok,
-               float* y, int64_t ldy) {
+               float* y, int64_t ldy, int path = SD_GEMV_AUTO) {
   if (!w || !xq || !xd || !y) return SD_EINVAL;
   if (N < 1 || N > ((int64_t)1 << 30) || K < 1 || n_tok < 1 || n_tok > SD_MAX_TOKENS || ldy < N)
     return SD_EINVAL;
   if (K % 256 != 0 || K > ((int64_t)1 << 24)) return SD_EUNSUPPORTED;
   if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4)) return SD_EALIGN;
+  if (path != SD_GEMV_AUTO && path != SD_GEMV_NARROW && path != SD_GEMV_MFMA) return SD_EINVAL;
   GemvPlan pl;
-  if (!plan_qgemv(N, K, n_tok, &pl)) return SD_EUNSUPPORTED;
+  if (!plan_qgemv(N, K, n_tok, path, &pl)) return SD_EUNSUPPORTED;
   return SD_OK;
 }
 
@@ -98,6 +99,15 @@ int sd_qgemv_q8_0_batch(const void* w, int64_t N, int64_t K, const int8_t* xq, c
   if (rc != SD_OK) return rc;
   if (residual && !aligned(residual, 4)) return SD_EALIGN;
   return from_hip(launch_qgemv(w, N, K, xq, xd, n_tok, residual, y, ldy, hs(stream)));
+}
+
+int sd_qgemv_q8_0_batch_path(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
+                             int n_tok, const float* residual, float* y, int64_t ldy, int path,
+                             sd_stream_t stream) {
+  int rc = check_gemv(w, N, K, xq, xd, n_tok, y, ldy, path);
+  if (rc != SD_OK) return rc;
+  if (residual && !aligned(residual, 4)) return SD_EALIGN;
+  return from_hip(launch_qgemv(w, N, K, xq, xd, n_tok, residual, y, ldy, hs(stream), path));
 }
 
 int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok, int64_t ld_head,

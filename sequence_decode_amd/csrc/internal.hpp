@@ -51,18 +51,21 @@ hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
 struct GemvPlan {
   int pairs;         // K / 64
   int chunks;        // pairs / 64 rounded up: the unit of the fixed reduction order
-  bool use_reg;      // activations held in registers (1..4 tokens, <= 4 chunks)
+  bool mfma;         // matrix-core kernel (tiles of 16 rows)
+  bool use_reg;      // activations held in registers (1..8 tokens, <= 4 chunks)
   int sp;            // waves per row in the register kernel (1, 2 or 4)
   int slice_pairs;   // pairs staged per LDS slice (multiple of 64, or all)
   int n_slices;
   size_t lds_bytes;
   int rows_per_wave;
-  int n_blocks;      // row blocks of rows_per_wave rows
+  int n_blocks;      // row blocks of rows_per_wave rows (MFMA kernel: 16-row tiles)
   int grid;
 };
-bool plan_qgemv(int64_t N, int64_t K, int n_tok, GemvPlan* plan);
+// path: SD_GEMV_AUTO, SD_GEMV_NARROW or SD_GEMV_MFMA; every path gives the same bits.
+bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan);
 hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
-                        int n_tok, const float* residual, float* y, int64_t ldy, hipStream_t st);
+                        int n_tok, const float* residual, float* y, int64_t ldy, hipStream_t st,
+                        int path = SD_GEMV_AUTO);
 
 hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok,
                               int64_t ld_head, const int32_t* pos, double theta, int n_rot,

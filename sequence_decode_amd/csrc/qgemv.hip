@@ -425,6 +425,279 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_lds(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Any batch width on the matrix cores (v_mfma_i32_16x16x64_i8), with the
+// same cells, tree and chunk order as the two kernels above, hence the same
+// bits.
+//
+// A workgroup (8 waves) owns tiles of 16 rows.  For K chunk c it stages the
+// activations of pairs 64c .. 64c+63 for all tokens in LDS, in the padded
+// pair layout (dwords 0..15 per pair and token; dword 16 and the two block
+// scales go to a per-pair table of 16-token vectors).  Wave w takes pairs
+// 64c + 8w + j, j = 0..7, of the tile.  Lane (col, kq) loads bytes
+// 16kq .. 16kq+15 of row col's pair (global_load_dwordx4; the first 64 of the
+// pair's 68 bytes) and the same 16 bytes of token col's activations, so that
+// one MFMA sums the products of all 64 bytes.  Two MFMAs per pair give the two
+// exact block sums: the first with the block-B dwords of the activation
+// operand masked off, the second with the block-A dwords masked off (the
+// scale bytes meet activation zeros either way).  The last four weights of
+// block B (pair bytes 64..67) join the second sum through v_dot4.
+// The accumulator of lane (col, kq) holds tokens 4kq .. 4kq+3 of row col, so
+// the lane forms those four cells (0 + s_A) + s_B exactly as the narrow
+// kernels do and runs the 8-leaf tree of its pairs in registers.  The eight
+// wave subtrees meet in LDS as ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)), the last
+// three levels of the 64-leaf tree, and the chunk sums are added in chunk
+// order.  A wave loads the next tile's weights while it works on the current
+// one (two register sets), and the per-tile sums alternate between two LDS
+// tables, so a tile costs one barrier.
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr int kMfmaThreads = 512;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaPairs = 8;   // pairs per wave per chunk
+constexpr int kMfmaGroup = 8;   // tiles whose running totals a thread keeps across chunks
+
+// Lane l gets x of lane l % 16 (first 16-lane row), resp. of lane 32 + l % 16.
+__device__ __forceinline__ uint32_t bcast_row0(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const uint32_t t = a[0];
+  const auto b = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+  return b[0];
+}
+__device__ __forceinline__ uint32_t bcast_row2(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const uint32_t t = a[1];
+  const auto b = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+  return b[0];
+}
+
+__device__ __forceinline__ v4i and4(const u32x4a& v, uint32_t m0, uint32_t m1) {
+  return v4i{(int)(v.x & m0), (int)(v.y & m1), (int)(v.z & m1), (int)(v.w & m1)};
+}
+
+struct MfmaW {  // one wave's weights of one tile: bytes 16kq.. and dword 16 of 8 pairs
+  u32x4a q[kMfmaPairs];
+  uint32_t d16[kMfmaPairs];
+};
+
+__global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
+    const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
+    const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd, int n_tok,
+    const float* residual, float* y, int64_t ldy, int n_tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  uint32_t* s_act = reinterpret_cast<uint32_t*>(lds_dyn);            // [64 pairs][16 tokens][16]
+  float* s_sc = reinterpret_cast<float*>(s_act + 64 * 16 * 16);      // [64 pairs][3][16 tokens]
+  float* s_tab = s_sc + 64 * 3 * 16;                                 // [2][8 waves][16 rows][16 tokens]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop bounds
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+  const int chunks = (P + 63) / 64;
+  const int nb = 2 * P;
+  const int my_tiles = (int)blockIdx.x < n_tiles ? (n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  // dwords 4kq .. 4kq+3 of a pair: all block A for kq <= 1; for kq = 2 dword 8
+  // is block A (its last two weights) and 9..11 block B; all block B for kq = 3
+  const uint32_t mA0 = kq <= 2 ? ~0u : 0u;
+  const uint32_t mA1 = kq <= 1 ? ~0u : 0u;
+  const int trow = (tid >> 4) & 15;  // combine: threads 0..255 -> (row, token)
+  const int ttok = tid & 15;
+  const uint32_t* act_l = s_act + (wave * kMfmaPairs * 16 + col) * 16 + 4 * kq;
+  const float* sc_l = s_sc + wave * kMfmaPairs * 48 + 4 * kq;
+
+  // weights of item (chunk c, tile) for this wave
+  auto load_w = [&](MfmaW& B, int c, int tile) {
+    const int np = min(64, P - 64 * c);
+    // rows past N read row N-1; their sums stay in their own column and are never stored
+    const int n = min(tile * 16 + col, N - 1);
+    const uint8_t* pb = w + (int64_t)n * row_bytes + (int64_t)kPairBytes * (64 * (int64_t)c + kMfmaPairs * wave);
+    if (kMfmaPairs * wave + kMfmaPairs <= np) {
+#pragma unroll
+      for (int j = 0; j < kMfmaPairs; ++j) {
+        B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 16 * kq);
+        B.d16[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j + 64);
+      }
+    } else {
+      // last chunk of a row: pairs past the end are zero cells
+#pragma unroll
+      for (int j = 0; j < kMfmaPairs; ++j) {
+        B.q[j] = u32x4a{0u, 0u, 0u, 0u};
+        B.d16[j] = 0u;
+        if (kMfmaPairs * wave + j < np) {
+          B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 16 * kq);
+          B.d16[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j + 64);
+        }
+      }
+    }
+  };
+
+  // this wave's 8-leaf subtree for the 4 tokens of its lane
+  auto wave_sub = [&](const MfmaW& B, float (&sub)[4]) {
+    struct PairOps {
+      v4i DA, DB;
+      f32x4 xa, xb;
+      u32x4a a16;
+    };
+    auto issue = [&](int j, PairOps& o) {
+      u32x4a av = u32x4a{0u, 0u, 0u, 0u};
+      if (col < n_tok) av = *reinterpret_cast<const u32x4a*>(act_l + j * 256);
+      const v4i wop = __builtin_bit_cast(v4i, B.q[j]);
+      const v4i zero = {0, 0, 0, 0};
+      o.DA = __builtin_amdgcn_mfma_i32_16x16x64_i8(and4(av, mA0, mA1), wop, zero, 0, 0, 0);
+      o.DB = __builtin_amdgcn_mfma_i32_16x16x64_i8(and4(av, ~mA0, ~mA1), wop, zero, 0, 0, 0);
+      o.xa = *reinterpret_cast<const f32x4*>(sc_l + j * 48);
+      o.xb = *reinterpret_cast<const f32x4*>(sc_l + j * 48 + 16);
+      o.a16 = *reinterpret_cast<const u32x4a*>(sc_l + j * 48 + 32);
+      // keep program order: a pair's math must not wait for every pair's sums
+      asm volatile("" : "+v"(o.DA), "+v"(o.DB));
+    };
+    float st[3][4];
+    auto math = [&](int j, const PairOps& o) {
+      const float dwA = f16_bits_to_f32(bcast_row0(B.q[j].x));
+      const float dwB = f16_bits_to_f32(bcast_row2(B.q[j].x) >> 16);
+      const float xar[4] = {o.xa.x, o.xa.y, o.xa.z, o.xa.w};
+      const float xbr[4] = {o.xb.x, o.xb.y, o.xb.z, o.xb.w};
+      const uint32_t a16r[4] = {o.a16.x, o.a16.y, o.a16.z, o.a16.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int iA = o.DA[r];
+        const int iB = __builtin_amdgcn_sdot4((int)B.d16[j], (int)a16r[r], o.DB[r], false);
+        const float sA = fmul(fmul(dwA, xar[r]), (float)iA);
+        const float sB = fmul(fmul(dwB, xbr[r]), (float)iB);
+        float v = fadd(fadd(0.0f, sA), sB);
+        // 8-leaf tree over j, built as leaves arrive
+        if ((j & 1) == 0) {
+          st[0][r] = v;
+        } else {
+          v = fadd(st[0][r], v);
+          if ((j & 2) == 0) {
+            st[1][r] = v;
+          } else {
+            v = fadd(st[1][r], v);
+            if ((j & 4) == 0) st[2][r] = v;
+            else sub[r] = fadd(st[2][r], v);
+          }
+        }
+      }
+      asm volatile("" : "+v"(st[0][0]), "+v"(st[0][1]), "+v"(st[0][2]), "+v"(st[0][3]));
+    };
+    PairOps ops[2];
+    issue(0, ops[0]);
+#pragma unroll
+    for (int j = 0; j < kMfmaPairs; ++j) {
+      if (j + 1 < kMfmaPairs) issue(j + 1, ops[(j + 1) & 1]);
+      math(j, ops[j & 1]);
+    }
+  };
+
+  int staged = -1;
+  MfmaW wA, wB;
+  for (int g0 = 0; g0 < my_tiles; g0 += kMfmaGroup) {
+    const int ng = min(kMfmaGroup, my_tiles - g0);
+    const int n_items = chunks * ng;  // item i = (chunk i / ng, tile g0 + i % ng)
+    float tot[kMfmaGroup];
+#pragma unroll
+    for (int kk = 0; kk < kMfmaGroup; ++kk) tot[kk] = 0.0f;
+    auto tile_of = [&](int i) { return (int)blockIdx.x + (g0 + i % ng) * (int)gridDim.x; };
+    auto item = [&](int i, MfmaW& cur, MfmaW& nxt) {
+      const int c = i / ng;
+      const int kk = i - c * ng;
+      if (staged != c) {
+        __syncthreads();
+        const int np = min(64, P - 64 * c);
+        for (int e = tid; e < 64 * 16; e += kMfmaThreads) {
+          const int pl = e >> 4;
+          const int t = e & 15;
+          const int64_t pp = 64 * (int64_t)c + pl;
+          uint32_t o[17];
+          float da = 0.0f, db = 0.0f;
+          if (pl < np && t < n_tok) {
+            const u32x4a* src = reinterpret_cast<const u32x4a*>(xq + (int64_t)t * K + 64 * pp);
+            uint32_t a[16];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const u32x4a q = src[v];
+              a[4 * v + 0] = q.x;
+              a[4 * v + 1] = q.y;
+              a[4 * v + 2] = q.z;
+              a[4 * v + 3] = q.w;
+            }
+            o[0] = a[0] << 16;
+#pragma unroll
+            for (int q = 1; q < 8; ++q) o[q] = (a[q - 1] >> 16) | (a[q] << 16);
+            o[8] = a[7] >> 16;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[9 + q] = a[8 + q];
+            da = xd[(int64_t)t * nb + 2 * pp];
+            db = xd[(int64_t)t * nb + 2 * pp + 1];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 17; ++q) o[q] = 0u;
+          }
+          if (t < n_tok) {
+            u32x4a* dst = reinterpret_cast<u32x4a*>(s_act + (pl * 16 + t) * 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dst[v] = u32x4a{o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]};
+          }
+          s_sc[(pl * 3 + 0) * 16 + t] = da;
+          s_sc[(pl * 3 + 1) * 16 + t] = db;
+          s_sc[(pl * 3 + 2) * 16 + t] = __uint_as_float(o[16]);
+        }
+        __syncthreads();
+        staged = c;
+      }
+      // wait for this tile's weights here, once, before the next tile's loads
+      // queue up behind them (the memory counter retires loads in order)
+#pragma unroll
+      for (int j = 0; j < kMfmaPairs; ++j) asm volatile("" ::"v"(cur.q[j]), "v"(cur.d16[j]));
+      if (i + 1 < n_items) load_w(nxt, (i + 1) / ng, tile_of(i + 1));
+      float sub[4];
+      wave_sub(cur, sub);
+      float* tab = s_tab + (i & 1) * (kMfmaWaves * 256);
+      *reinterpret_cast<f32x4*>(tab + (wave * 16 + col) * 16 + 4 * kq) = f32x4{sub[0], sub[1], sub[2], sub[3]};
+      __syncthreads();
+      if (tid < 256) {
+        const float* tb = tab + trow * 16 + ttok;
+        const float cs = fadd(fadd(fadd(tb[0], tb[256]), fadd(tb[512], tb[768])),
+                              fadd(fadd(tb[1024], tb[1280]), fadd(tb[1536], tb[1792])));
+#pragma unroll
+        for (int q = 0; q < kMfmaGroup; ++q)
+          if (q == kk) tot[q] = c == 0 ? cs : fadd(tot[q], cs);
+        if (c == chunks - 1) {
+          const int n = tile_of(i) * 16 + trow;
+          if (n < N && ttok < n_tok) {
+            float v = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kMfmaGroup; ++q)
+              if (q == kk) v = tot[q];
+            store_out(v, n, ttok, residual, y, ldy);
+          }
+        }
+      }
+    };
+    load_w(wA, 0, tile_of(0));
+    for (int i = 0; i < n_items; i += 2) {
+      item(i, wA, wB);
+      if (i + 1 < n_items) item(i + 1, wB, wA);
+    }
+  }
+}
+
+hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
+                       const float* xd, int n_tok, const float* residual, float* y, int64_t ldy,
+                       hipStream_t st) {
+  static bool lds_raised = false;  // up to 80 KiB of dynamic LDS
+  if (!lds_raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_mfma),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
+  hipLaunchKernelGGL(k_qgemv_q8_0_mfma, dim3(pl.grid), dim3(kMfmaThreads), pl.lds_bytes, st,
+                     static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
+                     xq, K, xd, n_tok, residual, y, ldy, pl.n_blocks);
+  return hipGetLastError();
+}
+
 template <int NT, int SP>
 hipError_t launch_dma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                       const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st) {
@@ -472,13 +745,32 @@ hipError_t launch_dma_nt(const GemvPlan& pl, const void* w, int64_t N, int64_t K
 
 }  // namespace
 
-bool plan_qgemv(int64_t N, int64_t K, int n_tok, GemvPlan* plan) {
+size_t mfma_lds_bytes() { return (size_t)64 * 16 * 16 * 4 + 64 * 3 * 16 * 4 + 2 * 8 * 16 * 16 * 4; }
+
+bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan) {
   if (N < 1 || K < 256 || K % 256 != 0 || n_tok < 1 || n_tok > SD_MAX_TOKENS) return false;
   if (N > (int64_t)1 << 30 || K > (int64_t)1 << 24) return false;
   GemvPlan p;
   p.pairs = (int)(K / 64);
   p.chunks = (p.pairs + 63) / 64;
   const size_t per_pair = (size_t)n_tok * kActDw * 4;
+  if (path == SD_GEMV_AUTO) path = n_tok <= 8 && p.chunks <= 4 ? SD_GEMV_NARROW : SD_GEMV_MFMA;
+  if (path != SD_GEMV_NARROW && path != SD_GEMV_MFMA) return false;
+  p.mfma = path == SD_GEMV_MFMA;
+  if (p.mfma) {
+    p.use_reg = false;
+    p.sp = 0;
+    p.rows_per_wave = 0;
+    p.slice_pairs = 64;
+    p.n_slices = p.chunks;
+    p.n_blocks = (int)((N + 15) / 16);  // tiles of 16 rows
+    const int64_t max_grid = 256;
+    const int64_t iters = (p.n_blocks + max_grid - 1) / max_grid;
+    p.grid = (int)((p.n_blocks + iters - 1) / iters);
+    p.lds_bytes = mfma_lds_bytes();
+    *plan = p;
+    return true;
+  }
   p.use_reg = n_tok <= 8 && p.chunks <= 4;
   if (p.use_reg) {
     p.sp = p.chunks == 1 ? 1 : (p.chunks == 2 ? 2 : 4);
@@ -518,9 +810,11 @@ bool plan_qgemv(int64_t N, int64_t K, int n_tok, GemvPlan* plan) {
 }
 
 hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
-                        int n_tok, const float* residual, float* y, int64_t ldy, hipStream_t st) {
+                        int n_tok, const float* residual, float* y, int64_t ldy, hipStream_t st,
+                        int path) {
   GemvPlan pl;
-  if (!plan_qgemv(N, K, n_tok, &pl)) return hipErrorInvalidValue;
+  if (!plan_qgemv(N, K, n_tok, path, &pl)) return hipErrorInvalidValue;
+  if (pl.mfma) return launch_mfma(pl, w, N, K, xq, xd, n_tok, residual, y, ldy, st);
   if (pl.use_reg) {
     switch (n_tok) {
       case 1: return launch_dma_nt<1>(pl, w, N, K, xq, xd, residual, y, ldy, st);

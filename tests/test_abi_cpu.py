@@ -58,6 +58,16 @@ def test_gemv_rejections(L):
     assert g(FAKE, 0, 14336, FAKE, FAKE, 16, None, FAKE, 64, None) == SD_EINVAL
 
 
+def test_gemv_path_rejections(L):
+    g = L.sd_qgemv_q8_0_batch_path
+    for path in (-1, 3, 99):
+        assert g(FAKE, 64, 256, FAKE, FAKE, 1, None, FAKE, 64, path, None) == SD_EINVAL
+    for path in (0, 1, 2):
+        assert g(FAKE, 64, 256, FAKE, FAKE, 17, None, FAKE, 64, path, None) == SD_EINVAL
+        assert g(FAKE, 64, 4000, FAKE, FAKE, 1, None, FAKE, 64, path, None) == SD_EUNSUPPORTED
+        assert g(ODD, 64, 256, FAKE, FAKE, 1, None, FAKE, 64, path, None) == SD_EALIGN
+
+
 def test_quantize_rejections(L):
     q = L.sd_quantize_q8_act
     assert q(FAKE, 64, 1, 48, FAKE, FAKE, None) == SD_EUNSUPPORTED

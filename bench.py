@@ -13,7 +13,9 @@ Cache).  The timed steps replay a HIP
 graph of the sweep, so the host's launch rate does not limit the GPU.  Inputs
 are resident in HBM before timing starts.
 
-Also reported: the same sweep at n_tok = 1..4, the dominant kernel's roofline
+Also reported: the same sweep at n_tok = 1..4; the widened verify batch at
+n_tok = 8, 12, 16 on the v_dot4 kernels and on the matrix-core kernel (with a
+bitwise comparison of the two); the dominant kernel's roofline
 (per-launch HIP-event durations of every GEMV in an eager pass of the same
 sweep), the aggregate tokens/s of the full synthetic decode step for 1..4
 sequences (plus the serial one-sequence-at-a-time baseline), and the CPU
@@ -76,7 +78,9 @@ class Sweep:
                   for name, N, K in SHAPES}
         self.weight_bytes = sum(N * (K // 32) * 34 for _, N, K in SHAPES) * N_LAYERS
 
-    def step(self, n_tok):
+    def step(self, n_tok, path=None):
+        """One sweep; path=None uses sd_qgemv_q8_0_batch, else the kernel that
+        sd_qgemv_q8_0_batch_path picks for that path."""
         sd, lib = self.sd, self.sd._lib.load()
         import ctypes
         st = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
@@ -90,8 +94,13 @@ class Sweep:
             for name, N, K in SHAPES:
                 xq, xd = self.xq[K], self.xd[K]
                 y = self.y[name]
-                rc = lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()),
-                                             P(xd.data_ptr()), n_tok, None, P(y.data_ptr()), N, st)
+                if path is None:
+                    rc = lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()),
+                                                 P(xd.data_ptr()), n_tok, None, P(y.data_ptr()), N, st)
+                else:
+                    rc = lib.sd_qgemv_q8_0_batch_path(P(L[name].data_ptr()), N, K, P(xq.data_ptr()),
+                                                      P(xd.data_ptr()), n_tok, None, P(y.data_ptr()), N,
+                                                      path, st)
                 if rc:
                     raise sd.SdError("sd_qgemv_q8_0_batch", rc)
 
@@ -156,6 +165,32 @@ def roofline_pass(torch, sweep, n_tok, reps):
         tot_ms += ms
         launches += n
     return tot_bytes, tot_ms, launches, per
+
+
+def verify_widths(torch, sweep, steps):
+    """The widened verify batch (n_tok 8, 12, 16) on the same 32-layer sweep:
+    GB/s of the v_dot4 kernels and of the matrix-core kernel, and whether the
+    two give bitwise the same outputs."""
+    from sequence_decode_amd import GEMV_NARROW, GEMV_MFMA
+    out = {}
+    for n in (8, 12, 16):
+        row = {}
+        ys = {}
+        for label, path in (("narrow", GEMV_NARROW), ("mfma", GEMV_MFMA)):
+            dt = time_graph(torch, lambda: sweep.step(n, path), steps, 2)
+            gbs = sweep.bytes_per_step(n) / dt / 1e9
+            row[label] = {"GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                          "ms_per_step": round(dt * 1e3, 4)}
+            sweep.step(n, path)
+            torch.cuda.synchronize()
+            ys[label] = {name: sweep.y[name][:n].clone() for name, _, _ in SHAPES}
+        row["bitwise_equal"] = all(torch.equal(ys["narrow"][k].view(torch.int32), ys["mfma"][k].view(torch.int32))
+                                   for k in ys["narrow"])
+        row["mfma_speedup"] = round(row["mfma"]["GB_s"] / row["narrow"]["GB_s"], 3)
+        out[str(n)] = row
+        log(f"verify width n_tok={n}: narrow {row['narrow']['GB_s']} GB/s, mfma {row['mfma']['GB_s']} GB/s, "
+            f"bitwise equal {row['bitwise_equal']}")
+    return out
 
 
 def cpu_baseline(torch, sweep, n_tok, budget_s):
@@ -308,6 +343,7 @@ def main():
                      "kernel": f"k_qgemv_q8_0_dma<{n},SP,1>", "launches": launches,
                      "avg_launch_us": round(tms / launches * 1e3, 3), "per_shape": per_shape},
     }
+    line["verify_widths"] = verify_widths(torch, sweep, max(3, args.steps // 2))
     line["decode_step"] = None
     if not args.no_decode:
         line["decode_step"] = decode_bench(torch, steps=max(8, args.steps), warmup=args.warmup)

@@ -206,6 +206,33 @@ int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* view
                             int n_seq, int H_q, int H_kv, int D, float scale,
                             float* out, void* ws, size_t ws_bytes, sd_stream_t stream);
 
+/*
+ * sd_decode_attn_verify -- several query tokens per sequence: the newest
+ * n_new[s] positions of sequence s, each attending causally (the packed
+ * multi-sequence verification of proposed tokens, "feat(qwen36): complete
+ * concurrent serving implementation with speculation").  The tokens' own K/V
+ * rows are already in the cache, so ctx_len_s counts them.  Token i of
+ * sequence s (position p = ctx_len_s - n_new[s] + i) gives
+ *   out[r][h] = sum_j softmax_j(scale * q[r][h] . k_j) v_j,  j <= p,
+ * with r = (n_new[0] + .. + n_new[s-1]) + i the packed row.  Each token's
+ * reduction has the shape of a one-token call over p + 1 keys, so its bits are
+ * those of sd_decode_attn_multiseq with ctx_len = p + 1, whatever the other
+ * tokens and sequences are.
+ *   q    [rows][H_q][D] fp32 at row stride ld_q, packed as above, 16-byte aligned.
+ *   out  [rows][H_q][D] fp32 contiguous, 16-byte aligned.
+ *   n_new [host] n_seq entries, 1 <= n_new[s] <= SD_ATTN_MAX_NEW, <= ctx_len_s.
+ *   ws   at least sd_decode_attn_verify_workspace_bytes().
+ * Other requirements and errors as sd_decode_attn_multiseq, which is this call
+ * with every n_new[s] = 1.
+ */
+#define SD_ATTN_MAX_NEW 4
+size_t sd_decode_attn_verify_workspace_bytes(const sd_seqview* views, const int32_t* n_new,
+                                             int n_seq, int H_q, int D);
+int sd_decode_attn_verify(const float* q, int64_t ld_q, const sd_seqview* views,
+                          const int32_t* n_new, int n_seq, int H_q, int H_kv, int D,
+                          float scale, float* out, void* ws, size_t ws_bytes,
+                          sd_stream_t stream);
+
 /* ------------------------------------------------------------ step glue
  * Pieces of the fused decode step (ds4 pull request 604, "2. Single-GPU
  * decode batches don't scale" and "Commit walkthrough / Graph driver").

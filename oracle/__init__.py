@@ -153,6 +153,23 @@ def attn_decode_multiseq(q: np.ndarray, caches, ctx_lens, scale: float) -> np.nd
                      for s in range(q.shape[0])])
 
 
+def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float) -> np.ndarray:
+    """Several query tokens per sequence, packed by sequence (the verification of
+    proposed tokens in "feat(qwen36): complete concurrent serving implementation
+    with speculation"): the n_new[s] newest positions of sequence s, token i at
+    position p = ctx_lens[s] - n_new[s] + i attending to keys 0..p.  Each token
+    is the one-token decode attention over its own prefix of p + 1 keys.
+    q_rows [sum(n_new)][H_q][D] -> same shape."""
+    out = []
+    r = 0
+    for s, T in enumerate(n_new):
+        for i in range(T):
+            p = ctx_lens[s] - T + i
+            out.append(attn_decode_one(q_rows[r], caches[s][0], caches[s][1], p + 1, scale))
+            r += 1
+    return np.stack(out)
+
+
 def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     x = _req(x, np.float32)
     n_tok, D = x.shape

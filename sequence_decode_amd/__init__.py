@@ -13,6 +13,7 @@ from ._lib import SeqView
 __all__ = [
     "SdError", "load", "abi_version", "quantize_q8_act", "qgemv_q8_0_batch", "rope_posvec",
     "kv_append_f16", "seqview", "decode_attn_workspace_bytes", "decode_attn_multiseq",
+    "decode_attn_verify", "ATTN_MAX_NEW",
     "rmsnorm_q8", "swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
     "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA",
 ]
@@ -20,6 +21,7 @@ __all__ = [
 MAX_TOKENS = 16
 MAX_SEQS = 4
 ATTN_CHUNK = 256
+ATTN_MAX_NEW = 4
 GEMV_AUTO, GEMV_NARROW, GEMV_MFMA = 0, 1, 2
 
 
@@ -148,6 +150,26 @@ def decode_attn_multiseq(q, views, H_kv, scale, out=None, ws=None, stream=None):
     out = torch.empty_like(q) if out is None else out
     _check("sd_decode_attn_multiseq", _lib.load().sd_decode_attn_multiseq(
         _p(q), H_q * D, arr, len(views), H_q, H_kv, D, float(scale), _p(out), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_verify(q, views, n_new, H_kv, scale, out=None, ws=None, stream=None):
+    """q [rows][H_q][D] fp32 with rows = sum(n_new), packed by sequence; the
+    n_new[s] newest positions of sequence s attend causally -> out like q."""
+    import torch
+    _need(q, torch.float32, "q")
+    rows, H_q, D = q.shape
+    if rows != sum(n_new):
+        raise ValueError("q rows must equal sum(n_new)")
+    arr = _views(views)
+    nn = (ctypes.c_int32 * len(n_new))(*[int(v) for v in n_new])
+    need = _lib.load().sd_decode_attn_verify_workspace_bytes(arr, nn, len(views), H_q, D)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q) if out is None else out
+    _check("sd_decode_attn_verify", _lib.load().sd_decode_attn_verify(
+        _p(q), H_q * D, arr, nn, len(views), H_q, H_kv, D, float(scale), _p(out), _p(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
     return out
 

@@ -19,6 +19,8 @@ SIGNATURES = {
     "sd_kv_append_f16": ([P, P, i64, P, i32, i32, i32, P], i32),
     "sd_decode_attn_workspace_bytes": ([P, i32, i32, i32], sz),
     "sd_decode_attn_multiseq": ([P, i64, P, i32, i32, i32, i32, f32, P, P, sz, P], i32),
+    "sd_decode_attn_verify_workspace_bytes": ([P, P, i32, i32, i32], sz),
+    "sd_decode_attn_verify": ([P, i64, P, P, i32, i32, i32, i32, f32, P, P, sz, P], i32),
     "sd_rmsnorm_q8": ([P, i64, i32, i64, P, f32, P, P, P, P], i32),
     "sd_swiglu_q8": ([P, i64, i32, i64, P, P, P, P], i32),
     "sd_embed_f16": ([P, i64, i64, P, i32, P, P], i32),

@@ -51,7 +51,7 @@ int check_views(const sd_seqview* views, int n_seq, int D, bool attn) {
   return SD_OK;
 }
 
-void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a) {
+void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a, const int32_t* n_new = nullptr) {
   *a = SeqArgs{};
   a->n_seq = n_seq;
   for (int s = 0; s < n_seq; ++s) {
@@ -63,7 +63,33 @@ void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a) {
     x.ld_tok = views[s].ld_tok;
     x.ld_head = views[s].ld_head;
     x.ctx_len = views[s].ctx_len;
+    x.n_new = n_new ? n_new[s] : 1;
   }
+}
+
+// n_new [host]: query tokens per sequence, 1..SD_ATTN_MAX_NEW and <= ctx_len
+bool check_new(const sd_seqview* views, const int32_t* n_new, int n_seq) {
+  for (int s = 0; s < n_seq; ++s)
+    if (n_new[s] < 1 || n_new[s] > SD_ATTN_MAX_NEW || n_new[s] > views[s].ctx_len) return false;
+  return true;
+}
+
+int attn_common(const float* q, int64_t ld_q, const sd_seqview* views, const int32_t* n_new,
+                int n_seq, int H_q, int H_kv, int D, float scale, float* out, void* ws,
+                size_t ws_bytes, sd_stream_t stream) {
+  if (!q || !out || !ws || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SD_EINVAL;
+  if (D != kAttnHeadDim || H_q / H_kv != kAttnGroup) return SD_EUNSUPPORTED;
+  if (ld_q < (int64_t)H_q * D || !isfinite(scale)) return SD_EINVAL;
+  int rc = check_views(views, n_seq, D, true);
+  if (rc != SD_OK) return rc;
+  if (n_new && !check_new(views, n_new, n_seq)) return SD_EINVAL;
+  if (!aligned(q, 16) || ld_q % 4 != 0 || !aligned(out, 16) || !aligned(ws, 16)) return SD_EALIGN;
+  SeqArgs a;
+  fill_seqargs(views, n_seq, &a, n_new);
+  const size_t need = attn_layout(&a, H_q, H_kv) * sizeof(float);
+  if (ws_bytes < need) return SD_EWORKSPACE;
+  return from_hip(launch_attn(q, ld_q, a, H_q, H_kv, scale, out, static_cast<float*>(ws), nullptr,
+                              nullptr, hs(stream)));
 }
 
 }  // namespace
@@ -135,29 +161,31 @@ int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
 }
 
 size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_q, int D) {
+  return sd_decode_attn_verify_workspace_bytes(views, nullptr, n_seq, H_q, D);
+}
+
+size_t sd_decode_attn_verify_workspace_bytes(const sd_seqview* views, const int32_t* n_new,
+                                             int n_seq, int H_q, int D) {
   if (!views || n_seq < 1 || n_seq > SD_MAX_SEQS || H_q < 1 || D != kAttnHeadDim) return 0;
   SeqArgs a;
   for (int s = 0; s < n_seq; ++s)
     if (views[s].ctx_len < 1) return 0;
-  fill_seqargs(views, n_seq, &a);
+  if (n_new && !check_new(views, n_new, n_seq)) return 0;
+  fill_seqargs(views, n_seq, &a, n_new);
   return attn_layout(&a, H_q, H_q / kAttnGroup) * sizeof(float);
 }
 
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views, int n_seq,
                             int H_q, int H_kv, int D, float scale, float* out, void* ws,
                             size_t ws_bytes, sd_stream_t stream) {
-  if (!q || !out || !ws || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SD_EINVAL;
-  if (D != kAttnHeadDim || H_q / H_kv != kAttnGroup) return SD_EUNSUPPORTED;
-  if (ld_q < (int64_t)H_q * D || !isfinite(scale)) return SD_EINVAL;
-  int rc = check_views(views, n_seq, D, true);
-  if (rc != SD_OK) return rc;
-  if (!aligned(q, 16) || ld_q % 4 != 0 || !aligned(out, 16) || !aligned(ws, 16)) return SD_EALIGN;
-  SeqArgs a;
-  fill_seqargs(views, n_seq, &a);
-  const size_t need = attn_layout(&a, H_q, H_kv) * sizeof(float);
-  if (ws_bytes < need) return SD_EWORKSPACE;
-  return from_hip(launch_attn(q, ld_q, a, H_q, H_kv, scale, out, static_cast<float*>(ws), nullptr,
-                              nullptr, hs(stream)));
+  return attn_common(q, ld_q, views, nullptr, n_seq, H_q, H_kv, D, scale, out, ws, ws_bytes, stream);
+}
+
+int sd_decode_attn_verify(const float* q, int64_t ld_q, const sd_seqview* views,
+                          const int32_t* n_new, int n_seq, int H_q, int H_kv, int D, float scale,
+                          float* out, void* ws, size_t ws_bytes, sd_stream_t stream) {
+  if (!n_new) return SD_EINVAL;
+  return attn_common(q, ld_q, views, n_new, n_seq, H_q, H_kv, D, scale, out, ws, ws_bytes, stream);
 }
 
 int sd_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D, const float* gamma, float eps,

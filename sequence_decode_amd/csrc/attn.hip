@@ -17,6 +17,13 @@
 //   values straight into fp32 FMAs).
 // * Each wave keeps its own softmax partial over its 64 keys, and the four
 //   merge in wave order: partial (m, l, o[128]) per head and chunk.
+// * A sequence may bring up to four query tokens, its newest positions (the
+//   packed verification of proposed tokens in "feat(qwen36): complete
+//   concurrent serving implementation with speculation"): token i at position
+//   p_i sees keys 0..p_i.  The four heads of a group times up to four tokens are
+//   the 16 columns of the MFMA tiles, and each column keeps its own key limit
+//   and its own chunk count ceil((p_i + 1) / SD_ATTN_CHUNK), so token i gets
+//   bitwise what a one-token call over p_i + 1 keys gives.
 // * A second kernel merges the partials of each (sequence, head) with fixed
 //   reduction shapes.  Every sum has a fixed shape, so a sequence's output bits do not
 //   depend on the other sequences in the call.
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
                                                     SeqArgs seqs, int H_q, float scale,
                                                     float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_v[4 * kWaveVBytes];  // V rows, then O partials
-  __shared__ float s_m[4][kAttnGroup], s_l[4][kAttnGroup];
+  __shared__ float s_m[4][16], s_l[4][16];  // per wave and MFMA column (token, head)
 
   const int s = find_seq(seqs, blockIdx.x);
   const SeqArg& A = seqs.s[s];
@@ -107,6 +114,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int col = lane & 15;  // MFMA row (A loads) / column (B, D)
   const int kg = lane >> 4;   // MFMA k-group
   const int wk = wave * kWaveKeys;
+  // MFMA column col = 4 * (burst token) + (head in the group); token tk sits at
+  // position ctx_len - T + tk and sees the keys up to it
+  const int T = A.n_new;
+  const int tk = col >> 2;
+  const int hh = col & (kAttnGroup - 1);
+  const bool colv = tk < T;
+  const int nk_col = colv ? min(C, A.ctx_len - T + tk + 1 - j0) : 0;
 
   // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
   const int jk = wk + 8 * (col >> 2) + (col & 3);
@@ -121,15 +135,15 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       if (jk + dj < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + dj * A.ld_tok + 32 * kk);
     }
   }
-  // ---- q (score B operands): column col < 4 = head g*4 + col, dims 32kk + 8kg ..
+  // ---- q (score B operands): column col = (token tk, head g*4 + hh), dims 32kk + 8kg ..
   f32x4 qv[4][2];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     qv[kk][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     qv[kk][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (col < kAttnGroup) {
+    if (colv) {
       const f32x4* qp = reinterpret_cast<const f32x4*>(
-          q + (int64_t)s * ld_q + (int64_t)(g * kAttnGroup + col) * HD + 32 * kk + 8 * kg);
+          q + (int64_t)(A.row0 + tk) * ld_q + (int64_t)(g * kAttnGroup + hh) * HD + 32 * kk + 8 * kg);
       qv[kk][0] = qp[0];
       qv[kk][1] = qp[1];
     }
@@ -181,10 +195,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int jl = wk + 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
-      z[t][r] = (jl < nk && col < kAttnGroup) ? fmul(acc[r], scale) : -INFINITY;
+      z[t][r] = jl < nk_col ? fmul(acc[r], scale) : -INFINITY;
     }
   }
-  // ---- the chunk maximum per head, shared by the four waves
+  // ---- the chunk maximum per column, shared by the four waves
   {
     float mw = -INFINITY;
 #pragma unroll
@@ -192,11 +206,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
       for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
     mw = cross_row_max(mw);
-    if (lane < kAttnGroup) s_m[wave][lane] = mw;
+    if (lane < 16) s_m[wave][lane] = mw;
   }
   __syncthreads();
-  const int hc = col & (kAttnGroup - 1);
-  const float M = fmaxf(fmaxf(s_m[0][hc], s_m[1][hc]), fmaxf(s_m[2][hc], s_m[3][hc]));
+  const float M = fmaxf(fmaxf(s_m[0][col], s_m[1][col]), fmaxf(s_m[2][col], s_m[3][col]));
   // ---- weights, their sum, and the P^T operands (block b: slot j = tile 2b + j/4, slot j%4)
   h8 phi[2], plo[2];
   float lw = 0.0f;
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       plo[t >> 1][4 * (t & 1) + r] = lo;
     }
   lw = cross_row_sum_fixed(lw);
-  if (lane < kAttnGroup) s_l[wave][lane] = lw;
+  if (lane < 16) s_l[wave][lane] = lw;
 
   // ---- weighted values: this wave's V rows have landed in LDS
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -235,31 +248,32 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);
     }
   }
-  // D slot r of lane (col, kg) = dim 16dt + 4kg + r of head col; the wave's own
-  // V region (now read) takes its partial O[head][dim]
+  // D slot r of lane (col, kg) = dim 16dt + 4kg + r of column col; the wave's
+  // own V region (now read) takes its partial O[column][dim]
   float* so = reinterpret_cast<float*>(vw);
-  if (col < kAttnGroup)
+  if (colv)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       *reinterpret_cast<f32x4*>(so + col * HD + 16 * dt + 4 * kg) =
           f32x4{o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
   __syncthreads();
 
-  // ---- sum of the four wave partials, in wave order
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int idx = tid + 256 * rep;
-    const int hh = idx / HD;
-    const int d = idx - hh * HD;
+  // ---- sum of the four wave partials, in wave order, for each column whose
+  // token reaches this chunk
+  for (int idx = tid; idx < T * kAttnGroup * HD; idx += 256) {
+    const int cc = idx / HD;
+    const int d = idx - cc * HD;
+    const int t2 = cc >> 2;
+    if (c * C > A.ctx_len - T + t2) continue;  // chunk past this token's position
     float O = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       O = fadd(O, reinterpret_cast<const float*>(s_v + w * kWaveVBytes)[idx]);
-      L = fadd(L, s_l[w][hh]);
+      L = fadd(L, s_l[w][cc]);
     }
-    const float Mh = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
-    const int h = g * kAttnGroup + hh;
-    float* dst = part + ((int64_t)A.partial_begin + (int64_t)h * A.n_chunks + c) * PF;
+    const float Mh = fmaxf(fmaxf(s_m[0][cc], s_m[1][cc]), fmaxf(s_m[2][cc], s_m[3][cc]));
+    const int h = g * kAttnGroup + (cc & (kAttnGroup - 1));
+    float* dst = part + ((int64_t)A.partial_begin + ((int64_t)t2 * H_q + h) * A.n_chunks + c) * PF;
     dst[4 + d] = O;
     if (d == 0) {
       dst[0] = Mh;
@@ -268,8 +282,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   }
 }
 
-// Grid (n_seq * H_q), 256 threads.  Merges the chunk partials of one
-// (sequence, head): M = max_c m_c; w_c = exp(m_c - M); L = sum_c l_c w_c by a
+// Grid (query rows * H_q), 256 threads.  Merges the chunk partials of one
+// (sequence, token, head) -- its chunks are those up to the token's position: M = max_c m_c; w_c = exp(m_c - M); L = sum_c l_c w_c by a
 // fixed tree over chunk index; O[d] = sum_c o_c[d] w_c with chunks split into
 // two interleaved halves (threads 0..127 take even chunks, 128..255 odd ones,
 // each in chunk order) that are then added.  Every shape depends only on the
@@ -283,12 +297,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
   __shared__ float s_w[kMaxChunks];
   __shared__ float s_red[256];
   __shared__ float s_o[HD];
-  const int s = blockIdx.x / H_q;
-  const int h = blockIdx.x - s * H_q;
+  const int row = blockIdx.x / H_q;
+  const int h = blockIdx.x - row * H_q;
   const int tid = threadIdx.x;
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < SD_MAX_SEQS; ++i)
+    if (i < seqs.n_seq && row >= seqs.s[i].row0) s = i;
   const SeqArg& A = seqs.s[s];
-  const int nc = A.n_chunks;
-  const float* base = part + ((int64_t)A.partial_begin + (int64_t)h * nc) * PF;
+  const int t = row - A.row0;
+  const int nc = (A.ctx_len - A.n_new + t + 1 + C - 1) / C;
+  const float* base = part + ((int64_t)A.partial_begin + ((int64_t)t * H_q + h) * A.n_chunks) * PF;
 
   // maximum of the chunk maxima (exact, order-free)
   float mx = -INFINITY;
@@ -331,7 +350,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
   __syncthreads();
   if (half == 0) {
     const float v = fdiv(fadd(O, s_o[d]), L);
-    const int64_t idx = ((int64_t)s * H_q + h) * HD + d;
+    const int64_t idx = ((int64_t)row * H_q + h) * HD + d;
     out[idx] = v;
     if (oq) {
       const float amax = group_max<32>(fabsf(v));
@@ -345,14 +364,16 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
 }  // namespace
 
 size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
-  int units = 0, parts = 0;
+  int units = 0, parts = 0, rows = 0;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.n_chunks = (x.ctx_len + C - 1) / C;
     x.unit_begin = units;
     x.partial_begin = parts;
+    x.row0 = rows;
     units += x.n_chunks * (H_q / kAttnGroup);
-    parts += x.n_chunks * H_q;
+    parts += x.n_chunks * H_q * x.n_new;
+    rows += x.n_new;
   }
   (void)H_kv;
   return (size_t)parts * PF;
@@ -366,7 +387,9 @@ hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_
   hipLaunchKernelGGL(k_attn_chunk, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(seqs.n_seq * H_q), dim3(256), 0, st, seqs, H_q, partials,
+  int rows = 0;
+  for (int s = 0; s < seqs.n_seq; ++s) rows += seqs.s[s].n_new;
+  hipLaunchKernelGGL(k_attn_combine, dim3(rows * H_q), dim3(256), 0, st, seqs, H_q, partials,
                      out, oq, od);
   return hipGetLastError();
 }

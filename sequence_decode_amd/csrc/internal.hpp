@@ -22,6 +22,7 @@ constexpr int kAttnChunk = SD_ATTN_CHUNK;
 constexpr int kAttnHeadDim = 128;
 constexpr int kAttnGroup = 4;       // query heads per KV head handled by one workgroup
 constexpr int kAttnPartialFloats = 132;  // m, l, 2 pad, o[128]
+constexpr int kAttnMaxNew = 4;           // query tokens per sequence in one attention call
 
 // Per-sequence view as passed by value to the attention / append kernels.
 struct SeqArg {
@@ -34,7 +35,9 @@ struct SeqArg {
   int32_t ctx_len;
   int32_t n_chunks;
   int32_t unit_begin;     // first workgroup index of this sequence
-  int32_t partial_begin;  // first partial slot of this sequence (per head: n_chunks slots)
+  int32_t partial_begin;  // first partial slot of this sequence (per token and head: n_chunks slots)
+  int32_t n_new;          // query tokens of the sequence (the newest n_new positions), 1..4
+  int32_t row0;           // q / out row of its first query token
 };
 
 struct SeqArgs {
@@ -78,7 +81,8 @@ hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads, int n_kv
                                const int32_t* pos, double theta, const SeqArgs& seqs,
                                hipStream_t st);
 
-// Fills per-sequence chunk bookkeeping; returns workspace floats needed.
+// Fills per-sequence chunk bookkeeping (n_new must be set); returns workspace
+// floats needed.
 size_t attn_layout(SeqArgs* seqs, int H_q, int H_kv);
 hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_q, int H_kv,
                        float scale, float* out, float* partials, int8_t* oq, float* od,

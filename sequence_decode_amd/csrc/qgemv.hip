@@ -431,21 +431,21 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_lds(
 // bits.
 //
 // A workgroup (8 waves) owns tiles of 16 rows.  For K chunk c it stages the
-// activations of pairs 64c .. 64c+63 for all tokens in LDS, in the padded
-// pair layout (dwords 0..15 per pair and token; dword 16 and the two block
-// scales go to a per-pair table of 16-token vectors).  Wave w takes pairs
-// 64c + 8w + j, j = 0..7, of the tile.  Lane (col, kq) loads bytes
-// 16kq .. 16kq+15 of row col's pair (global_load_dwordx4; the first 64 of the
-// pair's 68 bytes) and the same 16 bytes of token col's activations, so that
-// one MFMA sums the products of all 64 bytes.  Two MFMAs per pair give the two
-// exact block sums: the first with the block-B dwords of the activation
-// operand masked off, the second with the block-A dwords masked off (the
-// scale bytes meet activation zeros either way).  The last four weights of
-// block B (pair bytes 64..67) join the second sum through v_dot4.
-// The accumulator of lane (col, kq) holds tokens 4kq .. 4kq+3 of row col, so
-// the lane forms those four cells (0 + s_A) + s_B exactly as the narrow
-// kernels do and runs the 8-leaf tree of its pairs in registers.  The eight
-// wave subtrees meet in LDS as ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)), the last
+// activations of pairs 64c .. 64c+63 for all tokens in LDS in the padded pair
+// layout: dwords 1..16 of each (pair, token) as one 64-byte entry; dword 0
+// and the two block scales go to a per-pair table of 16-token vectors.  Wave
+// w takes pairs 64c + 8w + j, j = 0..7, of the tile.  Lane (col, kq) loads
+// pair bytes 4 + 16kq .. 19 + 16kq of row col (global_load_dwordx4) and pair
+// dword 0; the 16-byte pieces of lanes kq = 0, 1 lie in block A (weights 2..31
+// and the scale of B, which meets activation zeros), those of kq = 2, 3 in
+// block B.  Against token col's activation piece at the same bytes, one MFMA
+// sums block A (lanes kq >= 2 feed zeros, read from a zero region of LDS) and
+// one sums block B (lanes kq <= 1 feed zeros); weights 0, 1 of block A (pair
+// dword 0, whose scale bytes meet zeros) join the first sum through v_dot4.
+// The accumulator of lane (col, kq) holds tokens 4kq .. 4kq+3 of row col; the
+// lane forms those four cells (0 + s_A) + s_B exactly as the narrow kernels
+// do and runs the 8-leaf tree of its pairs in registers.  The eight wave
+// subtrees meet in LDS as ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)), the last
 // three levels of the 64-leaf tree, and the chunk sums are added in chunk
 // order.  A wave loads the next tile's weights while it works on the current
 // one (two register sets), and the per-tile sums alternate between two LDS
@@ -455,28 +455,17 @@ constexpr int kMfmaThreads = 512;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaPairs = 8;   // pairs per wave per chunk
 constexpr int kMfmaGroup = 8;   // tiles whose running totals a thread keeps across chunks
+// LDS (bytes): activations [64 pairs][16 tokens][16 dwords]; per-pair vectors
+// [64][3][16] (scale A, scale B, dword 0); zeros covering one wave's read span;
+// two tables [8 waves][16 rows][16 tokens]
+constexpr int kMfmaActBytes = 64 * 16 * 64;
+constexpr int kMfmaScBytes = 64 * 3 * 16 * 4;
+constexpr int kMfmaZeroBytes = kMfmaPairs * 1024 + 1024;
+constexpr int kMfmaTabBytes = 2 * kMfmaWaves * 256 * 4;
 
-// Lane l gets x of lane l % 16 (first 16-lane row), resp. of lane 32 + l % 16.
-__device__ __forceinline__ uint32_t bcast_row0(uint32_t x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  const uint32_t t = a[0];
-  const auto b = __builtin_amdgcn_permlane16_swap(t, t, false, false);
-  return b[0];
-}
-__device__ __forceinline__ uint32_t bcast_row2(uint32_t x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  const uint32_t t = a[1];
-  const auto b = __builtin_amdgcn_permlane16_swap(t, t, false, false);
-  return b[0];
-}
-
-__device__ __forceinline__ v4i and4(const u32x4a& v, uint32_t m0, uint32_t m1) {
-  return v4i{(int)(v.x & m0), (int)(v.y & m1), (int)(v.z & m1), (int)(v.w & m1)};
-}
-
-struct MfmaW {  // one wave's weights of one tile: bytes 16kq.. and dword 16 of 8 pairs
+struct MfmaW {  // one wave's weights of one tile: 16 bytes at 4 + 16kq and dword 0 of 8 pairs
   u32x4a q[kMfmaPairs];
-  uint32_t d16[kMfmaPairs];
+  uint32_t d0[kMfmaPairs];
 };
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
@@ -484,9 +473,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd, int n_tok,
     const float* residual, float* y, int64_t ldy, int n_tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  uint32_t* s_act = reinterpret_cast<uint32_t*>(lds_dyn);            // [64 pairs][16 tokens][16]
-  float* s_sc = reinterpret_cast<float*>(s_act + 64 * 16 * 16);      // [64 pairs][3][16 tokens]
-  float* s_tab = s_sc + 64 * 3 * 16;                                 // [2][8 waves][16 rows][16 tokens]
+  uint32_t* s_act = reinterpret_cast<uint32_t*>(lds_dyn);
+  float* s_sc = reinterpret_cast<float*>(lds_dyn + kMfmaActBytes);
+  uint32_t* s_zero = reinterpret_cast<uint32_t*>(lds_dyn + kMfmaActBytes + kMfmaScBytes);
+  float* s_tab = reinterpret_cast<float*>(lds_dyn + kMfmaActBytes + kMfmaScBytes + kMfmaZeroBytes);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop bounds
@@ -495,14 +485,20 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
   const int chunks = (P + 63) / 64;
   const int nb = 2 * P;
   const int my_tiles = (int)blockIdx.x < n_tiles ? (n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-  // dwords 4kq .. 4kq+3 of a pair: all block A for kq <= 1; for kq = 2 dword 8
-  // is block A (its last two weights) and 9..11 block B; all block B for kq = 3
-  const uint32_t mA0 = kq <= 2 ? ~0u : 0u;
-  const uint32_t mA1 = kq <= 1 ? ~0u : 0u;
-  const int trow = (tid >> 4) & 15;  // combine: threads 0..255 -> (row, token)
-  const int ttok = tid & 15;
+  // combine: 32 lanes of every wave -> output (row, token)
+  const bool comb = lane < 32;
+  const int cidx = wave * 32 + (lane & 31);
+  const int trow = cidx >> 4;
+  const int ttok = cidx & 15;
+  for (int e = tid; e < kMfmaZeroBytes / 4; e += kMfmaThreads) s_zero[e] = 0u;
+  // this lane's activation piece of pair j: act_l + 256 j dwords (tokens >= n_tok
+  // and the other block's lanes read zeros at the same offsets)
   const uint32_t* act_l = s_act + (wave * kMfmaPairs * 16 + col) * 16 + 4 * kq;
+  const uint32_t* zero_l = s_zero + col * 16 + 4 * kq;
+  const uint32_t* srcA = (kq <= 1 && col < n_tok) ? act_l : zero_l;
+  const uint32_t* srcB = (kq >= 2 && col < n_tok) ? act_l : zero_l;
   const float* sc_l = s_sc + wave * kMfmaPairs * 48 + 4 * kq;
+  const int bperm_b = (col + 16) * 4;  // lane holding pair dword 8 (the scale of B) for this row
 
   // weights of item (chunk c, tile) for this wave
   auto load_w = [&](MfmaW& B, int c, int tile) {
@@ -513,18 +509,18 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
     if (kMfmaPairs * wave + kMfmaPairs <= np) {
 #pragma unroll
       for (int j = 0; j < kMfmaPairs; ++j) {
-        B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 16 * kq);
-        B.d16[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j + 64);
+        B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 4 + 16 * kq);
+        B.d0[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j);
       }
     } else {
       // last chunk of a row: pairs past the end are zero cells
 #pragma unroll
       for (int j = 0; j < kMfmaPairs; ++j) {
         B.q[j] = u32x4a{0u, 0u, 0u, 0u};
-        B.d16[j] = 0u;
+        B.d0[j] = 0u;
         if (kMfmaPairs * wave + j < np) {
-          B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 16 * kq);
-          B.d16[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j + 64);
+          B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 4 + 16 * kq);
+          B.d0[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j);
         }
       }
     }
@@ -535,32 +531,34 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
     struct PairOps {
       v4i DA, DB;
       f32x4 xa, xb;
-      u32x4a a16;
+      u32x4a a0;
+      uint32_t dwb;
     };
     auto issue = [&](int j, PairOps& o) {
-      u32x4a av = u32x4a{0u, 0u, 0u, 0u};
-      if (col < n_tok) av = *reinterpret_cast<const u32x4a*>(act_l + j * 256);
+      const v4i opA = __builtin_bit_cast(v4i, *reinterpret_cast<const u32x4a*>(srcA + j * 256));
+      const v4i opB = __builtin_bit_cast(v4i, *reinterpret_cast<const u32x4a*>(srcB + j * 256));
       const v4i wop = __builtin_bit_cast(v4i, B.q[j]);
       const v4i zero = {0, 0, 0, 0};
-      o.DA = __builtin_amdgcn_mfma_i32_16x16x64_i8(and4(av, mA0, mA1), wop, zero, 0, 0, 0);
-      o.DB = __builtin_amdgcn_mfma_i32_16x16x64_i8(and4(av, ~mA0, ~mA1), wop, zero, 0, 0, 0);
+      o.DA = __builtin_amdgcn_mfma_i32_16x16x64_i8(opA, wop, zero, 0, 0, 0);
+      o.DB = __builtin_amdgcn_mfma_i32_16x16x64_i8(opB, wop, zero, 0, 0, 0);
       o.xa = *reinterpret_cast<const f32x4*>(sc_l + j * 48);
       o.xb = *reinterpret_cast<const f32x4*>(sc_l + j * 48 + 16);
-      o.a16 = *reinterpret_cast<const u32x4a*>(sc_l + j * 48 + 32);
+      o.a0 = *reinterpret_cast<const u32x4a*>(sc_l + j * 48 + 32);
+      o.dwb = (uint32_t)__builtin_amdgcn_ds_bpermute(bperm_b, (int)B.q[j].w);
       // keep program order: a pair's math must not wait for every pair's sums
       asm volatile("" : "+v"(o.DA), "+v"(o.DB));
     };
     float st[3][4];
     auto math = [&](int j, const PairOps& o) {
-      const float dwA = f16_bits_to_f32(bcast_row0(B.q[j].x));
-      const float dwB = f16_bits_to_f32(bcast_row2(B.q[j].x) >> 16);
+      const float dwA = f16_bits_to_f32(B.d0[j]);
+      const float dwB = f16_bits_to_f32(o.dwb >> 16);
       const float xar[4] = {o.xa.x, o.xa.y, o.xa.z, o.xa.w};
       const float xbr[4] = {o.xb.x, o.xb.y, o.xb.z, o.xb.w};
-      const uint32_t a16r[4] = {o.a16.x, o.a16.y, o.a16.z, o.a16.w};
+      const uint32_t a0r[4] = {o.a0.x, o.a0.y, o.a0.z, o.a0.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int iA = o.DA[r];
-        const int iB = __builtin_amdgcn_sdot4((int)B.d16[j], (int)a16r[r], o.DB[r], false);
+        const int iA = __builtin_amdgcn_sdot4((int)B.d0[j], (int)a0r[r], o.DA[r], false);
+        const int iB = o.DB[r];
         const float sA = fmul(fmul(dwA, xar[r]), (float)iA);
         const float sB = fmul(fmul(dwB, xbr[r]), (float)iB);
         float v = fadd(fadd(0.0f, sA), sB);
@@ -636,11 +634,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
           if (t < n_tok) {
             u32x4a* dst = reinterpret_cast<u32x4a*>(s_act + (pl * 16 + t) * 16);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) dst[v] = u32x4a{o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]};
+            for (int v = 0; v < 4; ++v)
+              dst[v] = u32x4a{o[4 * v + 1], o[4 * v + 2], o[4 * v + 3], o[4 * v + 4]};
           }
           s_sc[(pl * 3 + 0) * 16 + t] = da;
           s_sc[(pl * 3 + 1) * 16 + t] = db;
-          s_sc[(pl * 3 + 2) * 16 + t] = __uint_as_float(o[16]);
+          s_sc[(pl * 3 + 2) * 16 + t] = __uint_as_float(o[0]);
         }
         __syncthreads();
         staged = c;
@@ -648,14 +647,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
       // wait for this tile's weights here, once, before the next tile's loads
       // queue up behind them (the memory counter retires loads in order)
 #pragma unroll
-      for (int j = 0; j < kMfmaPairs; ++j) asm volatile("" ::"v"(cur.q[j]), "v"(cur.d16[j]));
+      for (int j = 0; j < kMfmaPairs; ++j) asm volatile("" ::"v"(cur.q[j]), "v"(cur.d0[j]));
       if (i + 1 < n_items) load_w(nxt, (i + 1) / ng, tile_of(i + 1));
       float sub[4];
       wave_sub(cur, sub);
       float* tab = s_tab + (i & 1) * (kMfmaWaves * 256);
       *reinterpret_cast<f32x4*>(tab + (wave * 16 + col) * 16 + 4 * kq) = f32x4{sub[0], sub[1], sub[2], sub[3]};
       __syncthreads();
-      if (tid < 256) {
+      if (comb) {
         const float* tb = tab + trow * 16 + ttok;
         const float cs = fadd(fadd(fadd(tb[0], tb[256]), fadd(tb[512], tb[768])),
                               fadd(fadd(tb[1024], tb[1280]), fadd(tb[1536], tb[1792])));
@@ -745,7 +744,7 @@ hipError_t launch_dma_nt(const GemvPlan& pl, const void* w, int64_t N, int64_t K
 
 }  // namespace
 
-size_t mfma_lds_bytes() { return (size_t)64 * 16 * 16 * 4 + 64 * 3 * 16 * 4 + 2 * 8 * 16 * 16 * 4; }
+size_t mfma_lds_bytes() { return (size_t)kMfmaActBytes + kMfmaScBytes + kMfmaZeroBytes + kMfmaTabBytes; }
 
 bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan) {
   if (N < 1 || K < 256 || K % 256 != 0 || n_tok < 1 || n_tok > SD_MAX_TOKENS) return false;

@@ -111,6 +111,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     sa.s[s].ld_tok = layer_elems_per_tok;
     sa.s[s].ld_head = D;
     sa.s[s].ctx_len = io->seqs[s].pos + 1;
+    sa.s[s].n_new = 1;
   }
   attn_layout(&sa, Hq, Hkv);
 

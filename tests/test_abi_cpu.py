@@ -102,6 +102,22 @@ def test_attention_rejections(L):
     assert L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128) == (9 + 128) * 32 * 132 * 4
 
 
+def test_verify_attention_rejections_and_workspace(L):
+    a = L.sd_decode_attn_verify
+    v2 = (_lib.SeqView * 2)(_view(258, 300), _view(3, 16))
+    nn = (ctypes.c_int32 * 2)(4, 3)
+    need = L.sd_decode_attn_verify_workspace_bytes(v2, nn, 2, 32, 128)
+    assert need == (2 * 4 + 1 * 3) * 32 * 132 * 4  # chunks x tokens x heads partials
+    assert L.sd_decode_attn_verify_workspace_bytes(v2, None, 2, 32, 128) == \
+        L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128)
+    for bad in ((0, 1), (5, 1), (4, 4)):   # 0 tokens, more than 4, more than ctx_len
+        b = (ctypes.c_int32 * 2)(*bad)
+        assert a(FAKE, 4096, v2, b, 2, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EINVAL
+        assert L.sd_decode_attn_verify_workspace_bytes(v2, b, 2, 32, 128) == 0
+    assert a(FAKE, 4096, v2, None, 2, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EINVAL
+    assert a(FAKE, 4096, v2, nn, 2, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
+
+
 def test_rope_kv_and_glue_rejections(L):
     r = L.sd_rope_posvec
     assert r(FAKE, 4, 32, 128, 4096, 128, FAKE, 1e6, 127, None) == SD_EINVAL

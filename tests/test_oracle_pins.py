@@ -374,6 +374,39 @@ def test_attn_multiseq_is_per_sequence(oracle_mod):
         assert np.array_equal(o[s], one)
 
 
+def test_attn_verify_is_the_causal_mask(oracle_mod):
+    """Burst tokens against the matrix form of causal attention: scores of all
+    burst rows against all keys, -inf above each row's position, row softmax,
+    times V (numpy fp64, a different route than the per-prefix oracle)."""
+    lens, news = [6, 9, 4], [3, 4, 4]
+    H_q, H_kv, Dh = 4, 2, 16
+    caches, qs = [], []
+    for s, (L, T) in enumerate(zip(lens, news)):
+        q, k, v = _attn_case(60 + s, L + 2, H_q, H_kv, Dh)
+        caches.append((k, v))
+        qs.append(synth.rng(70 + s).standard_normal((T, H_q, Dh), dtype=np.float32))
+    q_rows = np.concatenate(qs)
+    o = oracle_mod.attn_verify(q_rows, caches, lens, news, 0.3)
+    sc = float(np.float32(0.3))
+    r = 0
+    for s, (L, T) in enumerate(zip(lens, news)):
+        kk = caches[s][0].view(np.float16).astype(np.float64)[:L]
+        vv = caches[s][1].view(np.float16).astype(np.float64)[:L]
+        pos = np.arange(L - T, L)
+        mask = np.where(np.arange(L)[None, :] <= pos[:, None], 0.0, -np.inf)
+        for h in range(H_q):
+            S = sc * qs[s][:, h, :].astype(np.float64) @ kk[:, h // 2, :].T + mask
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            ref = (P @ vv[:, h // 2, :]).astype(np.float32)
+            got = o[r:r + T, h]
+            assert np.all(np.abs(got - ref) <= brute.ulp32(ref)), (s, h)
+        r += T
+    # one token per sequence is the single-query oracle; the last burst token sees everything
+    one = oracle_mod.attn_verify(q_rows[[2, 6, 10]], caches, lens, [1, 1, 1], 0.3)
+    assert np.array_equal(one, oracle_mod.attn_decode_multiseq(q_rows[[2, 6, 10]], caches, lens, 0.3))
+
+
 # ------------------------------------------------------------------ step glue
 
 def test_rmsnorm_decimal_and_closed_form(oracle_mod):

@@ -224,7 +224,7 @@ def decode_bench(torch, steps, warmup):
     ragged = [2050, 3072, 16384, 32768]
     g = torch.Generator(device="cuda")
     g.manual_seed(12)
-    span = warmup + steps + 1
+    span = warmup + steps + 4
     caches = [SeqCache.random_device(g, 32, ctx + span, 8, 128) for ctx in ragged]
     out = {"model": "random-init dense 32-layer, hidden 4096, 32/8 heads, ffn 14336, "
                     "vocab 151936, q8_0 weights, fp16 KV",
@@ -252,6 +252,24 @@ def decode_bench(torch, steps, warmup):
                                     "host_enqueue_ms": round(host / steps * 1e3, 3)}
             log(f"decode {label} n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step, "
                 f"host enqueue {host / steps * 1e3:.3f} ms)")
+    # verify steps: every sequence brings n_new proposed tokens (causal within the burst);
+    # the same positions are re-verified each timed step
+    for label, ctxs in (("ragged", ragged), ("ctx2050", [2050] * 4)):
+        for T in (2, 4):
+            r = StepRunner(model, caches, max_ctx=max(ctxs) + span, n_new=[T] * 4)
+            r.tokens.copy_(torch.arange(4 * T, dtype=torch.int32) + 7)
+            r.set_positions([c - 1 for c in ctxs])
+            for _ in range(warmup):
+                r.step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                r.step()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / steps
+            res[f"verify_{label}_n4_t{T}"] = {"tok_s": round(4 * T / dt, 2), "ms_per_step": round(dt * 1e3, 3),
+                                              "rows": 4 * T}
+            log(f"verify step {label} 4 sequences x {T} tokens: {4 * T / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
     # serial baseline: the four ragged sequences one at a time (one-token steps back to back)
     runners = [StepRunner(model, [caches[s]], max_ctx=ragged[s] + span) for s in range(4)]
     for s in range(4):

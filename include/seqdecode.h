@@ -47,7 +47,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 1
+#define SD_ABI_VERSION 2
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -307,36 +307,43 @@ typedef struct sd_step_seq {
   uint16_t* k_cache;
   uint16_t* v_cache;
   int32_t capacity;
-  int32_t pos;        /* position of this step's token; ctx_len = pos + 1 */
+  int32_t pos;        /* position of this sequence's first token in the step */
+  int32_t n_new;      /* its tokens in the step, 1..SD_ATTN_MAX_NEW (0 counts as 1):
+                         positions pos .. pos + n_new - 1, ctx_len = pos + n_new */
 } sd_step_seq;
 
-/* Inputs and outputs of one step. */
+/* Inputs and outputs of one step.  Token rows are packed by sequence:
+ * sequence s owns rows n_new[0] + .. + n_new[s-1] onward; rows = the sum. */
 typedef struct sd_step_io {
   int32_t n_seq;
   const sd_step_seq* seqs;   /* [host] n_seq entries */
-  const int32_t* tokens;     /* [n_seq] input token per sequence */
-  const int32_t* positions;  /* [n_seq] equal to seqs[s].pos */
-  float* logits;             /* [n_seq][vocab] */
-  int32_t* next_tokens;      /* [n_seq] greedy argmax of logits */
+  const int32_t* tokens;     /* [rows] input tokens */
+  const int32_t* positions;  /* [rows] seqs[s].pos + i for row i of sequence s */
+  float* logits;             /* [rows][vocab] */
+  int32_t* next_tokens;      /* [rows] greedy argmax of logits */
   void* ws;                  /* workspace, 256-byte aligned */
   size_t ws_bytes;
 } sd_step_io;
 
-/* Workspace bytes sd_decode_step needs for n_seq sequences whose contexts
- * are at most max_ctx keys (0 on invalid arguments). */
-size_t sd_decode_step_workspace_bytes(const sd_model* m, int n_seq, int max_ctx);
+/* Workspace bytes sd_decode_step needs for `rows` token rows (the sum of n_new;
+ * n_seq for one-token steps, at most SD_MAX_TOKENS) whose contexts are at most
+ * max_ctx keys (0 on invalid arguments). */
+size_t sd_decode_step_workspace_bytes(const sd_model* m, int rows, int max_ctx);
 
 /*
  * sd_decode_step -- one batched decode step for n_seq sequences: embedding,
  * n_layers x (rmsnorm, QKV projection, pos-vector RoPE, KV append, multi-
  * sequence attention, O projection + residual, rmsnorm, gate/up projection,
  * SwiGLU, down projection + residual), final rmsnorm, LM head, argmax.  The
- * projections run once for all sequences (ds4 pull request 604, "2. Single-GPU
- * decode batches don't scale").  Every sequence's logits and token are bitwise
- * those of a step with that sequence alone.
- * Requires 1 <= n_seq <= SD_MAX_SEQS, head_dim == 128, n_heads == 4*n_kv_heads,
- * hidden % 256 == 0, ffn % 256 == 0, n_heads*head_dim % 256 == 0,
- * 0 <= pos < capacity.
+ * projections run once for all token rows (ds4 pull request 604, "2.
+ * Single-GPU decode batches don't scale").  A sequence may bring up to
+ * SD_ATTN_MAX_NEW tokens (a verify step for proposed tokens, "feat(qwen36):
+ * complete concurrent serving implementation with speculation"); they attend
+ * causally.  Every row's logits and token are bitwise those of one-token steps
+ * of that sequence alone, run one after another over the same tokens.
+ * Requires 1 <= n_seq <= SD_MAX_SEQS, rows <= SD_MAX_TOKENS, head_dim == 128,
+ * n_heads == 4*n_kv_heads, hidden % 256 == 0, ffn % 256 == 0,
+ * n_heads*head_dim % 256 == 0, 0 <= pos and pos + n_new <= capacity.
  */
 int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream);
 

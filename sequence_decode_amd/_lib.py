@@ -51,7 +51,7 @@ class Model(ctypes.Structure):
 
 class StepSeq(ctypes.Structure):
     _fields_ = [("k_cache", P), ("v_cache", P), ("capacity", ctypes.c_int32),
-                ("pos", ctypes.c_int32)]
+                ("pos", ctypes.c_int32), ("n_new", ctypes.c_int32)]
 
 
 class StepIO(ctypes.Structure):

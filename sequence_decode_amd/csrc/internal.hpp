@@ -76,10 +76,11 @@ hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, in
 hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_new,
                             const SeqArgs& seqs, int H_kv, int D, hipStream_t st);
 // Fused step helper: rotates q (n_heads) and k (n_kv) rows of qkv in place and
-// writes rotated k and v into each sequence's cache row pos = ctx_len - 1.
-hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads, int n_kv, int head_dim,
-                               const int32_t* pos, double theta, const SeqArgs& seqs,
-                               hipStream_t st);
+// writes rotated k and v into the cache: row t is token t - row0 of its
+// sequence, at cache position ctx_len - n_new + (t - row0) (row0 set).
+hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int rows, int n_heads, int n_kv,
+                               int head_dim, const int32_t* pos, double theta,
+                               const SeqArgs& seqs, hipStream_t st);
 
 // Fills per-sequence chunk bookkeeping (n_new must be set); returns workspace
 // floats needed.

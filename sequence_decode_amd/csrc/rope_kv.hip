@@ -96,8 +96,12 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
     const int g = h - n_heads;
     const float* kh = row + (int64_t)(n_heads + g) * head_dim;
     const float* vh = row + (int64_t)(n_heads + n_kv + g) * head_dim;
-    const SeqArg& a = seqs.s[t];
-    const int64_t dst = (int64_t)(a.ctx_len - 1) * a.ld_tok + (int64_t)g * a.ld_head;
+    int sq = 0;
+#pragma unroll
+    for (int i = 1; i < SD_MAX_SEQS; ++i)
+      if (i < seqs.n_seq && t >= seqs.s[i].row0) sq = i;
+    const SeqArg& a = seqs.s[sq];
+    const int64_t dst = (int64_t)(a.ctx_len - a.n_new + (t - a.row0)) * a.ld_tok + (int64_t)g * a.ld_head;
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
       rope_angle(p, i, head_dim, theta, &c, &s);
@@ -128,10 +132,10 @@ hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_n
   return hipGetLastError();
 }
 
-hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads, int n_kv, int head_dim,
-                               const int32_t* pos, double theta, const SeqArgs& seqs,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(k_rope_kv_step, dim3(seqs.n_seq, n_heads + n_kv), dim3(64), 0, st, qkv,
+hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int rows, int n_heads, int n_kv,
+                               int head_dim, const int32_t* pos, double theta,
+                               const SeqArgs& seqs, hipStream_t st) {
+  hipLaunchKernelGGL(k_rope_kv_step, dim3(rows, n_heads + n_kv), dim3(64), 0, st, qkv,
                      ld_qkv, n_heads, n_kv, head_dim, pos, theta, seqs);
   return hipGetLastError();
 }

@@ -64,25 +64,29 @@ StepLayout layout(const sd_model* m, int n, int max_ctx) {
 
 extern "C" {
 
-size_t sd_decode_step_workspace_bytes(const sd_model* m, int n_seq, int max_ctx) {
-  if (!model_ok(m) || n_seq < 1 || n_seq > SD_MAX_SEQS || max_ctx < 1) return 0;
-  return layout(m, n_seq, max_ctx).total;
+size_t sd_decode_step_workspace_bytes(const sd_model* m, int rows, int max_ctx) {
+  if (!model_ok(m) || rows < 1 || rows > SD_MAX_TOKENS || max_ctx < 1) return 0;
+  return layout(m, rows, max_ctx).total;
 }
 
 int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) {
   if (!model_ok(m)) return SD_EUNSUPPORTED;
   if (!io || !io->seqs || !io->tokens || !io->positions || !io->logits || !io->next_tokens || !io->ws)
     return SD_EINVAL;
-  const int n = io->n_seq;
-  if (n < 1 || n > SD_MAX_SEQS) return SD_EINVAL;
-  int max_ctx = 1;
-  for (int s = 0; s < n; ++s) {
+  const int n_seq = io->n_seq;
+  if (n_seq < 1 || n_seq > SD_MAX_SEQS) return SD_EINVAL;
+  int max_ctx = 1, n = 0;  // n = token rows
+  for (int s = 0; s < n_seq; ++s) {
     const sd_step_seq& q = io->seqs[s];
-    if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || q.pos >= q.capacity) return SD_EINVAL;
-    if (q.pos + 1 > SD_MAX_CTX) return SD_EUNSUPPORTED;
+    const int T = q.n_new == 0 ? 1 : q.n_new;
+    if (T < 1 || T > SD_ATTN_MAX_NEW) return SD_EINVAL;
+    if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || q.pos > q.capacity - T) return SD_EINVAL;
+    if (q.pos + T > SD_MAX_CTX) return SD_EUNSUPPORTED;
     if (((uintptr_t)q.k_cache % 16) || ((uintptr_t)q.v_cache % 16)) return SD_EALIGN;
-    if (q.pos + 1 > max_ctx) max_ctx = q.pos + 1;
+    if (q.pos + T > max_ctx) max_ctx = q.pos + T;
+    n += T;
   }
+  if (n > SD_MAX_TOKENS) return SD_EINVAL;
   if ((uintptr_t)io->ws % 256 || (uintptr_t)io->logits % 4 || (uintptr_t)io->tokens % 4 ||
       (uintptr_t)io->positions % 4 || (uintptr_t)io->next_tokens % 4)
     return SD_EALIGN;
@@ -106,12 +110,13 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   const int64_t layer_elems_per_tok = (int64_t)Hkv * D;
 
   SeqArgs sa{};
-  sa.n_seq = n;
-  for (int s = 0; s < n; ++s) {
+  sa.n_seq = n_seq;
+  for (int s = 0; s < n_seq; ++s) {
+    const int T = io->seqs[s].n_new == 0 ? 1 : io->seqs[s].n_new;
     sa.s[s].ld_tok = layer_elems_per_tok;
     sa.s[s].ld_head = D;
-    sa.s[s].ctx_len = io->seqs[s].pos + 1;
-    sa.s[s].n_new = 1;
+    sa.s[s].ctx_len = io->seqs[s].pos + T;
+    sa.s[s].n_new = T;
   }
   attn_layout(&sa, Hq, Hkv);
 
@@ -123,7 +128,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   SD_TRY(launch_embed(m->tok_embd, m->vocab, H, io->tokens, n, x, st));
   for (int l = 0; l < m->n_layers; ++l) {
     const sd_layer_weights& L = m->layers[l];
-    for (int s = 0; s < n; ++s) {
+    for (int s = 0; s < n_seq; ++s) {
       const int64_t off = (int64_t)l * io->seqs[s].capacity * layer_elems_per_tok;
       sa.s[s].k = io->seqs[s].k_cache + off;
       sa.s[s].v = io->seqs[s].v_cache + off;
@@ -132,7 +137,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     }
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
     SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
-    SD_TRY(launch_rope_kv_step(qkv, QKV, Hq, Hkv, D, io->positions, m->rope_theta, sa, st));
+    SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, io->positions, m->rope_theta, sa, st));
     SD_TRY(launch_attn(qkv, QKV, sa, Hq, Hkv, scale, attn_o, part, aq, ad, st));
     SD_TRY(launch_qgemv(L.w_o, H, HqD, aq, ad, n, x, x, H, st));
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));

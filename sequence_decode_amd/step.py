@@ -102,40 +102,53 @@ class SeqCache:
 
 
 class StepRunner:
-    """Preallocated inputs/outputs/workspace for repeated sd_decode_step calls."""
+    """Preallocated inputs/outputs/workspace for repeated sd_decode_step calls.
 
-    def __init__(self, model: DecodeModel, caches, max_ctx: int):
+    n_new[s] (default 1) is the number of tokens sequence s brings to each step
+    (a verify step when above 1); token rows are packed by sequence."""
+
+    def __init__(self, model: DecodeModel, caches, max_ctx: int, n_new=None):
         import torch
         self.model = model
         self.caches = list(caches)
         n = len(self.caches)
+        self.n_new = [1] * n if n_new is None else [int(t) for t in n_new]
+        if len(self.n_new) != n:
+            raise ValueError("one n_new entry per sequence")
+        rows = sum(self.n_new)
         V = model.dims["vocab"]
         dev = model.device
-        need = _lib.load().sd_decode_step_workspace_bytes(ctypes.byref(model.struct), n, max_ctx)
+        need = _lib.load().sd_decode_step_workspace_bytes(ctypes.byref(model.struct), rows, max_ctx)
         if need == 0:
             raise ValueError("model or batch not supported by sd_decode_step")
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        self.logits = torch.empty((n, V), dtype=torch.float32, device=dev)
-        self.next_tokens = torch.empty(n, dtype=torch.int32, device=dev)
-        self.tokens = torch.zeros(n, dtype=torch.int32, device=dev)
-        self.positions = torch.zeros(n, dtype=torch.int32, device=dev)
+        self.logits = torch.empty((rows, V), dtype=torch.float32, device=dev)
+        self.next_tokens = torch.empty(rows, dtype=torch.int32, device=dev)
+        self.tokens = torch.zeros(rows, dtype=torch.int32, device=dev)
+        self.positions = torch.zeros(rows, dtype=torch.int32, device=dev)
         self._seqs = (_lib.StepSeq * n)()
         for s, c in enumerate(self.caches):
-            self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0)
+            self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0, self.n_new[s])
         self.io = _lib.StepIO(n, ctypes.cast(self._seqs, ctypes.c_void_p), self.tokens.data_ptr(),
                               self.positions.data_ptr(), self.logits.data_ptr(),
                               self.next_tokens.data_ptr(), self.ws.data_ptr(), need)
 
     def set_positions(self, pos):
-        """Sets every sequence's position (host structs and device copy)."""
+        """Sets every sequence's first position this step (host structs and the
+        device position of every token row)."""
         import torch
+        rows = []
         for s, p in enumerate(pos):
             self._seqs[s].pos = int(p)
-        self.positions.copy_(torch.tensor(list(pos), dtype=torch.int32))
+            rows += [int(p) + i for i in range(self.n_new[s])]
+        self.positions.copy_(torch.tensor(rows, dtype=torch.int32))
 
     def advance(self):
-        """Moves every sequence one position on and feeds the greedy tokens back,
-        without a host round trip (both updates are enqueued on the stream)."""
+        """One-token steps: moves every sequence one position on and feeds the
+        greedy tokens back, without a host round trip (both updates are
+        enqueued on the stream)."""
+        if any(t != 1 for t in self.n_new):
+            raise ValueError("advance() is for one-token steps")
         for s in range(len(self.caches)):
             self._seqs[s].pos += 1
         self.positions.add_(1)

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 1
+    assert L.sd_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -141,7 +141,8 @@ def test_step_rejections(L):
                    FAKE.value, ctypes.cast(lw, ctypes.c_void_p))
     need = L.sd_decode_step_workspace_bytes(ctypes.byref(m), 4, 32768)
     assert need > 0
-    assert L.sd_decode_step_workspace_bytes(ctypes.byref(m), 5, 32768) == 0
+    assert L.sd_decode_step_workspace_bytes(ctypes.byref(m), 17, 32768) == 0   # rows <= 16
+    assert L.sd_decode_step_workspace_bytes(ctypes.byref(m), 16, 32768) > need
     bad = _lib.Model(1, 4096, 32, 8, 64, 14336, 1000, 1e-6, 1e6, FAKE.value, FAKE.value,
                      FAKE.value, ctypes.cast(lw, ctypes.c_void_p))
     assert L.sd_decode_step_workspace_bytes(ctypes.byref(bad), 1, 16) == 0
@@ -150,6 +151,16 @@ def test_step_rejections(L):
                      FAKE.value, 0x100000, 1 << 30)
     assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EINVAL
     assert L.sd_decode_step(ctypes.byref(bad), ctypes.byref(io), None) == SD_EUNSUPPORTED
+    seqs[0].pos = 13
+    seqs[0].n_new = 4                 # positions 13..16 do not fit capacity 16
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EINVAL
+    seqs[0].n_new = 5                 # more than SD_ATTN_MAX_NEW
     seqs[0].pos = 3
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EINVAL
+    seqs[0].n_new = 4
     io.ws_bytes = 16
     assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EWORKSPACE
+    five = (_lib.StepSeq * 5)(*[_lib.StepSeq(FAKE.value, FAKE.value, 64, 3, 4) for _ in range(5)])
+    io5 = _lib.StepIO(5, ctypes.cast(five, ctypes.c_void_p), FAKE.value, FAKE.value, FAKE.value,
+                      FAKE.value, 0x100000, 1 << 30)
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io5), None) == SD_EINVAL

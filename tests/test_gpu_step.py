@@ -147,3 +147,43 @@ def test_step_matches_oracle_end_to_end(sd, model, model_host):
             gk = cs[s][0][L, pos[s]].view(np.float16).astype(np.float32)
             ok = ocache[s][0][L, pos[s]].view(np.float16).astype(np.float32)
             assert np.max(np.abs(gk - ok)) <= 2e-2 * max(1.0, np.max(np.abs(ok)))
+
+
+def test_verify_step_equals_one_token_steps(sd, model, model_host):
+    """A verify step (several tokens per sequence through the whole model, causal
+    within each sequence) gives, for every token row, bitwise the logits of
+    one-token steps of that sequence alone run one after another over the same
+    tokens, and leaves the same caches.  Bursts straddle a 256-key chunk edge."""
+    import torch
+    say("verify step == sequential one-token steps")
+    ch = _caches_host(3, seed=3300)
+    news, pos = [4, 2, 3], [10, 255, 100]
+    toks = [[5, 17, 333, 2], [999, 0], [41, 42, 43]]
+    caches = [SeqCache.from_host(*c) for c in ch]
+    r = StepRunner(model, caches, max_ctx=CAP, n_new=news)
+    r.tokens.copy_(torch.tensor(sum(toks, []), dtype=torch.int32))
+    r.set_positions(pos)
+    r.step()
+    lg, nt = host(r.logits), host(r.next_tokens)
+    row = 0
+    for s in range(3):
+        c1 = SeqCache.from_host(*ch[s])
+        rr = StepRunner(model, [c1], max_ctx=CAP)
+        for i in range(news[s]):
+            rr.tokens.copy_(torch.tensor([toks[s][i]], dtype=torch.int32))
+            rr.set_positions([pos[s] + i])
+            rr.step()
+            assert np.array_equal(bits(host(rr.logits)[0]), bits(lg[row])), (s, i)
+            assert int(host(rr.next_tokens)[0]) == int(nt[row])
+            row += 1
+        assert np.array_equal(host(c1.k), host(caches[s].k)) and np.array_equal(host(c1.v), host(caches[s].v))
+    # and against the oracle's sequential steps for the first sequence
+    h = model_host
+    m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
+                    h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
+                    h["w_lm"], h["layers"])
+    oc = [(ch[0][0].copy(), ch[0][1].copy())]
+    for i in range(news[0]):
+        olg, _ = ostep.decode_step(m, oc, [toks[0][i]], [pos[0] + i])
+        rel = np.linalg.norm(lg[i] - olg[0]) / np.linalg.norm(olg[0])
+        assert rel <= 1e-3, (i, rel)

@@ -47,7 +47,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 2
+#define SD_ABI_VERSION 3
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -151,11 +151,18 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
                    double theta, int n_rot, sd_stream_t stream);
 
 /* --------------------------------------------------- per-sequence KV views
- * One sequence's fp16 key and value caches (bit patterns), element (j, g, d) at
- * base[j*ld_tok + g*ld_head + d] (elements).  The struct array is [host] memory;
- * kernels receive the views by value in their arguments (ds4 pull request 604,
- * "Commit walkthrough / CUDA kernels").  ctx_len counts every key in use,
- * including the current token's (its position is ctx_len - 1).
+ * One sequence's fp16 key and value caches (bit patterns), element (row r,
+ * head g, dim d) at base[r*ld_tok + g*ld_head + d] (elements).  The struct
+ * array is [host] memory; kernels receive the views by value in their
+ * arguments (ds4 pull request 604, "Commit walkthrough / CUDA kernels", whose
+ * sequences each attend to their own KV ring).  ctx_len is one past the
+ * newest position (the current token sits at ctx_len - 1).
+ *   window  0: a token at position p attends to positions 0..p; else to the
+ *           last `window` positions max(0, p - window + 1)..p.
+ *   ring    0: position j lives in row j (ctx_len <= capacity);
+ *           1: the cache is a ring, position j in row j % capacity (needs
+ *           window >= 1 and room for every position still attended to).
+ * Zero-initialised trailing fields give the plain layout.
  */
 typedef struct sd_seqview {
   uint16_t* k;
@@ -164,17 +171,21 @@ typedef struct sd_seqview {
   int32_t capacity;
   int64_t ld_tok;
   int64_t ld_head;
+  int32_t window;
+  int32_t ring;
 } sd_seqview;
 
 /*
  * sd_kv_append_f16 -- write the current token's key and value rows.
- * For sequence s: row ctx_len_s - 1 of views[s] receives fp16(k_new[s]) and
+ * For sequence s: the row of position ctx_len_s - 1 of views[s] (row
+ * (ctx_len_s - 1) % capacity for a ring) receives fp16(k_new[s]) and
  * fp16(v_new[s]) (round to nearest even); no other row is touched (ds4 pull
  * request 604, "2. Single-GPU decode batches don't scale": the append runs per
  * sequence).
  *   k_new, v_new  [n_seq][H_kv][D] fp32 at sequence stride ld_new (elements).
  *   views         [host] n_seq views; 4-byte aligned bases, even strides.
- * Requires 1 <= n_seq <= SD_MAX_SEQS, 1 <= ctx_len <= capacity, D even.
+ * Requires 1 <= n_seq <= SD_MAX_SEQS, ctx_len >= 1, ctx_len <= capacity
+ * unless ring, D even.
  */
 int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
                      const sd_seqview* views, int n_seq, int H_kv, int D,
@@ -200,7 +211,12 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  *   views [host]: 16-byte aligned bases, ld_tok and ld_head multiples of 8.
  * Requires 1 <= n_seq <= SD_MAX_SEQS, D == 128, H_q % H_kv == 0,
  * H_q / H_kv == 4 (grouped-query attention with four query heads per KV head),
- * 1 <= ctx_len <= capacity, ctx_len <= SD_MAX_CTX (else SD_EUNSUPPORTED).
+ * ctx_len >= 1 and, for a plain view, ctx_len <= capacity; a ring needs
+ * window >= 1 and min(ctx_len, window + n_new - 1) <= capacity (n_new = 1
+ * here).  The keys attended to span at most SD_MAX_CTX positions (else
+ * SD_EUNSUPPORTED).  Windows: token at p sees max(0, p - window + 1)..p; the
+ * chunks are aligned to absolute positions, so a windowed result is the same
+ * in a ring as in a plain cache holding the same rows.
  */
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
                             int n_seq, int H_q, int H_kv, int D, float scale,
@@ -300,6 +316,8 @@ typedef struct sd_model {
   const float* out_norm;           /* [hidden] */
   const void* w_lm_head;           /* q8_0 [vocab][hidden] */
   const sd_layer_weights* layers;  /* [host] n_layers entries */
+  int32_t n_rot;                   /* rotated dims: the last n_rot of each head (0 = head_dim) */
+  int32_t window;                  /* attention window in positions (0 = the whole context) */
 } sd_model;
 
 /* One sequence's state for a step: caches [n_layers][capacity][H_kv][D] fp16. */
@@ -310,6 +328,8 @@ typedef struct sd_step_seq {
   int32_t pos;        /* position of this sequence's first token in the step */
   int32_t n_new;      /* its tokens in the step, 1..SD_ATTN_MAX_NEW (0 counts as 1):
                          positions pos .. pos + n_new - 1, ctx_len = pos + n_new */
+  int32_t ring;       /* 1: the caches are rings of capacity positions (needs a model
+                         window); position j in row j % capacity */
 } sd_step_seq;
 
 /* Inputs and outputs of one step.  Token rows are packed by sequence:

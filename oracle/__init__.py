@@ -153,19 +153,29 @@ def attn_decode_multiseq(q: np.ndarray, caches, ctx_lens, scale: float) -> np.nd
                      for s in range(q.shape[0])])
 
 
-def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float) -> np.ndarray:
+def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, window: int = 0,
+                rings=None) -> np.ndarray:
     """Several query tokens per sequence, packed by sequence (the verification of
     proposed tokens in "feat(qwen36): complete concurrent serving implementation
     with speculation"): the n_new[s] newest positions of sequence s, token i at
-    position p = ctx_lens[s] - n_new[s] + i attending to keys 0..p.  Each token
-    is the one-token decode attention over its own prefix of p + 1 keys.
+    position p = ctx_lens[s] - n_new[s] + i.  A token attends to positions
+    lo..p, lo = max(0, p - window + 1) with a window, else 0; it is the one-token
+    decode attention over exactly those keys.  rings[s] true: the cache is a
+    ring (ds4 pull request 604, "Commit walkthrough / CUDA kernels": each
+    sequence attends to its own KV ring), position j stored in row j % capacity.
     q_rows [sum(n_new)][H_q][D] -> same shape."""
     out = []
     r = 0
     for s, T in enumerate(n_new):
+        k_bits, v_bits = caches[s]
+        cap = k_bits.shape[0]
         for i in range(T):
             p = ctx_lens[s] - T + i
-            out.append(attn_decode_one(q_rows[r], caches[s][0], caches[s][1], p + 1, scale))
+            lo = max(0, p - window + 1) if window else 0
+            rows = np.arange(lo, p + 1)
+            if rings is not None and rings[s]:
+                rows = rows % cap
+            out.append(attn_decode_one(q_rows[r], k_bits[rows], v_bits[rows], p + 1 - lo, scale))
             r += 1
     return np.stack(out)
 

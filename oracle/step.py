@@ -7,8 +7,9 @@ feed-forward and output head run on the batch, and the logits land one row per
 sequence.  The pages define no model; the layer used here is the plain dense
 pre-norm block with no biases:
 
-    a  = rmsnorm(x) ; q, k, v = split(W_qkv a) ; q, k = rope(q, k, pos)
-    cache[pos] = fp16(k), fp16(v) ; o = attention(q, cache[0 .. pos])
+    a  = rmsnorm(x) ; q, k, v = split(W_qkv a) ; q, k = rope(q, k, pos)  (last n_rot dims)
+    cache[pos] = fp16(k), fp16(v) ; o = attention(q, cache[lo .. pos])  (lo = 0, or
+                                                   pos - window + 1 with a window)
     h  = x + W_o o
     n  = rmsnorm(h) ; g, u = split(W_gate_up n) ; x' = h + W_down (silu(g) * u)
 
@@ -25,10 +26,12 @@ class Model:
     """Host copy of a synthetic model: fields mirror the library's model struct."""
 
     def __init__(self, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, eps, theta,
-                 tok_embd_bits, out_norm, w_lm, layers):
+                 tok_embd_bits, out_norm, w_lm, layers, n_rot=0, window=0):
         self.hidden, self.n_heads, self.n_kv_heads = hidden, n_heads, n_kv_heads
         self.head_dim, self.ffn, self.vocab = head_dim, ffn, vocab
         self.eps, self.theta = eps, theta
+        self.n_rot = n_rot or head_dim        # rotated dims: the last n_rot of each head
+        self.window = window                  # attention window in positions, 0 = none
         self.tok_embd_bits = tok_embd_bits    # uint16 [vocab][hidden]
         self.out_norm = out_norm              # fp32 [hidden]
         self.w_lm = w_lm                      # q8_0 blob [vocab][hidden]
@@ -56,13 +59,13 @@ def decode_step(m: Model, caches, tokens, pos):
         q = qkv[:, :Hq * D].reshape(n, Hq, D)
         k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(n, Hkv, D)
         v = qkv[:, (Hq + Hkv) * D:].reshape(n, Hkv, D)
-        q = O.rope_posvec(q, pos, m.theta)
-        k = O.rope_posvec(k, pos, m.theta)
+        q = O.rope_posvec(q, pos, m.theta, m.n_rot)
+        k = O.rope_posvec(k, pos, m.theta, m.n_rot)
         for s in range(n):
             caches[s][0][li, pos[s]] = O.f32_to_f16_bits(k[s])
             caches[s][1][li, pos[s]] = O.f32_to_f16_bits(v[s])
-        o = O.attn_decode_multiseq(q, [(c[0][li], c[1][li]) for c in caches],
-                                   [int(p) + 1 for p in pos], scale)
+        o = O.attn_verify(q, [(c[0][li], c[1][li]) for c in caches],
+                          [int(p) + 1 for p in pos], [1] * n, scale, window=m.window)
         oq, od = O.quantize_q8_act(o.reshape(n, Hq * D))
         h = O.qgemv_q8_0(L["w_o"], H, Hq * D, oq, od, residual=x)
         nrm = O.rmsnorm(h, L["ffn_norm"], m.eps)

@@ -112,10 +112,13 @@ def rope_posvec(x, pos, theta, n_rot=None, stream=None):
     return x
 
 
-def seqview(k, v, ctx_len):
-    """View of one sequence's caches k, v: [capacity][H_kv][D] fp16 (or int16 bits)."""
+def seqview(k, v, ctx_len, window=0, ring=False):
+    """View of one sequence's caches k, v: [capacity][H_kv][D] fp16 (or int16
+    bits).  window > 0: tokens attend to their last `window` positions; ring:
+    position j lives in row j % capacity."""
     cap, H_kv, D = k.shape
-    return SeqView(k.data_ptr(), v.data_ptr(), int(ctx_len), int(cap), H_kv * D, D)
+    return SeqView(k.data_ptr(), v.data_ptr(), int(ctx_len), int(cap), H_kv * D, D, int(window),
+                   1 if ring else 0)
 
 
 def _views(views):

@@ -33,7 +33,8 @@ SIGNATURES = {
 
 class SeqView(ctypes.Structure):
     _fields_ = [("k", P), ("v", P), ("ctx_len", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("ld_tok", ctypes.c_int64), ("ld_head", ctypes.c_int64)]
+                ("ld_tok", ctypes.c_int64), ("ld_head", ctypes.c_int64),
+                ("window", ctypes.c_int32), ("ring", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -46,12 +47,13 @@ class Model(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
-                ("tok_embd", P), ("out_norm", P), ("w_lm_head", P), ("layers", P)]
+                ("tok_embd", P), ("out_norm", P), ("w_lm_head", P), ("layers", P),
+                ("n_rot", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 class StepSeq(ctypes.Structure):
     _fields_ = [("k_cache", P), ("v_cache", P), ("capacity", ctypes.c_int32),
-                ("pos", ctypes.c_int32), ("n_new", ctypes.c_int32)]
+                ("pos", ctypes.c_int32), ("n_new", ctypes.c_int32), ("ring", ctypes.c_int32)]
 
 
 class StepIO(ctypes.Structure):

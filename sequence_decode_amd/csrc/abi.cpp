@@ -10,6 +10,8 @@
 // type surfaced as an error).
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 
 using namespace sd;
@@ -35,13 +37,29 @@ int check_gemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const floa
   return SD_OK;
 }
 
-int check_views(const sd_seqview* views, int n_seq, int D, bool attn) {
+int check_views(const sd_seqview* views, int n_seq, int D, bool attn,
+                const int32_t* n_new = nullptr) {
   if (!views || n_seq < 1 || n_seq > SD_MAX_SEQS) return SD_EINVAL;
   for (int s = 0; s < n_seq; ++s) {
     const sd_seqview& v = views[s];
     if (!v.k || !v.v) return SD_EINVAL;
-    if (v.capacity < 1 || v.ctx_len < 1 || v.ctx_len > v.capacity) return SD_EINVAL;
-    if (attn && v.ctx_len > SD_MAX_CTX) return SD_EUNSUPPORTED;
+    if (v.capacity < 1 || v.ctx_len < 1) return SD_EINVAL;
+    if (v.window < 0 || (v.ring != 0 && v.ring != 1)) return SD_EINVAL;
+    const int T = n_new ? n_new[s] : 1;
+    if (T < 1 || T > SD_ATTN_MAX_NEW || T > v.ctx_len) return SD_EINVAL;
+    if (v.ring) {
+      // every position still attended to must have its own row
+      if (v.window < 1) return SD_EINVAL;
+      const int64_t span = v.ctx_len < (int64_t)v.window + T - 1 ? v.ctx_len : (int64_t)v.window + T - 1;
+      if (span > v.capacity) return SD_EINVAL;
+    } else if (v.ctx_len > v.capacity) {
+      return SD_EINVAL;
+    }
+    if (attn) {
+      const int lo0 = v.window ? std::max(0, v.ctx_len - T - v.window + 1) : 0;
+      if ((v.ctx_len - 1) / SD_ATTN_CHUNK - lo0 / SD_ATTN_CHUNK + 1 > SD_MAX_CTX / SD_ATTN_CHUNK)
+        return SD_EUNSUPPORTED;
+    }
     if (v.ld_head < D || v.ld_tok < D) return SD_EINVAL;
     const size_t al = attn ? 16 : 4;
     if (!aligned(v.k, al) || !aligned(v.v, al)) return SD_EALIGN;
@@ -64,15 +82,13 @@ void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a, const int32_t*
     x.ld_head = views[s].ld_head;
     x.ctx_len = views[s].ctx_len;
     x.n_new = n_new ? n_new[s] : 1;
+    x.window = views[s].window;
+    x.ring_cap = views[s].ring ? views[s].capacity : 0;
   }
 }
 
 // n_new [host]: query tokens per sequence, 1..SD_ATTN_MAX_NEW and <= ctx_len
-bool check_new(const sd_seqview* views, const int32_t* n_new, int n_seq) {
-  for (int s = 0; s < n_seq; ++s)
-    if (n_new[s] < 1 || n_new[s] > SD_ATTN_MAX_NEW || n_new[s] > views[s].ctx_len) return false;
-  return true;
-}
+
 
 int attn_common(const float* q, int64_t ld_q, const sd_seqview* views, const int32_t* n_new,
                 int n_seq, int H_q, int H_kv, int D, float scale, float* out, void* ws,
@@ -80,9 +96,8 @@ int attn_common(const float* q, int64_t ld_q, const sd_seqview* views, const int
   if (!q || !out || !ws || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SD_EINVAL;
   if (D != kAttnHeadDim || H_q / H_kv != kAttnGroup) return SD_EUNSUPPORTED;
   if (ld_q < (int64_t)H_q * D || !isfinite(scale)) return SD_EINVAL;
-  int rc = check_views(views, n_seq, D, true);
+  int rc = check_views(views, n_seq, D, true, n_new);
   if (rc != SD_OK) return rc;
-  if (n_new && !check_new(views, n_new, n_seq)) return SD_EINVAL;
   if (!aligned(q, 16) || ld_q % 4 != 0 || !aligned(out, 16) || !aligned(ws, 16)) return SD_EALIGN;
   SeqArgs a;
   fill_seqargs(views, n_seq, &a, n_new);
@@ -168,9 +183,7 @@ size_t sd_decode_attn_verify_workspace_bytes(const sd_seqview* views, const int3
                                              int n_seq, int H_q, int D) {
   if (!views || n_seq < 1 || n_seq > SD_MAX_SEQS || H_q < 1 || D != kAttnHeadDim) return 0;
   SeqArgs a;
-  for (int s = 0; s < n_seq; ++s)
-    if (views[s].ctx_len < 1) return 0;
-  if (n_new && !check_new(views, n_new, n_seq)) return 0;
+  if (check_views(views, n_seq, D, true, n_new) != SD_OK) return 0;
   fill_seqargs(views, n_seq, &a, n_new);
   return attn_layout(&a, H_q, H_q / kAttnGroup) * sizeof(float);
 }

@@ -104,9 +104,17 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const SeqArg& A = seqs.s[s];
   const int local = blockIdx.x - A.unit_begin;
   const int g = local / A.n_chunks;
-  const int c = local - g * A.n_chunks;
+  const int ci = local - g * A.n_chunks;  // chunk of this unit, counted from c0
+  const int c = A.c0 + ci;                // absolute chunk: positions c*C .. c*C + C-1
   const int j0 = c * C;
-  const int nk = min(C, A.ctx_len - j0);
+  const int nk = min(C, A.ctx_len - j0);  // keys of the chunk below ctx_len
+  const int jlo = max(0, A.lo0 - j0);     // keys of the chunk below any query's window
+  // ring caches: row of chunk key jl (jlo <= jl < nk) runs on from that of jlo
+  // and wraps once at the ring's end (the keys in use span at most the ring)
+  auto krow = [&](int prow0, int jl) {
+    const int r = prow0 + (jl - jlo);
+    return r >= A.ring_cap ? r - A.ring_cap : r;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,24 +123,47 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int kg = lane >> 4;   // MFMA k-group
   const int wk = wave * kWaveKeys;
   // MFMA column col = 4 * (burst token) + (head in the group); token tk sits at
-  // position ctx_len - T + tk and sees the keys up to it
+  // position p = ctx_len - T + tk and sees the keys from max(0, p - window + 1)
+  // (or 0) up to p
   const int T = A.n_new;
   const int tk = col >> 2;
   const int hh = col & (kAttnGroup - 1);
   const bool colv = tk < T;
-  const int nk_col = colv ? min(C, A.ctx_len - T + tk + 1 - j0) : 0;
+  const int p_col = A.ctx_len - T + tk;
+  const int nk_col = colv ? min(C, p_col + 1 - j0) : 0;
+  const int jlo_col = A.window ? max(0, p_col - A.window + 1) - j0 : 0;
 
   // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
   const int jk = wk + 8 * (col >> 2) + (col & 3);
-  const uint16_t* kr = A.k + (int64_t)g * A.ld_head + (int64_t)(j0 + jk) * A.ld_tok + 8 * kg;
+  const uint16_t* kb = A.k + (int64_t)g * A.ld_head + 8 * kg;
+  // plain caches: row = position, so tile t's rows are a fixed stride apart.
+  // Keys outside jlo .. nk-1 read the nearest key in use: their scores are
+  // replaced by -inf below, so what they load does not matter (it is finite).
+  const bool lin = A.ring_cap == 0;
   u32x4a ka[4][4];
+  if (__builtin_expect(lin, 1)) {
+    // plain cache: row = position, tile t's rows a fixed stride apart; keys
+    // past the end load zeros, keys below a window are real rows (masked below)
+    const uint16_t* kr = kb + (int64_t)(j0 + jk) * A.ld_tok;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int dj = 32 * (t >> 1) + 4 * (t & 1);
+    for (int t = 0; t < 4; ++t) {
+      const int dj = 32 * (t >> 1) + 4 * (t & 1);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      ka[t][kk] = u32x4a{0u, 0u, 0u, 0u};
-      if (jk + dj < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + dj * A.ld_tok + 32 * kk);
+      for (int kk = 0; kk < 4; ++kk) {
+        ka[t][kk] = u32x4a{0u, 0u, 0u, 0u};
+        if (jk + dj < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + dj * A.ld_tok + 32 * kk);
+      }
+    }
+  } else {
+    // ring: keys outside jlo .. nk-1 read the nearest key in use (their scores
+    // are replaced by -inf below)
+    const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+      const uint16_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
     }
   }
   // ---- q (score B operands): column col = (token tk, head g*4 + hh), dims 32kk + 8kg ..
@@ -153,17 +184,32 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   // 16-byte piece (l%16) ^ 2 vswz(row).
   uint8_t* vw = s_v + wave * kWaveVBytes;
   {
+    // keys past the end read the last key, and in a ring keys below jlo read
+    // key jlo (their weight is 0); a plain cache's keys below a window are
+    // real rows and read as they are
     const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
     const int jv = wk + (lane >> 4);
-    const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + jv) * A.ld_tok);
-    const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + nk - 1) * A.ld_tok);
-    const int64_t step4 = 4 * A.ld_tok * 2;
+    if (__builtin_expect(lin, 1)) {
+      const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + jv) * A.ld_tok);
+      const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + nk - 1) * A.ld_tok);
+      const int64_t step4 = 4 * A.ld_tok * 2;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const int piece = (lane & 15) ^ (2 * vswz(r));
-      const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int piece = (lane & 15) ^ (2 * vswz(r));
+        const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+      }
+    } else {
+      const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int piece = (lane & 15) ^ (2 * vswz(r));
+        const int jl = min(max(jv + 4 * i, jlo), nk - 1);
+        const uint8_t* row = reinterpret_cast<const uint8_t*>(vbase + (int64_t)krow(prow0, jl) * A.ld_tok);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+      }
     }
   }
 
@@ -195,7 +241,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int jl = wk + 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
-      z[t][r] = jl < nk_col ? fmul(acc[r], scale) : -INFINITY;
+      z[t][r] = (jl < nk_col && jl >= jlo_col) ? fmul(acc[r], scale) : -INFINITY;
     }
   }
   // ---- the chunk maximum per column, shared by the four waves
@@ -264,7 +310,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     const int cc = idx / HD;
     const int d = idx - cc * HD;
     const int t2 = cc >> 2;
-    if (c * C > A.ctx_len - T + t2) continue;  // chunk past this token's position
+    const int p2 = A.ctx_len - T + t2;
+    if (j0 > p2) continue;  // chunk past this token's position
+    if (A.window && j0 + C <= p2 - A.window + 1) continue;  // chunk before its window
     float O = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -273,7 +321,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     }
     const float Mh = fmaxf(fmaxf(s_m[0][cc], s_m[1][cc]), fmaxf(s_m[2][cc], s_m[3][cc]));
     const int h = g * kAttnGroup + (cc & (kAttnGroup - 1));
-    float* dst = part + ((int64_t)A.partial_begin + ((int64_t)t2 * H_q + h) * A.n_chunks + c) * PF;
+    float* dst = part + ((int64_t)A.partial_begin + ((int64_t)t2 * H_q + h) * A.n_chunks + ci) * PF;
     dst[4 + d] = O;
     if (d == 0) {
       dst[0] = Mh;
@@ -306,8 +354,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
     if (i < seqs.n_seq && row >= seqs.s[i].row0) s = i;
   const SeqArg& A = seqs.s[s];
   const int t = row - A.row0;
-  const int nc = (A.ctx_len - A.n_new + t + 1 + C - 1) / C;
-  const float* base = part + ((int64_t)A.partial_begin + ((int64_t)t * H_q + h) * A.n_chunks) * PF;
+  const int p = A.ctx_len - A.n_new + t;
+  const int lo = A.window ? max(0, p - A.window + 1) : 0;
+  const int nc = p / C - lo / C + 1;  // this token's chunks: those of positions lo..p
+  const float* base =
+      part + ((int64_t)A.partial_begin + ((int64_t)t * H_q + h) * A.n_chunks + (lo / C - A.c0)) * PF;
 
   // maximum of the chunk maxima (exact, order-free)
   float mx = -INFINITY;
@@ -367,7 +418,9 @@ size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
   int units = 0, parts = 0, rows = 0;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
-    x.n_chunks = (x.ctx_len + C - 1) / C;
+    x.lo0 = x.window ? (x.ctx_len - x.n_new - x.window + 1 > 0 ? x.ctx_len - x.n_new - x.window + 1 : 0) : 0;
+    x.c0 = x.lo0 / C;
+    x.n_chunks = (x.ctx_len - 1) / C - x.c0 + 1;
     x.unit_begin = units;
     x.partial_begin = parts;
     x.row0 = rows;

@@ -38,7 +38,15 @@ struct SeqArg {
   int32_t partial_begin;  // first partial slot of this sequence (per token and head: n_chunks slots)
   int32_t n_new;          // query tokens of the sequence (the newest n_new positions), 1..4
   int32_t row0;           // q / out row of its first query token
+  int32_t window;         // attention window in positions, 0 = whole context
+  int32_t ring_cap;       // ring of ring_cap rows (position j in row j % ring_cap), 0 = plain
+  int32_t lo0;            // lowest position any query token of the call attends to
+  int32_t c0;             // chunk (absolute, lo0 / SD_ATTN_CHUNK) of the first work unit
 };
+
+__device__ __host__ inline int64_t seq_row(const SeqArg& a, int64_t j) {
+  return a.ring_cap ? j % a.ring_cap : j;
+}
 
 struct SeqArgs {
   SeqArg s[SD_MAX_SEQS];
@@ -77,9 +85,10 @@ hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_n
                             const SeqArgs& seqs, int H_kv, int D, hipStream_t st);
 // Fused step helper: rotates q (n_heads) and k (n_kv) rows of qkv in place and
 // writes rotated k and v into the cache: row t is token t - row0 of its
-// sequence, at cache position ctx_len - n_new + (t - row0) (row0 set).
+// sequence, at position ctx_len - n_new + (t - row0) (row0 set); the last
+// n_rot dims of each head rotate.
 hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int rows, int n_heads, int n_kv,
-                               int head_dim, const int32_t* pos, double theta,
+                               int head_dim, int n_rot, const int32_t* pos, double theta,
                                const SeqArgs& seqs, hipStream_t st);
 
 // Fills per-sequence chunk bookkeeping (n_new must be set); returns workspace

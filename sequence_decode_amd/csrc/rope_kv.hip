@@ -63,7 +63,7 @@ __global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ k_n
   const int s = blockIdx.x;
   const int g = blockIdx.y;
   const SeqArg& a = seqs.s[s];
-  const int64_t row = (int64_t)(a.ctx_len - 1) * a.ld_tok + (int64_t)g * a.ld_head;
+  const int64_t row = seq_row(a, a.ctx_len - 1) * a.ld_tok + (int64_t)g * a.ld_head;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     const int64_t src = (int64_t)s * ld_new + (int64_t)g * D + d;
     a.k_w[row + d] = f32_to_f16_bits(k_new[src]);
@@ -72,22 +72,25 @@ __global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ k_n
 }
 
 // Fused step helper.  Workgroup (t, h) for h < n_heads rotates query head h of
-// token t in place; for n_heads <= h < n_heads + n_kv it rotates key head
-// g = h - n_heads and writes it, with value head g, into sequence t's cache.
+// token row t in place; for n_heads <= h < n_heads + n_kv it rotates key head
+// g = h - n_heads and writes it, with value head g, into the cache row of the
+// row's position.  Only the last n_rot dims of a head rotate (the same pairs
+// and angles as k_rope_posvec); the others pass through.
 __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads,
-                                                     int n_kv, int head_dim,
+                                                     int n_kv, int head_dim, int n_rot,
                                                      const int32_t* __restrict__ pos,
                                                      double theta, SeqArgs seqs) {
   const int t = blockIdx.x;
   const int h = blockIdx.y;
-  const int half = head_dim / 2;
+  const int off = head_dim - n_rot;
+  const int half = n_rot / 2;
   const int p = pos[t];
   float* row = qkv + (int64_t)t * ld_qkv;
   if (h < n_heads) {
-    float* v = row + (int64_t)h * head_dim;
+    float* v = row + (int64_t)h * head_dim + off;
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
-      rope_angle(p, i, head_dim, theta, &c, &s);
+      rope_angle(p, i, n_rot, theta, &c, &s);
       rotate(v[i], v[i + half], c, s, &y0, &y1);
       v[i] = y0;
       v[i + half] = y1;
@@ -101,16 +104,16 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
     for (int i = 1; i < SD_MAX_SEQS; ++i)
       if (i < seqs.n_seq && t >= seqs.s[i].row0) sq = i;
     const SeqArg& a = seqs.s[sq];
-    const int64_t dst = (int64_t)(a.ctx_len - a.n_new + (t - a.row0)) * a.ld_tok + (int64_t)g * a.ld_head;
+    const int64_t dst = seq_row(a, a.ctx_len - a.n_new + (t - a.row0)) * a.ld_tok + (int64_t)g * a.ld_head;
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
-      rope_angle(p, i, head_dim, theta, &c, &s);
-      rotate(kh[i], kh[i + half], c, s, &y0, &y1);
-      a.k_w[dst + i] = f32_to_f16_bits(y0);
-      a.k_w[dst + i + half] = f32_to_f16_bits(y1);
-      a.v_w[dst + i] = f32_to_f16_bits(vh[i]);
-      a.v_w[dst + i + half] = f32_to_f16_bits(vh[i + half]);
+      rope_angle(p, i, n_rot, theta, &c, &s);
+      rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
+      a.k_w[dst + off + i] = f32_to_f16_bits(y0);
+      a.k_w[dst + off + i + half] = f32_to_f16_bits(y1);
     }
+    for (int d = threadIdx.x; d < off; d += blockDim.x) a.k_w[dst + d] = f32_to_f16_bits(kh[d]);
+    for (int d = threadIdx.x; d < head_dim; d += blockDim.x) a.v_w[dst + d] = f32_to_f16_bits(vh[d]);
   }
 }
 
@@ -133,10 +136,10 @@ hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_n
 }
 
 hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int rows, int n_heads, int n_kv,
-                               int head_dim, const int32_t* pos, double theta,
+                               int head_dim, int n_rot, const int32_t* pos, double theta,
                                const SeqArgs& seqs, hipStream_t st) {
   hipLaunchKernelGGL(k_rope_kv_step, dim3(rows, n_heads + n_kv), dim3(64), 0, st, qkv,
-                     ld_qkv, n_heads, n_kv, head_dim, pos, theta, seqs);
+                     ld_qkv, n_heads, n_kv, head_dim, n_rot, pos, theta, seqs);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ bool model_ok(const sd_model* m) {
   if (m->hidden % 256 != 0 || m->ffn % 256 != 0 || (m->n_heads * m->head_dim) % 256 != 0) return false;
   if (m->hidden > 32768 || m->ffn > 32768) return false;
   if (!(m->rms_eps >= 0.0f) || !(m->rope_theta > 0.0)) return false;
+  if (m->n_rot < 0 || m->n_rot > m->head_dim || m->n_rot % 2 != 0 || m->window < 0) return false;
   for (int l = 0; l < m->n_layers; ++l) {
     const sd_layer_weights& L = m->layers[l];
     if (!L.w_qkv || !L.w_o || !L.w_gate_up || !L.w_down || !L.attn_norm || !L.ffn_norm) return false;
@@ -80,10 +81,27 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     const sd_step_seq& q = io->seqs[s];
     const int T = q.n_new == 0 ? 1 : q.n_new;
     if (T < 1 || T > SD_ATTN_MAX_NEW) return SD_EINVAL;
-    if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || q.pos > q.capacity - T) return SD_EINVAL;
-    if (q.pos + T > SD_MAX_CTX) return SD_EUNSUPPORTED;
+    if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || (q.ring != 0 && q.ring != 1)) return SD_EINVAL;
+    if (q.ring) {
+      // a ring keeps the positions still attended to: window + T - 1 of them at most
+      if (m->window < 1 || q.pos > 0x7fffffff - T) return SD_EINVAL;
+      const int64_t span = q.pos + T < (int64_t)m->window + T - 1 ? q.pos + T : (int64_t)m->window + T - 1;
+      if (span > q.capacity) return SD_EINVAL;
+    } else if (q.pos > q.capacity - T) {
+      return SD_EINVAL;
+    }
+    {
+      const int lo0 = m->window ? (q.pos - m->window + 1 > 0 ? q.pos - m->window + 1 : 0) : 0;
+      if ((q.pos + T - 1) / SD_ATTN_CHUNK - lo0 / SD_ATTN_CHUNK + 1 > SD_MAX_CTX / SD_ATTN_CHUNK)
+        return SD_EUNSUPPORTED;
+    }
     if (((uintptr_t)q.k_cache % 16) || ((uintptr_t)q.v_cache % 16)) return SD_EALIGN;
-    if (q.pos + T > max_ctx) max_ctx = q.pos + T;
+    {
+      // attention chunks of this sequence are at most those of max_ctx keys
+      const int lo0 = m->window ? (q.pos - m->window + 1 > 0 ? q.pos - m->window + 1 : 0) : 0;
+      const int keys = q.pos + T - (lo0 / SD_ATTN_CHUNK) * SD_ATTN_CHUNK;
+      if (keys > max_ctx) max_ctx = keys;
+    }
     n += T;
   }
   if (n > SD_MAX_TOKENS) return SD_EINVAL;
@@ -117,6 +135,8 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     sa.s[s].ld_head = D;
     sa.s[s].ctx_len = io->seqs[s].pos + T;
     sa.s[s].n_new = T;
+    sa.s[s].window = m->window;
+    sa.s[s].ring_cap = io->seqs[s].ring ? io->seqs[s].capacity : 0;
   }
   attn_layout(&sa, Hq, Hkv);
 
@@ -137,7 +157,8 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     }
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
     SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
-    SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, io->positions, m->rope_theta, sa, st));
+    SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, m->n_rot ? m->n_rot : D, io->positions,
+                               m->rope_theta, sa, st));
     SD_TRY(launch_attn(qkv, QKV, sa, Hq, Hkv, scale, attn_o, part, aq, ad, st));
     SD_TRY(launch_qgemv(L.w_o, H, HqD, aq, ad, n, x, x, H, st));
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));

@@ -32,7 +32,8 @@ class DecodeModel:
         self.struct = _lib.Model(d["n_layers"], d["hidden"], d["n_heads"], d["n_kv_heads"],
                                  d["head_dim"], d["ffn"], d["vocab"], float(d["eps"]),
                                  float(d["theta"]), tok_embd.data_ptr(), out_norm.data_ptr(),
-                                 w_lm.data_ptr(), ctypes.cast(self._lw, ctypes.c_void_p))
+                                 w_lm.data_ptr(), ctypes.cast(self._lw, ctypes.c_void_p),
+                                 int(d.get("n_rot", 0)), int(d.get("window", 0)))
         self.device = tok_embd.device
         del torch
 
@@ -54,6 +55,7 @@ class DecodeModel:
             layers.append({k: dev(v) for k, v in L.items()})
         dims = {k: h[k] for k in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim",
                                   "ffn", "vocab", "eps", "theta")}
+        dims.update({k: h[k] for k in ("n_rot", "window") if k in h})
         return cls(dims, layers, dev(h["tok_embd_bits"], torch.float16), dev(h["out_norm"]),
                    dev(h["w_lm"]))
 
@@ -107,7 +109,7 @@ class StepRunner:
     n_new[s] (default 1) is the number of tokens sequence s brings to each step
     (a verify step when above 1); token rows are packed by sequence."""
 
-    def __init__(self, model: DecodeModel, caches, max_ctx: int, n_new=None):
+    def __init__(self, model: DecodeModel, caches, max_ctx: int, n_new=None, ring=False):
         import torch
         self.model = model
         self.caches = list(caches)
@@ -128,7 +130,8 @@ class StepRunner:
         self.positions = torch.zeros(rows, dtype=torch.int32, device=dev)
         self._seqs = (_lib.StepSeq * n)()
         for s, c in enumerate(self.caches):
-            self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0, self.n_new[s])
+            self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0, self.n_new[s],
+                                         1 if ring else 0)
         self.io = _lib.StepIO(n, ctypes.cast(self._seqs, ctypes.c_void_p), self.tokens.data_ptr(),
                               self.positions.data_ptr(), self.logits.data_ptr(),
                               self.next_tokens.data_ptr(), self.ws.data_ptr(), need)

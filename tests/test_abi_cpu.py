@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 2
+    assert L.sd_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -116,6 +116,29 @@ def test_verify_attention_rejections_and_workspace(L):
         assert L.sd_decode_attn_verify_workspace_bytes(v2, b, 2, 32, 128) == 0
     assert a(FAKE, 4096, v2, None, 2, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EINVAL
     assert a(FAKE, 4096, v2, nn, 2, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
+
+
+def test_window_and_ring_rejections(L):
+    a = L.sd_decode_attn_multiseq
+    def view(ctx, cap, window, ring):
+        return (_lib.SeqView * 1)(_lib.SeqView(FAKE.value, FAKE.value, ctx, cap, 1024, 128, window, ring))
+    ok = view(5000, 300, 256, 1)          # ring: 256 positions in use fit 300 rows
+    assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, 0, None) == SD_EWORKSPACE
+    need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
+    assert need == 2 * 32 * 132 * 4       # positions 4744..4999 touch chunks 18 and 19
+    for bad in (view(5000, 300, 0, 1),    # a ring needs a window
+                view(5000, 200, 256, 1),  # the window does not fit the ring
+                view(10, 16, -1, 0),      # negative window
+                view(10, 16, 0, 2),       # unknown ring flag
+                view(17, 16, 4, 0)):      # a plain view still needs ctx_len <= capacity
+        assert a(FAKE, 4096, bad, 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EINVAL
+        assert L.sd_decode_attn_workspace_bytes(bad, 1, 32, 128) == 0
+    nn = (ctypes.c_int32 * 1)(4)          # a burst of 4 needs window + 3 rows in the ring
+    assert L.sd_decode_attn_verify(FAKE, 4096, view(5000, 258, 256, 1), nn, 1, 32, 8, 128, 0.088,
+                                   FAKE, FAKE, 1 << 30, None) == SD_EINVAL
+    assert L.sd_decode_attn_verify_workspace_bytes(view(5000, 259, 256, 1), nn, 1, 32, 128) > 0
+    huge = view(1 << 30, 1 << 20, 0, 0)
+    assert L.sd_decode_attn_workspace_bytes(huge, 1, 32, 128) == 0
 
 
 def test_rope_kv_and_glue_rejections(L):

@@ -187,3 +187,56 @@ def test_verify_step_equals_one_token_steps(sd, model, model_host):
         olg, _ = ostep.decode_step(m, oc, [toks[0][i]], [pos[0] + i])
         rel = np.linalg.norm(lg[i] - olg[0]) / np.linalg.norm(olg[0])
         assert rel <= 1e-3, (i, rel)
+
+
+def test_window_rope_tail_step_vs_oracle_and_ring(sd):
+    """A model with a 100-position attention window and RoPE on the last 64 of
+    128 head dims: the step agrees with the oracle's step, and the same steps on
+    ring caches of window + 3 rows give bitwise the plain-cache logits, for
+    one-token steps and for a verify step."""
+    import torch
+    say("window + rope tail step, ring == plain")
+    h = synth.model_host(3400, **DIMS)
+    h["n_rot"], h["window"] = 64, 100
+    model = DecodeModel.from_host(h)
+    m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
+                    h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
+                    h["w_lm"], h["layers"], n_rot=64, window=100)
+    ch = _caches_host(2, seed=3401)
+    toks, pos = [3, 700], [150, 290]
+    lg, nt, cs = _run(model, ch, toks, pos)
+    ocache = [(k.copy(), v.copy()) for k, v in ch]
+    olg, ont = ostep.decode_step(m, ocache, toks, pos)
+    rel = np.linalg.norm(lg - olg) / np.linalg.norm(olg)
+    say(f"  logits normwise relative error vs oracle: {rel:.3e}")
+    assert rel <= 1e-3
+    # ring caches: each layer keeps the last 103 positions at row j % 103
+    cap = 103
+    rings = []
+    for k, v in ch:
+        rk = np.zeros((k.shape[0], cap) + k.shape[2:], k.dtype)
+        rings.append((rk, np.zeros_like(rk)))
+    for s in range(2):
+        k, v = ch[s]
+        for j in range(pos[s] - cap + 1, pos[s]):
+            rings[s][0][:, j % cap], rings[s][1][:, j % cap] = k[:, j], v[:, j]
+    plain = [SeqCache.from_host(*c) for c in ch]
+    ring = [SeqCache.from_host(*c) for c in rings]
+    rp = StepRunner(model, plain, max_ctx=CAP)
+    rr = StepRunner(model, ring, max_ctx=CAP, ring=True)
+    t = list(toks)
+    for step in range(6):
+        for r_ in (rp, rr):
+            r_.tokens.copy_(torch.tensor(t, dtype=torch.int32))
+            r_.set_positions([p + step for p in pos])
+            r_.step()
+        assert np.array_equal(bits(host(rp.logits)), bits(host(rr.logits))), step
+        t = [int(x) for x in host(rp.next_tokens)]
+    # a verify step of 3 tokens per sequence on both
+    vp = StepRunner(model, plain, max_ctx=CAP, n_new=[3, 3])
+    vr = StepRunner(model, ring, max_ctx=CAP, n_new=[3, 3], ring=True)
+    for r_ in (vp, vr):
+        r_.tokens.copy_(torch.tensor([9, 8, 7, 6, 5, 4], dtype=torch.int32))
+        r_.set_positions([p + 6 for p in pos])
+        r_.step()
+    assert np.array_equal(bits(host(vp.logits)), bits(host(vr.logits)))

@@ -407,6 +407,44 @@ def test_attn_verify_is_the_causal_mask(oracle_mod):
     assert np.array_equal(one, oracle_mod.attn_decode_multiseq(q_rows[[2, 6, 10]], caches, lens, 0.3))
 
 
+def test_attn_window_and_ring_storage(oracle_mod):
+    """Windowed attention: a window covering the context changes nothing; a
+    window of one returns the newest value; the band-masked matrix form agrees;
+    a ring holding the same positions gives the same bits."""
+    L, T, cap = 40, 3, 16
+    H_q, H_kv, Dh = 4, 2, 8
+    q0, k, v = _attn_case(80, L, H_q, H_kv, Dh)
+    q = synth.rng(81).standard_normal((T, H_q, Dh), dtype=np.float32)
+    caches = [(k, v)]
+    full = oracle_mod.attn_verify(q, caches, [L], [T], 0.3)
+    assert np.array_equal(oracle_mod.attn_verify(q, caches, [L], [T], 0.3, window=L + 5), full)
+    one = oracle_mod.attn_verify(q, caches, [L], [T], 0.3, window=1)
+    vv = v.view(np.float16).astype(np.float32)
+    for i in range(T):
+        for h in range(H_q):
+            assert np.array_equal(one[i, h], vv[L - T + i, h // 2])
+    W = 11
+    win = oracle_mod.attn_verify(q, caches, [L], [T], 0.3, window=W)
+    kk = k.view(np.float16).astype(np.float64)
+    sc = float(np.float32(0.3))
+    pos = np.arange(L - T, L)
+    j = np.arange(L)[None, :]
+    band = np.where((j <= pos[:, None]) & (j > pos[:, None] - W), 0.0, -np.inf)
+    for h in range(H_q):
+        S = sc * q[:, h, :].astype(np.float64) @ kk[:, h // 2, :].T + band
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        ref = (P @ vv.astype(np.float64)[:, h // 2, :]).astype(np.float32)
+        assert np.all(np.abs(win[:, h] - ref) <= brute.ulp32(ref))
+    # the same positions kept in a ring of 16 rows (position j in row j % 16)
+    rk = np.zeros((cap,) + k.shape[1:], k.dtype)
+    rv = np.zeros_like(rk)
+    for jj in range(L - cap, L):
+        rk[jj % cap], rv[jj % cap] = k[jj], v[jj]
+    ring = oracle_mod.attn_verify(q, [(rk, rv)], [L], [T], 0.3, window=W, rings=[True])
+    assert np.array_equal(ring, win)
+
+
 # ------------------------------------------------------------------ step glue
 
 def test_rmsnorm_decimal_and_closed_form(oracle_mod):

@@ -270,6 +270,29 @@ def decode_bench(torch, steps, warmup):
             res[f"verify_{label}_n4_t{T}"] = {"tok_s": round(4 * T / dt, 2), "ms_per_step": round(dt * 1e3, 3),
                                               "rows": 4 * T}
             log(f"verify step {label} 4 sequences x {T} tokens: {4 * T / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
+    # paged pool: the four ragged sequences in one shared pool of 64-row blocks at
+    # shuffled places (block-table lookup in the append and attention kernels)
+    bs = 64
+    nb = [(c + span + bs - 1) // bs for c in ragged]
+    place = torch.randperm(sum(nb), generator=g, device="cuda").to(torch.int32)
+    tables = [place[sum(nb[:s]):sum(nb[:s + 1])].contiguous() for s in range(4)]
+    pool = SeqCache.random_device(g, 32, sum(nb) * bs, 8, 128)
+    r = StepRunner(model, [pool] * 4, max_ctx=max(ragged) + span, block_tables=tables, block_size=bs)
+    r.tokens.copy_(torch.arange(4, dtype=torch.int32) + 7)
+    r.set_positions([c - 1 for c in ragged])
+    for _ in range(warmup):
+        r.step()
+        r.advance()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+        r.advance()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    res["paged64_ragged_n4"] = {"tok_s": round(4 / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
+    log(f"decode paged (64-row blocks) ragged n_seq=4: {4 / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
+    del r, pool
     # serial baseline: the four ragged sequences one at a time (one-token steps back to back)
     runners = [StepRunner(model, [caches[s]], max_ctx=ragged[s] + span) for s in range(4)]
     for s in range(4):

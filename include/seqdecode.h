@@ -47,7 +47,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 3
+#define SD_ABI_VERSION 4
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -162,6 +162,19 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
  *   ring    0: position j lives in row j (ctx_len <= capacity);
  *           1: the cache is a ring, position j in row j % capacity (needs
  *           window >= 1 and room for every position still attended to).
+ *   block_table  NULL, or a paged cache ("feat(qwen36): complete concurrent
+ *           serving implementation with speculation", "Summary": a shared
+ *           paged KV pool with per-sequence block tables): k and v are a pool
+ *           of capacity rows in blocks of block_size rows, and position j
+ *           lives in row block_table[j / block_size] * block_size
+ *           + j % block_size.  block_table is [device] int32, 4-byte aligned,
+ *           with an entry for every block up to position ctx_len - 1 (entries
+ *           of blocks wholly below a window may hold anything); block_size is
+ *           64, 128 or 256 and divides capacity; an entry outside
+ *           0 .. capacity / block_size - 1 is clamped into it, so no access
+ *           leaves the pool.  ctx_len is not bounded by capacity (blocks may
+ *           be shared).  Not combined with ring.  The table is read by the
+ *           kernels on the stream: it must stay valid until they are done.
  * Zero-initialised trailing fields give the plain layout.
  */
 typedef struct sd_seqview {
@@ -173,19 +186,23 @@ typedef struct sd_seqview {
   int64_t ld_head;
   int32_t window;
   int32_t ring;
+  const int32_t* block_table;
+  int32_t block_size;
+  int32_t reserved;
 } sd_seqview;
 
 /*
  * sd_kv_append_f16 -- write the current token's key and value rows.
  * For sequence s: the row of position ctx_len_s - 1 of views[s] (row
- * (ctx_len_s - 1) % capacity for a ring) receives fp16(k_new[s]) and
+ * (ctx_len_s - 1) % capacity for a ring, the block table's row for a paged
+ * view) receives fp16(k_new[s]) and
  * fp16(v_new[s]) (round to nearest even); no other row is touched (ds4 pull
  * request 604, "2. Single-GPU decode batches don't scale": the append runs per
  * sequence).
  *   k_new, v_new  [n_seq][H_kv][D] fp32 at sequence stride ld_new (elements).
  *   views         [host] n_seq views; 4-byte aligned bases, even strides.
  * Requires 1 <= n_seq <= SD_MAX_SEQS, ctx_len >= 1, ctx_len <= capacity
- * unless ring, D even.
+ * for a plain view, D even.
  */
 int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
                      const sd_seqview* views, int n_seq, int H_kv, int D,
@@ -216,7 +233,8 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  * here).  The keys attended to span at most SD_MAX_CTX positions (else
  * SD_EUNSUPPORTED).  Windows: token at p sees max(0, p - window + 1)..p; the
  * chunks are aligned to absolute positions, so a windowed result is the same
- * in a ring as in a plain cache holding the same rows.
+ * in a ring as in a plain cache holding the same rows.  A paged view (see
+ * sd_seqview) gives the same bits as a plain cache holding the same keys.
  */
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
                             int n_seq, int H_q, int H_kv, int D, float scale,
@@ -330,6 +348,11 @@ typedef struct sd_step_seq {
                          positions pos .. pos + n_new - 1, ctx_len = pos + n_new */
   int32_t ring;       /* 1: the caches are rings of capacity positions (needs a model
                          window); position j in row j % capacity */
+  const int32_t* block_table;  /* NULL, or [device] block table of a paged cache: the caches
+                                  are pools [n_layers][capacity][H_kv][D] in blocks of
+                                  block_size rows (64, 128 or 256), as in sd_seqview */
+  int32_t block_size;
+  int32_t reserved;
 } sd_step_seq;
 
 /* Inputs and outputs of one step.  Token rows are packed by sequence:
@@ -363,7 +386,8 @@ size_t sd_decode_step_workspace_bytes(const sd_model* m, int rows, int max_ctx);
  * of that sequence alone, run one after another over the same tokens.
  * Requires 1 <= n_seq <= SD_MAX_SEQS, rows <= SD_MAX_TOKENS, head_dim == 128,
  * n_heads == 4*n_kv_heads, hidden % 256 == 0, ffn % 256 == 0,
- * n_heads*head_dim % 256 == 0, 0 <= pos and pos + n_new <= capacity.
+ * n_heads*head_dim % 256 == 0, 0 <= pos and, for plain caches,
+ * pos + n_new <= capacity (rings and paged pools as in sd_seqview).
  */
 int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream);
 

@@ -154,7 +154,7 @@ def attn_decode_multiseq(q: np.ndarray, caches, ctx_lens, scale: float) -> np.nd
 
 
 def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, window: int = 0,
-                rings=None) -> np.ndarray:
+                rings=None, tables=None, block_size: int = 0) -> np.ndarray:
     """Several query tokens per sequence, packed by sequence (the verification of
     proposed tokens in "feat(qwen36): complete concurrent serving implementation
     with speculation"): the n_new[s] newest positions of sequence s, token i at
@@ -163,6 +163,10 @@ def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, windo
     decode attention over exactly those keys.  rings[s] true: the cache is a
     ring (ds4 pull request 604, "Commit walkthrough / CUDA kernels": each
     sequence attends to its own KV ring), position j stored in row j % capacity.
+    tables[s] not None: the cache is a pool of blocks of block_size rows shared
+    through per-sequence block tables ("feat(qwen36): complete concurrent serving
+    implementation with speculation", "Summary"), position j stored in row
+    tables[s][j // block_size] * block_size + j % block_size.
     q_rows [sum(n_new)][H_q][D] -> same shape."""
     out = []
     r = 0
@@ -175,6 +179,9 @@ def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, windo
             rows = np.arange(lo, p + 1)
             if rings is not None and rings[s]:
                 rows = rows % cap
+            if tables is not None and tables[s] is not None:
+                rows = np.asarray(tables[s], np.int64)[rows // block_size] * block_size \
+                    + rows % block_size
             out.append(attn_decode_one(q_rows[r], k_bits[rows], v_bits[rows], p + 1 - lo, scale))
             r += 1
     return np.stack(out)

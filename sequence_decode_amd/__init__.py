@@ -112,13 +112,21 @@ def rope_posvec(x, pos, theta, n_rot=None, stream=None):
     return x
 
 
-def seqview(k, v, ctx_len, window=0, ring=False):
+def seqview(k, v, ctx_len, window=0, ring=False, block_table=None, block_size=0):
     """View of one sequence's caches k, v: [capacity][H_kv][D] fp16 (or int16
     bits).  window > 0: tokens attend to their last `window` positions; ring:
-    position j lives in row j % capacity."""
+    position j lives in row j % capacity; block_table (int32 device tensor, kept
+    alive by the caller): k, v are a pool of blocks of block_size rows and
+    position j lives in row block_table[j // block_size] * block_size
+    + j % block_size."""
+    import torch
     cap, H_kv, D = k.shape
+    bt = 0
+    if block_table is not None:
+        _need(block_table, torch.int32, "block_table")
+        bt = block_table.data_ptr()
     return SeqView(k.data_ptr(), v.data_ptr(), int(ctx_len), int(cap), H_kv * D, D, int(window),
-                   1 if ring else 0)
+                   1 if ring else 0, bt, int(block_size), 0)
 
 
 def _views(views):

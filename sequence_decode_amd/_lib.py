@@ -34,7 +34,8 @@ SIGNATURES = {
 class SeqView(ctypes.Structure):
     _fields_ = [("k", P), ("v", P), ("ctx_len", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("ld_tok", ctypes.c_int64), ("ld_head", ctypes.c_int64),
-                ("window", ctypes.c_int32), ("ring", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("ring", ctypes.c_int32),
+                ("block_table", P), ("block_size", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -53,7 +54,8 @@ class Model(ctypes.Structure):
 
 class StepSeq(ctypes.Structure):
     _fields_ = [("k_cache", P), ("v_cache", P), ("capacity", ctypes.c_int32),
-                ("pos", ctypes.c_int32), ("n_new", ctypes.c_int32), ("ring", ctypes.c_int32)]
+                ("pos", ctypes.c_int32), ("n_new", ctypes.c_int32), ("ring", ctypes.c_int32),
+                ("block_table", P), ("block_size", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class StepIO(ctypes.Structure):

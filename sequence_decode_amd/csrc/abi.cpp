@@ -47,7 +47,13 @@ int check_views(const sd_seqview* views, int n_seq, int D, bool attn,
     if (v.window < 0 || (v.ring != 0 && v.ring != 1)) return SD_EINVAL;
     const int T = n_new ? n_new[s] : 1;
     if (T < 1 || T > SD_ATTN_MAX_NEW || T > v.ctx_len) return SD_EINVAL;
-    if (v.ring) {
+    if (v.block_table) {
+      // paged: blocks of 64, 128 or 256 rows, whole blocks in the pool
+      if (v.ring) return SD_EINVAL;
+      if (v.block_size != 64 && v.block_size != 128 && v.block_size != 256) return SD_EINVAL;
+      if (v.capacity % v.block_size != 0) return SD_EINVAL;
+      if (!aligned(v.block_table, 4)) return SD_EALIGN;
+    } else if (v.ring) {
       // every position still attended to must have its own row
       if (v.window < 1) return SD_EINVAL;
       const int64_t span = v.ctx_len < (int64_t)v.window + T - 1 ? v.ctx_len : (int64_t)v.window + T - 1;
@@ -84,6 +90,11 @@ void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a, const int32_t*
     x.n_new = n_new ? n_new[s] : 1;
     x.window = views[s].window;
     x.ring_cap = views[s].ring ? views[s].capacity : 0;
+    if (views[s].block_table) {
+      x.btab = views[s].block_table;
+      x.bshift = __builtin_ctz((unsigned)views[s].block_size);
+      x.n_blocks = views[s].capacity / views[s].block_size;
+    }
   }
 }
 

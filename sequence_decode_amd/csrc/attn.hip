@@ -12,9 +12,9 @@
 //   four sequences (a sequence-per-workgroup split would give 32 units).
 // * A workgroup loads each key and value row of its chunk once for the four
 //   query heads that share the KV head; every load is issued before any
-//   arithmetic.  Scores come from MFMA (fp16 keys as stored, the fp32 query as
-//   an exact fp16 hi + lo pair), the weighted value sum from v_fma_mix (fp16
-//   values straight into fp32 FMAs).
+//   arithmetic.  Scores and the weighted value sum both come from MFMA (fp16
+//   keys and values as stored, the fp32 query and the fp32 weights as exact
+//   fp16 hi + lo pairs, fp32 accumulation).
 // * Each wave keeps its own softmax partial over its 64 keys, and the four
 //   merge in wave order: partial (m, l, o[128]) per head and chunk.
 // * A sequence may bring up to four query tokens, its newest positions (the
@@ -24,6 +24,11 @@
 //   the 16 columns of the MFMA tiles, and each column keeps its own key limit
 //   and its own chunk count ceil((p_i + 1) / SD_ATTN_CHUNK), so token i gets
 //   bitwise what a one-token call over p_i + 1 keys gives.
+// * Caches: plain (position j in row j), ring (row j % capacity, with a
+//   sliding window), or paged (a per-sequence block table into a shared pool,
+//   "feat(qwen36): complete concurrent serving implementation with
+//   speculation", "Summary").  Which rows hold the keys does not enter any
+//   sum, so the three give the same bits for the same keys.
 // * A second kernel merges the partials of each (sequence, head) with fixed
 //   reduction shapes.  Every sum has a fixed shape, so a sequence's output bits do not
 //   depend on the other sequences in the call.
@@ -140,11 +145,21 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   // Keys outside jlo .. nk-1 read the nearest key in use: their scores are
   // replaced by -inf below, so what they load does not matter (it is finite).
   const bool lin = A.ring_cap == 0;
+  // plain and paged caches: the wave's 64 positions j0 + wk + x are the 64
+  // consecutive rows jrow + wk + x (a block holds a multiple of 64 positions and
+  // chunks start at multiples of C); jlast is the row of the chunk's last key.
+  // A wave wholly past the end loads no K and reads V from jlast only.
+  int64_t jrow = j0, jlast = j0 + nk - 1;
+  if (A.btab) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    jlast = seq_row(A, j0 + nk - 1);
+    jrow = wv * kWaveKeys < nk ? seq_row(A, j0 + wv * kWaveKeys) - wv * kWaveKeys : jlast;
+  }
   u32x4a ka[4][4];
   if (__builtin_expect(lin, 1)) {
-    // plain cache: row = position, tile t's rows a fixed stride apart; keys
-    // past the end load zeros, keys below a window are real rows (masked below)
-    const uint16_t* kr = kb + (int64_t)(j0 + jk) * A.ld_tok;
+    // plain / paged cache: tile t's rows a fixed stride apart; keys past the end
+    // load zeros, keys below a window are real rows (masked below)
+    const uint16_t* kr = kb + (jrow + jk) * A.ld_tok;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int dj = 32 * (t >> 1) + 4 * (t & 1);
@@ -190,8 +205,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
     const int jv = wk + (lane >> 4);
     if (__builtin_expect(lin, 1)) {
-      const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + jv) * A.ld_tok);
-      const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + (int64_t)(j0 + nk - 1) * A.ld_tok);
+      const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (jrow + jv) * A.ld_tok);
+      const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + jlast * A.ld_tok);
       const int64_t step4 = 4 * A.ld_tok * 2;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {

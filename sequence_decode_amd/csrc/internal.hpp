@@ -42,9 +42,18 @@ struct SeqArg {
   int32_t ring_cap;       // ring of ring_cap rows (position j in row j % ring_cap), 0 = plain
   int32_t lo0;            // lowest position any query token of the call attends to
   int32_t c0;             // chunk (absolute, lo0 / SD_ATTN_CHUNK) of the first work unit
+  const int32_t* btab;    // paged cache: block table (device), else null
+  int32_t bshift;         // log2 of the block size (paged)
+  int32_t n_blocks;       // blocks in the pool (paged)
 };
 
-__device__ __host__ inline int64_t seq_row(const SeqArg& a, int64_t j) {
+// Cache row of position j (device): plain, ring or paged.
+__device__ inline int64_t seq_row(const SeqArg& a, int64_t j) {
+  if (a.btab) {
+    int b = a.btab[j >> a.bshift];
+    b = b < 0 ? 0 : (b >= a.n_blocks ? a.n_blocks - 1 : b);
+    return ((int64_t)b << a.bshift) + (j & ((1 << a.bshift) - 1));
+  }
   return a.ring_cap ? j % a.ring_cap : j;
 }
 

@@ -82,9 +82,16 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     const int T = q.n_new == 0 ? 1 : q.n_new;
     if (T < 1 || T > SD_ATTN_MAX_NEW) return SD_EINVAL;
     if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || (q.ring != 0 && q.ring != 1)) return SD_EINVAL;
-    if (q.ring) {
+    if (q.pos > 0x7fffffff - T) return SD_EINVAL;
+    if (q.block_table) {
+      // paged pool: whole blocks of 64, 128 or 256 rows
+      if (q.ring) return SD_EINVAL;
+      if (q.block_size != 64 && q.block_size != 128 && q.block_size != 256) return SD_EINVAL;
+      if (q.capacity % q.block_size != 0) return SD_EINVAL;
+      if ((uintptr_t)q.block_table % 4) return SD_EALIGN;
+    } else if (q.ring) {
       // a ring keeps the positions still attended to: window + T - 1 of them at most
-      if (m->window < 1 || q.pos > 0x7fffffff - T) return SD_EINVAL;
+      if (m->window < 1) return SD_EINVAL;
       const int64_t span = q.pos + T < (int64_t)m->window + T - 1 ? q.pos + T : (int64_t)m->window + T - 1;
       if (span > q.capacity) return SD_EINVAL;
     } else if (q.pos > q.capacity - T) {
@@ -137,6 +144,11 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     sa.s[s].n_new = T;
     sa.s[s].window = m->window;
     sa.s[s].ring_cap = io->seqs[s].ring ? io->seqs[s].capacity : 0;
+    if (io->seqs[s].block_table) {
+      sa.s[s].btab = io->seqs[s].block_table;
+      sa.s[s].bshift = __builtin_ctz((unsigned)io->seqs[s].block_size);
+      sa.s[s].n_blocks = io->seqs[s].capacity / io->seqs[s].block_size;
+    }
   }
   attn_layout(&sa, Hq, Hkv);
 

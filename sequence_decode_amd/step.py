@@ -107,9 +107,14 @@ class StepRunner:
     """Preallocated inputs/outputs/workspace for repeated sd_decode_step calls.
 
     n_new[s] (default 1) is the number of tokens sequence s brings to each step
-    (a verify step when above 1); token rows are packed by sequence."""
+    (a verify step when above 1); token rows are packed by sequence.
+    block_tables[s] (int32 device tensors, with block_size): the caches are a
+    paged pool (the same SeqCache may serve several sequences) and sequence s
+    keeps position j in row block_tables[s][j // block_size] * block_size
+    + j % block_size of every layer."""
 
-    def __init__(self, model: DecodeModel, caches, max_ctx: int, n_new=None, ring=False):
+    def __init__(self, model: DecodeModel, caches, max_ctx: int, n_new=None, ring=False,
+                 block_tables=None, block_size=0):
         import torch
         self.model = model
         self.caches = list(caches)
@@ -128,10 +133,19 @@ class StepRunner:
         self.next_tokens = torch.empty(rows, dtype=torch.int32, device=dev)
         self.tokens = torch.zeros(rows, dtype=torch.int32, device=dev)
         self.positions = torch.zeros(rows, dtype=torch.int32, device=dev)
+        self.block_tables = None if block_tables is None else list(block_tables)
+        if self.block_tables is not None:
+            if len(self.block_tables) != n:
+                raise ValueError("one block table per sequence")
+            for bt in self.block_tables:
+                if bt.dtype != torch.int32 or not bt.is_cuda or not bt.is_contiguous():
+                    raise TypeError("block tables must be contiguous int32 device tensors")
         self._seqs = (_lib.StepSeq * n)()
         for s, c in enumerate(self.caches):
+            bt = 0 if self.block_tables is None else self.block_tables[s].data_ptr()
             self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0, self.n_new[s],
-                                         1 if ring else 0)
+                                         1 if ring else 0, bt,
+                                         int(block_size) if bt else 0, 0)
         self.io = _lib.StepIO(n, ctypes.cast(self._seqs, ctypes.c_void_p), self.tokens.data_ptr(),
                               self.positions.data_ptr(), self.logits.data_ptr(),
                               self.next_tokens.data_ptr(), self.ws.data_ptr(), need)

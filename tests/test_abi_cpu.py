@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 3
+    assert L.sd_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -141,6 +141,29 @@ def test_window_and_ring_rejections(L):
     assert L.sd_decode_attn_workspace_bytes(huge, 1, 32, 128) == 0
 
 
+def test_paged_rejections(L):
+    a = L.sd_decode_attn_multiseq
+    def view(ctx, cap, bs, table=FAKE, ring=0, window=0):
+        return (_lib.SeqView * 1)(_lib.SeqView(FAKE.value, FAKE.value, ctx, cap, 1024, 128, window,
+                                               ring, table.value, bs, 0))
+    for bs in (64, 128, 256):
+        ok = view(5000, 1024, bs)         # a paged context may exceed the pool (shared blocks)
+        need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
+        assert need == 20 * 32 * 132 * 4
+        assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
+    for bad in (view(100, 1024, 32),      # blocks of 64, 128 or 256 rows only
+                view(100, 1024, 100),
+                view(100, 1024, 0),
+                view(100, 1000, 64),      # the pool holds whole blocks
+                view(100, 1024, 64, ring=1, window=50)):  # not combined with a ring
+        assert a(FAKE, 4096, bad, 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EINVAL
+        assert L.sd_decode_attn_workspace_bytes(bad, 1, 32, 128) == 0
+    assert a(FAKE, 4096, view(100, 1024, 64, table=ODD), 1, 32, 8, 128, 0.088, FAKE, FAKE,
+             1 << 30, None) == SD_EALIGN
+    kv = L.sd_kv_append_f16
+    assert kv(FAKE, FAKE, 1024, view(100, 1000, 64), 1, 8, 128, None) == SD_EINVAL
+
+
 def test_rope_kv_and_glue_rejections(L):
     r = L.sd_rope_posvec
     assert r(FAKE, 4, 32, 128, 4096, 128, FAKE, 1e6, 127, None) == SD_EINVAL
@@ -183,6 +206,15 @@ def test_step_rejections(L):
     seqs[0].n_new = 4
     io.ws_bytes = 16
     assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io), None) == SD_EWORKSPACE
+    paged = (_lib.StepSeq * 1)(_lib.StepSeq(FAKE.value, FAKE.value, 256, 1000, 4, 0, FAKE.value, 64))
+    iop = _lib.StepIO(1, ctypes.cast(paged, ctypes.c_void_p), FAKE.value, FAKE.value, FAKE.value,
+                      FAKE.value, 0x100000, 16)
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(iop), None) == SD_EWORKSPACE  # pos past pool ok
+    for bs, cap, ring, table, rc in ((48, 256, 0, FAKE, SD_EINVAL), (64, 200, 0, FAKE, SD_EINVAL),
+                                     (64, 256, 1, FAKE, SD_EINVAL), (64, 256, 0, ODD, SD_EALIGN)):
+        paged[0].block_size, paged[0].capacity, paged[0].ring = bs, cap, ring
+        paged[0].block_table = table.value
+        assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(iop), None) == rc
     five = (_lib.StepSeq * 5)(*[_lib.StepSeq(FAKE.value, FAKE.value, 64, 3, 4) for _ in range(5)])
     io5 = _lib.StepIO(5, ctypes.cast(five, ctypes.c_void_p), FAKE.value, FAKE.value, FAKE.value,
                       FAKE.value, 0x100000, 1 << 30)

@@ -240,3 +240,50 @@ def test_window_rope_tail_step_vs_oracle_and_ring(sd):
         r_.set_positions([p + 6 for p in pos])
         r_.step()
     assert np.array_equal(bits(host(vp.logits)), bits(host(vr.logits)))
+
+
+def test_paged_pool_step_equals_plain(sd, model):
+    """Three sequences whose caches live in one shared pool of 64-row blocks at
+    shuffled places: one-token steps (crossing a block edge) and a verify step
+    give bitwise the plain-cache logits, and the pool rows the step wrote hold
+    the plain caches' new rows."""
+    import torch
+    say("paged pool step == plain")
+    bs = 64
+    ch = _caches_host(3, seed=3500)
+    nb = CAP // bs
+    n_pool = 3 * nb + 2
+    place = synth.rng(3501).permutation(n_pool)
+    tables = [place[s * nb:(s + 1) * nb].astype(np.int32) for s in range(3)]
+    L_, _, Hkv, Dh = ch[0][0].shape
+    pk = np.zeros((L_, n_pool * bs, Hkv, Dh), np.uint16)
+    pv = np.zeros_like(pk)
+    rows = [tables[s][np.arange(CAP) // bs] * bs + np.arange(CAP) % bs for s in range(3)]
+    for s, (k, v) in enumerate(ch):
+        pk[:, rows[s]], pv[:, rows[s]] = k, v
+    plain = [SeqCache.from_host(*c) for c in ch]
+    pool = SeqCache.from_host(pk, pv)
+    tabs = [dev(t) for t in tables]
+    rp = StepRunner(model, plain, max_ctx=CAP)
+    rq = StepRunner(model, [pool] * 3, max_ctx=CAP, block_tables=tabs, block_size=bs)
+    toks, pos = [5, 17, 901], [62, 200, 250]
+    t = list(toks)
+    for step in range(4):
+        for r_ in (rp, rq):
+            r_.tokens.copy_(torch.tensor(t, dtype=torch.int32))
+            r_.set_positions([p + step for p in pos])
+            r_.step()
+        assert np.array_equal(bits(host(rp.logits)), bits(host(rq.logits))), step
+        t = [int(x) for x in host(rp.next_tokens)]
+    vp = StepRunner(model, plain, max_ctx=CAP, n_new=[3, 1, 2])
+    vq = StepRunner(model, [pool] * 3, max_ctx=CAP, n_new=[3, 1, 2], block_tables=tabs,
+                    block_size=bs)
+    for r_ in (vp, vq):
+        r_.tokens.copy_(torch.tensor([9, 8, 7, 6, 5, 4], dtype=torch.int32))
+        r_.set_positions([p + 4 for p in pos])
+        r_.step()
+    assert np.array_equal(bits(host(vp.logits)), bits(host(vq.logits)))
+    pkh, pvh = host(pool.k), host(pool.v)
+    for s, c in enumerate(plain):
+        kh, vh = host(c.k), host(c.v)
+        assert np.array_equal(pkh[:, rows[s]], kh) and np.array_equal(pvh[:, rows[s]], vh), s

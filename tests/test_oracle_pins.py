@@ -445,6 +445,37 @@ def test_attn_window_and_ring_storage(oracle_mod):
     assert np.array_equal(ring, win)
 
 
+def test_attn_paged_storage(oracle_mod):
+    """A paged pool (blocks of 4 rows placed by a permuted block table, noise in
+    every other row of the pool, one block shared by two sequences) gives the
+    bits of plain storage of the same positions, with and without a window."""
+    L, T, bs, n_pool = 40, 2, 4, 24
+    H_q, H_kv, Dh = 4, 2, 8
+    _, k, v = _attn_case(82, L, H_q, H_kv, Dh)
+    _, k2, v2 = _attn_case(83, L, H_q, H_kv, Dh)
+    k2[:bs], v2[:bs] = k[:bs], v[:bs]  # the two sequences share their first block
+    g = synth.rng(84)
+    q = g.standard_normal((2 * T, H_q, Dh), dtype=np.float32)
+    pk, pv = synth.kv_cache(g, n_pool * bs, H_kv, Dh), synth.kv_cache(g, n_pool * bs, H_kv, Dh)
+    perm = g.permutation(n_pool - 1) + 1  # pool block 0 is the shared one
+    t1 = np.concatenate([[0], perm[:L // bs - 1]]).astype(np.int32)
+    t2 = np.concatenate([[0], perm[L // bs - 1:2 * (L // bs) - 2]]).astype(np.int32)
+    assert len(set(t1[1:]) | set(t2[1:])) == 2 * (L // bs - 1)
+    for tab, kk_, vv_ in ((t1, k, v), (t2, k2, v2)):
+        for j in range(L):
+            r = tab[j // bs] * bs + j % bs
+            pk[r], pv[r] = kk_[j], vv_[j]
+    for W in (0, 11):
+        plain = oracle_mod.attn_verify(q, [(k, v), (k2, v2)], [L, L], [T, T], 0.3, window=W)
+        paged = oracle_mod.attn_verify(q, [(pk, pv), (pk, pv)], [L, L], [T, T], 0.3, window=W,
+                                       tables=[t1, t2], block_size=bs)
+        assert np.array_equal(paged, plain)
+    # the table matters: the identity table reads other rows
+    ident = oracle_mod.attn_verify(q, [(pk, pv), (pk, pv)], [L, L], [T, T], 0.3,
+                                   tables=[np.arange(n_pool, dtype=np.int32)] * 2, block_size=bs)
+    assert not np.array_equal(ident, plain)
+
+
 # ------------------------------------------------------------------ step glue
 
 def test_rmsnorm_decimal_and_closed_form(oracle_mod):

@@ -293,6 +293,26 @@ def decode_bench(torch, steps, warmup):
     res["paged64_ragged_n4"] = {"tok_s": round(4 / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
     log(f"decode paged (64-row blocks) ragged n_seq=4: {4 / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
     del r, pool
+    # q8_0 KV caches (int8 codes, fp16 scale per 32 dims) for the ragged contexts
+    from sequence_decode_amd.step import SeqCacheQ8
+    q8c = [SeqCacheQ8.random_device(g, 32, ctx + span, 8, 128) for ctx in ragged]
+    for n in (1, 4):
+        r = StepRunner(model, q8c[:n], max_ctx=max(ragged[:n]) + span)
+        r.tokens.copy_(torch.arange(n, dtype=torch.int32) + 7)
+        r.set_positions([c - 1 for c in ragged[:n]])
+        for _ in range(warmup):
+            r.step()
+            r.advance()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            r.step()
+            r.advance()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        res[f"q8kv_ragged_n{n}"] = {"tok_s": round(n / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
+        log(f"decode q8_0 KV ragged n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
+    del r, q8c
     # serial baseline: the four ragged sequences one at a time (one-token steps back to back)
     runners = [StepRunner(model, [caches[s]], max_ctx=ragged[s] + span) for s in range(4)]
     for s in range(4):
@@ -311,6 +331,65 @@ def decode_bench(torch, steps, warmup):
     res["serial_ragged_n4"] = {"tok_s": round(4 / dt, 2), "ms_per_round": round(dt * 1e3, 3)}
     log(f"decode serial 4 sequences: {4 / dt:.1f} tok/s")
     out["results"] = res
+    return out
+
+
+def attention_bench(torch, reps=20):
+    """Graph-timed sd_decode_attn_multiseq (chunk + combine kernels) at the decode
+    contexts: fp16 and q8_0 caches, plain and in a paged pool (64-row blocks).
+    GB/s counts the cache bytes the call must read."""
+    import sequence_decode_amd as sd
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    H_q, H_kv, D = 32, 8, 128
+    cases = {"n1_2050": [2050], "n4_2050": [2050] * 4, "n4_ragged": [2050, 3072, 16384, 32768],
+             "n1_32768": [32768]}
+    out = {}
+    for cname, lens in cases.items():
+        for kind in ("f16", "q8_0", "f16_paged64"):
+            keep, sets = [], []
+            for _ in range(4):  # four cache sets, cycled, so no call finds the previous one in L2
+                if kind == "q8_0":
+                    cs = []
+                    for L in lens:
+                        kq = torch.randint(-127, 128, (L, H_kv, D), generator=g, device="cuda",
+                                           dtype=torch.int32).to(torch.int8)
+                        vq = torch.randint(-127, 128, (L, H_kv, D), generator=g, device="cuda",
+                                           dtype=torch.int32).to(torch.int8)
+                        kd = ((torch.rand((L, H_kv, D // 32), generator=g, device="cuda") + 2) / 127).half()
+                        vd = ((torch.rand((L, H_kv, D // 32), generator=g, device="cuda") + 2) / 127).half()
+                        cs.append((kq, kd, vq, vd))
+                    views = [sd.seqview_q8(*c, L) for c, L in zip(cs, lens)]
+                elif kind == "f16":
+                    cs = [(torch.randn((L, H_kv, D), generator=g, device="cuda").half(),
+                           torch.randn((L, H_kv, D), generator=g, device="cuda").half()) for L in lens]
+                    views = [sd.seqview(k, v, L) for (k, v), L in zip(cs, lens)]
+                else:
+                    bs = 64
+                    nb = [(L + bs - 1) // bs for L in lens]
+                    pk = torch.randn((sum(nb) * bs, H_kv, D), generator=g, device="cuda").half()
+                    pv = torch.randn((sum(nb) * bs, H_kv, D), generator=g, device="cuda").half()
+                    place = torch.randperm(sum(nb), generator=g, device="cuda").to(torch.int32)
+                    tabs = [place[sum(nb[:i]):sum(nb[:i + 1])].contiguous() for i in range(len(lens))]
+                    cs = [pk, pv, tabs]
+                    views = [sd.seqview(pk, pv, L, block_table=t, block_size=bs)
+                             for t, L in zip(tabs, lens)]
+                keep.append(cs)
+                sets.append(views)
+            q = torch.randn((len(lens), H_q, D), generator=g, device="cuda")
+            o = torch.empty_like(q)
+            ws = torch.empty(max(16, sd.decode_attn_workspace_bytes(sets[0], H_q, D)),
+                             dtype=torch.uint8, device="cuda")
+            def four():  # one call per cache set, captured in one graph
+                for v in sets:
+                    sd.decode_attn_multiseq(q, v, H_kv, 0.08838835, out=o, ws=ws)
+            us = time_graph(torch, four, reps, 2) * 1e6 / 4
+            per_key = 2176 if kind == "q8_0" else 4096
+            gbs = sum(lens) * per_key / us / 1e3
+            out[f"{cname}_{kind}"] = {"us": round(us, 2), "GB_s": round(gbs, 1)}
+            log(f"attention {cname} {kind}: {us:.2f} us, {gbs:.1f} GB/s of cache bytes")
+            del keep, sets
+            torch.cuda.empty_cache()
     return out
 
 
@@ -385,6 +464,7 @@ def main():
                      "avg_launch_us": round(tms / launches * 1e3, 3), "per_shape": per_shape},
     }
     line["verify_widths"] = verify_widths(torch, sweep, max(3, args.steps // 2))
+    line["attention"] = attention_bench(torch)
     line["decode_step"] = None
     if not args.no_decode:
         line["decode_step"] = decode_bench(torch, steps=max(8, args.steps), warmup=args.warmup)

@@ -47,7 +47,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 4
+#define SD_ABI_VERSION 5
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -151,8 +151,24 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
                    double theta, int n_rot, sd_stream_t stream);
 
 /* --------------------------------------------------- per-sequence KV views
- * One sequence's fp16 key and value caches (bit patterns), element (row r,
- * head g, dim d) at base[r*ld_tok + g*ld_head + d] (elements).  The struct
+ * Cache element types.  SD_KV_F16: fp16 keys and values (bit patterns).
+ * SD_KV_Q8_0: the "int8 KV" / "Q8" caches of "#1209 Speed up concurrent
+ * generation, fix QFUSE, and improve prefill monitoring" ("What changed and
+ * why": resident int8 KV) and "feat(qwen36): complete concurrent serving
+ * implementation with speculation" ("Validation": Q8 attention cases), in
+ * q8_0 blocks: each run of 32 consecutive dims of a (row, head) is 32 int8
+ * codes c with one fp16 scale d, value d * c.  Codes and scales live in two
+ * planes: codes at the element offsets of an fp16 cache, scales at the same
+ * offsets divided by 32.  Quantization of a new row (the append and the step)
+ * takes, per block, d = amax / 127 in fp32, c = clamp(round-half-away(x / d),
+ * -127, 127) (0 when d = 0), and stores fp16(d) rounded to nearest even.
+ */
+#define SD_KV_F16 0
+#define SD_KV_Q8_0 1
+
+/*
+ * One sequence's key and value caches, element (row r, head g, dim d) at
+ * base[r*ld_tok + g*ld_head + d] (elements).  The struct
  * array is [host] memory; kernels receive the views by value in their
  * arguments (ds4 pull request 604, "Commit walkthrough / CUDA kernels", whose
  * sequences each attend to their own KV ring).  ctx_len is one past the
@@ -162,6 +178,10 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
  *   ring    0: position j lives in row j (ctx_len <= capacity);
  *           1: the cache is a ring, position j in row j % capacity (needs
  *           window >= 1 and room for every position still attended to).
+ *   kv_type SD_KV_F16: k and v hold fp16 bits and k_q8 .. v_d are unused;
+ *           SD_KV_Q8_0: k and v are unused, codes in k_q8 / v_q8 (16-byte
+ *           aligned), scales in k_d / v_d (8-byte aligned); D % 32 == 0 and
+ *           ld_tok, ld_head multiples of 32 (of 128 for attention).
  *   block_table  NULL, or a paged cache ("feat(qwen36): complete concurrent
  *           serving implementation with speculation", "Summary": a shared
  *           paged KV pool with per-sequence block tables): k and v are a pool
@@ -188,7 +208,11 @@ typedef struct sd_seqview {
   int32_t ring;
   const int32_t* block_table;
   int32_t block_size;
-  int32_t reserved;
+  int32_t kv_type;      /* SD_KV_F16 (k, v) or SD_KV_Q8_0 (k_q8, v_q8, k_d, v_d) */
+  int8_t* k_q8;         /* q8_0 codes [capacity][H_kv][D] at ld_tok, ld_head (bytes) */
+  int8_t* v_q8;
+  uint16_t* k_d;        /* q8_0 fp16 scales: block b of (r, g) at r*(ld_tok/32) + g*(ld_head/32) + b */
+  uint16_t* v_d;
 } sd_seqview;
 
 /*
@@ -202,11 +226,22 @@ typedef struct sd_seqview {
  *   k_new, v_new  [n_seq][H_kv][D] fp32 at sequence stride ld_new (elements).
  *   views         [host] n_seq views; 4-byte aligned bases, even strides.
  * Requires 1 <= n_seq <= SD_MAX_SEQS, ctx_len >= 1, ctx_len <= capacity
- * for a plain view, D even.
+ * for a plain view, D even, every view SD_KV_F16.
  */
 int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
                      const sd_seqview* views, int n_seq, int H_kv, int D,
                      sd_stream_t stream);
+
+/*
+ * sd_kv_append_q8_0 -- the same append into SD_KV_Q8_0 views: the row of
+ * position ctx_len_s - 1 receives the q8_0 blocks of k_new[s] and v_new[s]
+ * (codes and fp16 scales, quantized as stated above); no other row is touched.
+ * Requires what sd_kv_append_f16 does, with every view SD_KV_Q8_0 and
+ * D % 32 == 0; k_new, v_new finite.
+ */
+int sd_kv_append_q8_0(const float* k_new, const float* v_new, int64_t ld_new,
+                      const sd_seqview* views, int n_seq, int H_kv, int D,
+                      sd_stream_t stream);
 
 /*
  * sd_decode_attn_workspace_bytes -- workspace size sd_decode_attn_multiseq
@@ -235,6 +270,8 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  * chunks are aligned to absolute positions, so a windowed result is the same
  * in a ring as in a plain cache holding the same rows.  A paged view (see
  * sd_seqview) gives the same bits as a plain cache holding the same keys.
+ * SD_KV_Q8_0 views: keys and values are the dequantized d * c (exact in fp32);
+ * all views of one call share one kv_type (else SD_EUNSUPPORTED).
  */
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
                             int n_seq, int H_q, int H_kv, int D, float scale,
@@ -352,7 +389,14 @@ typedef struct sd_step_seq {
                                   are pools [n_layers][capacity][H_kv][D] in blocks of
                                   block_size rows (64, 128 or 256), as in sd_seqview */
   int32_t block_size;
-  int32_t reserved;
+  int32_t kv_type;    /* SD_KV_F16 (k_cache, v_cache) or SD_KV_Q8_0: codes
+                         k_q8 / v_q8 [n_layers][capacity][H_kv][D] int8 and scales
+                         k_d / v_d [n_layers][capacity][H_kv][D/32] fp16; all
+                         sequences of a step share one kv_type */
+  int8_t* k_q8;
+  int8_t* v_q8;
+  uint16_t* k_d;
+  uint16_t* v_d;
 } sd_step_seq;
 
 /* Inputs and outputs of one step.  Token rows are packed by sequence:

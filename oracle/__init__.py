@@ -40,6 +40,8 @@ def lib():
         L.oracle_rope_posvec.argtypes = [P, i32, i32, i32, i64, i64, P, f64, i32]
         L.oracle_attn_decode_one.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32,
                                              f64, P]
+        L.oracle_attn_decode_one_f64.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32,
+                                                 f64, P]
         L.oracle_rmsnorm.argtypes = [P, i64, i32, i64, P, f64, P, i64]
         L.oracle_swiglu.argtypes = [P, P, i64, P]
         _lib = L
@@ -147,6 +149,44 @@ def attn_decode_one(q: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     return out
 
 
+def quantize_kv_q8_0(x: np.ndarray):
+    """q8_0 blocks of cache rows x [..., D] fp32 (the "int8 KV" cache of "#1209
+    Speed up concurrent generation, fix QFUSE, and improve prefill monitoring",
+    "What changed and why"): per run of 32 dims, d = amax / 127 and codes
+    round-half-away(x / d) clamped to +-127, as the activation quantizer; the
+    stored scale is fp16(d), nearest even.  Returns (codes int8 [..., D],
+    scale bits uint16 [..., D/32])."""
+    x = _req(x, np.float32)
+    D = x.shape[-1]
+    flat = x.reshape(-1, D)
+    codes, d = quantize_q8_act(flat)
+    return codes.reshape(x.shape), f32_to_f16_bits(d).reshape(x.shape[:-1] + (D // 32,))
+
+
+def dequant_kv_q8_0(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """The values d * c of q8_0 cache rows, in fp64 (exact)."""
+    codes = np.asarray(codes, np.int8)
+    d = np.asarray(scale_bits, np.uint16).view(np.float16).astype(np.float64)
+    return codes.astype(np.float64) * np.repeat(d, 32, axis=-1)
+
+
+def attn_decode_one_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_len: int,
+                        scale: float) -> np.ndarray:
+    """attn_decode_one over fp64 keys and values [cap][H_kv][D]."""
+    q = _req(q, np.float32)
+    H_q, D = q.shape
+    assert D <= 1024
+    k = _req(k, np.float64)
+    v = _req(v, np.float64)
+    cap, H_kv, Dk = k.shape
+    assert Dk == D and v.shape == k.shape and 1 <= ctx_len <= cap
+    assert H_q % H_kv == 0
+    out = np.empty((H_q, D), np.float32)
+    lib().oracle_attn_decode_one_f64(_ptr(q), _ptr(k), _ptr(v), H_kv * D, D, ctx_len, H_q, H_kv,
+                                     D, float(np.float32(scale)), _ptr(out))
+    return out
+
+
 def attn_decode_multiseq(q: np.ndarray, caches, ctx_lens, scale: float) -> np.ndarray:
     """q [n_seq][H_q][D]; caches = [(k_bits, v_bits)] per sequence."""
     return np.stack([attn_decode_one(q[s], caches[s][0], caches[s][1], ctx_lens[s], scale)
@@ -167,11 +207,19 @@ def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, windo
     through per-sequence block tables ("feat(qwen36): complete concurrent serving
     implementation with speculation", "Summary"), position j stored in row
     tables[s][j // block_size] * block_size + j % block_size.
+    caches[s] = (k_bits, v_bits) of an fp16 cache, or (kq, kd_bits, vq, vd_bits)
+    of a q8_0 cache, attended over its dequantized values.
     q_rows [sum(n_new)][H_q][D] -> same shape."""
     out = []
     r = 0
     for s, T in enumerate(n_new):
-        k_bits, v_bits = caches[s]
+        if len(caches[s]) == 4:
+            kq, kd, vq, vd = caches[s]
+            k_bits, v_bits = dequant_kv_q8_0(kq, kd), dequant_kv_q8_0(vq, vd)
+            one = attn_decode_one_f64
+        else:
+            k_bits, v_bits = caches[s]
+            one = attn_decode_one
         cap = k_bits.shape[0]
         for i in range(T):
             p = ctx_lens[s] - T + i
@@ -182,7 +230,7 @@ def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, windo
             if tables is not None and tables[s] is not None:
                 rows = np.asarray(tables[s], np.int64)[rows // block_size] * block_size \
                     + rows % block_size
-            out.append(attn_decode_one(q_rows[r], k_bits[rows], v_bits[rows], p + 1 - lo, scale))
+            out.append(one(q_rows[r], k_bits[rows], v_bits[rows], p + 1 - lo, scale))
             r += 1
     return np.stack(out)
 

@@ -230,6 +230,44 @@ void oracle_attn_decode_one(const float* q, const uint16_t* k, const uint16_t* v
 }
 
 /*
+ * The same decode attention over keys and values given as fp64 numbers (the
+ * dequantized d * c of a q8_0 cache, "#1209 Speed up concurrent generation,
+ * fix QFUSE, and improve prefill monitoring", "What changed and why": int8
+ * KV), element (j, g, d) at k[j*ld_tok + g*ld_head + d].
+ */
+void oracle_attn_decode_one_f64(const float* q, const double* k, const double* v,
+                                int64_t ld_tok, int64_t ld_head, int ctx_len,
+                                int H_q, int H_kv, int D, double scale, float* out) {
+  int G = H_q / H_kv;
+#pragma omp parallel for schedule(static)
+  for (int h = 0; h < H_q; ++h) {
+    int g = h / G;
+    double zmax = -INFINITY;
+    for (int j = 0; j < ctx_len; ++j) {
+      const double* kj = k + (int64_t)j * ld_tok + (int64_t)g * ld_head;
+      double z = 0.0;
+      for (int d = 0; d < D; ++d) z += (double)q[h * D + d] * kj[d];
+      z *= scale;
+      if (z > zmax) zmax = z;
+    }
+    double denom = 0.0;
+    double acc[1024];
+    for (int d = 0; d < D; ++d) acc[d] = 0.0;
+    for (int j = 0; j < ctx_len; ++j) {
+      const double* kj = k + (int64_t)j * ld_tok + (int64_t)g * ld_head;
+      const double* vj = v + (int64_t)j * ld_tok + (int64_t)g * ld_head;
+      double z = 0.0;
+      for (int d = 0; d < D; ++d) z += (double)q[h * D + d] * kj[d];
+      z *= scale;
+      double p = exp(z - zmax);
+      denom += p;
+      for (int d = 0; d < D; ++d) acc[d] += p * vj[d];
+    }
+    for (int d = 0; d < D; ++d) out[h * D + d] = (float)(acc[d] / denom);
+  }
+}
+
+/*
  * RMS normalization of n_tok rows of length D (fp64, rounded to fp32):
  *   y = x / sqrt(mean(x^2) + eps) * gamma.
  * The step structure (normalize, project, attend, feed-forward, output head)

@@ -43,7 +43,8 @@ def decode_step(m: Model, caches, tokens, pos):
     """One step for n = len(tokens) sequences.
 
     caches[s] = (k_bits, v_bits), each uint16 [n_layers][capacity][H_kv][D],
-    updated in place at row pos[s] of every layer.  Returns (logits [n][vocab]
+    or q8_0 caches (kq, kd_bits, vq, vd_bits) with codes int8 [..][D] and scale
+    bits uint16 [..][D/32]; updated in place at row pos[s] of every layer.  Returns (logits [n][vocab]
     fp32, next tokens int32 [n]).
     """
     tokens = np.asarray(tokens, np.int64)
@@ -62,9 +63,15 @@ def decode_step(m: Model, caches, tokens, pos):
         q = O.rope_posvec(q, pos, m.theta, m.n_rot)
         k = O.rope_posvec(k, pos, m.theta, m.n_rot)
         for s in range(n):
-            caches[s][0][li, pos[s]] = O.f32_to_f16_bits(k[s])
-            caches[s][1][li, pos[s]] = O.f32_to_f16_bits(v[s])
-        o = O.attn_verify(q, [(c[0][li], c[1][li]) for c in caches],
+            if len(caches[s]) == 4:  # q8_0 cache: codes and fp16 scales of the new rows
+                kq, kd = O.quantize_kv_q8_0(k[s])
+                vq, vd = O.quantize_kv_q8_0(v[s])
+                caches[s][0][li, pos[s]], caches[s][1][li, pos[s]] = kq, kd
+                caches[s][2][li, pos[s]], caches[s][3][li, pos[s]] = vq, vd
+            else:
+                caches[s][0][li, pos[s]] = O.f32_to_f16_bits(k[s])
+                caches[s][1][li, pos[s]] = O.f32_to_f16_bits(v[s])
+        o = O.attn_verify(q, [tuple(a[li] for a in c) for c in caches],
                           [int(p) + 1 for p in pos], [1] * n, scale, window=m.window)
         oq, od = O.quantize_q8_act(o.reshape(n, Hq * D))
         h = O.qgemv_q8_0(L["w_o"], H, Hq * D, oq, od, residual=x)

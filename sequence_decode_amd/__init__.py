@@ -23,6 +23,7 @@ MAX_SEQS = 4
 ATTN_CHUNK = 256
 ATTN_MAX_NEW = 4
 GEMV_AUTO, GEMV_NARROW, GEMV_MFMA = 0, 1, 2
+KV_F16, KV_Q8_0 = 0, 1
 
 
 class SdError(RuntimeError):
@@ -126,7 +127,29 @@ def seqview(k, v, ctx_len, window=0, ring=False, block_table=None, block_size=0)
         _need(block_table, torch.int32, "block_table")
         bt = block_table.data_ptr()
     return SeqView(k.data_ptr(), v.data_ptr(), int(ctx_len), int(cap), H_kv * D, D, int(window),
-                   1 if ring else 0, bt, int(block_size), 0)
+                   1 if ring else 0, bt, int(block_size), KV_F16)
+
+
+def seqview_q8(kq, kd, vq, vd, ctx_len, window=0, ring=False, block_table=None, block_size=0):
+    """View of one sequence's q8_0 caches: codes kq, vq [capacity][H_kv][D] int8
+    and fp16 block scales kd, vd [capacity][H_kv][D/32] (or int16 bits); the
+    other arguments as in seqview."""
+    import torch
+    cap, H_kv, D = kq.shape
+    for t, n, dt in ((kq, "kq", torch.int8), (vq, "vq", torch.int8)):
+        _need(t, dt, n)
+    for t, n in ((kd, "kd"), (vd, "vd")):
+        if t.dtype not in (torch.float16, torch.int16):
+            raise TypeError(f"{n} must be float16 (or int16 bits)")
+        if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (cap, H_kv, D // 32):
+            raise TypeError(f"{n} must be a contiguous CUDA tensor of shape {(cap, H_kv, D // 32)}")
+    bt = 0
+    if block_table is not None:
+        _need(block_table, torch.int32, "block_table")
+        bt = block_table.data_ptr()
+    return SeqView(0, 0, int(ctx_len), int(cap), H_kv * D, D, int(window), 1 if ring else 0, bt,
+                   int(block_size), KV_Q8_0, kq.data_ptr(), vq.data_ptr(), kd.data_ptr(),
+                   vd.data_ptr())
 
 
 def _views(views):
@@ -142,6 +165,18 @@ def kv_append_f16(k_new, v_new, views, stream=None):
     n_seq, H_kv, D = k_new.shape
     arr = _views(views)
     _check("sd_kv_append_f16", _lib.load().sd_kv_append_f16(
+        _p(k_new), _p(v_new), H_kv * D, arr, len(views), H_kv, D, _stream(stream)))
+
+
+def kv_append_q8_0(k_new, v_new, views, stream=None):
+    """Writes the q8_0 blocks of k_new[s], v_new[s] into row ctx_len-1 of each
+    q8_0 view."""
+    import torch
+    _need(k_new, torch.float32, "k_new")
+    _need(v_new, torch.float32, "v_new")
+    n_seq, H_kv, D = k_new.shape
+    arr = _views(views)
+    _check("sd_kv_append_q8_0", _lib.load().sd_kv_append_q8_0(
         _p(k_new), _p(v_new), H_kv * D, arr, len(views), H_kv, D, _stream(stream)))
 
 

@@ -17,6 +17,7 @@ SIGNATURES = {
     "sd_qgemv_q8_0_batch_path": ([P, i64, i64, P, P, i32, P, P, i64, i32, P], i32),
     "sd_rope_posvec": ([P, i32, i32, i32, i64, i64, P, f64, i32, P], i32),
     "sd_kv_append_f16": ([P, P, i64, P, i32, i32, i32, P], i32),
+    "sd_kv_append_q8_0": ([P, P, i64, P, i32, i32, i32, P], i32),
     "sd_decode_attn_workspace_bytes": ([P, i32, i32, i32], sz),
     "sd_decode_attn_multiseq": ([P, i64, P, i32, i32, i32, i32, f32, P, P, sz, P], i32),
     "sd_decode_attn_verify_workspace_bytes": ([P, P, i32, i32, i32], sz),
@@ -35,7 +36,8 @@ class SeqView(ctypes.Structure):
     _fields_ = [("k", P), ("v", P), ("ctx_len", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("ld_tok", ctypes.c_int64), ("ld_head", ctypes.c_int64),
                 ("window", ctypes.c_int32), ("ring", ctypes.c_int32),
-                ("block_table", P), ("block_size", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("block_table", P), ("block_size", ctypes.c_int32), ("kv_type", ctypes.c_int32),
+                ("k_q8", P), ("v_q8", P), ("k_d", P), ("v_d", P)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -55,7 +57,8 @@ class Model(ctypes.Structure):
 class StepSeq(ctypes.Structure):
     _fields_ = [("k_cache", P), ("v_cache", P), ("capacity", ctypes.c_int32),
                 ("pos", ctypes.c_int32), ("n_new", ctypes.c_int32), ("ring", ctypes.c_int32),
-                ("block_table", P), ("block_size", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("block_table", P), ("block_size", ctypes.c_int32), ("kv_type", ctypes.c_int32),
+                ("k_q8", P), ("v_q8", P), ("k_d", P), ("v_d", P)]
 
 
 class StepIO(ctypes.Structure):

@@ -37,12 +37,29 @@ int check_gemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const floa
   return SD_OK;
 }
 
+// kv_type: the element type every view must have, or -1 (attention: any, but
+// the same for all views of the call).
 int check_views(const sd_seqview* views, int n_seq, int D, bool attn,
-                const int32_t* n_new = nullptr) {
+                const int32_t* n_new = nullptr, int kv_type = -1) {
   if (!views || n_seq < 1 || n_seq > SD_MAX_SEQS) return SD_EINVAL;
   for (int s = 0; s < n_seq; ++s) {
     const sd_seqview& v = views[s];
-    if (!v.k || !v.v) return SD_EINVAL;
+    if (v.kv_type != SD_KV_F16 && v.kv_type != SD_KV_Q8_0) return SD_EINVAL;
+    if (kv_type >= 0 && v.kv_type != kv_type) return SD_EINVAL;
+    if (v.kv_type != views[0].kv_type) return SD_EUNSUPPORTED;
+    if (v.kv_type == SD_KV_F16) {
+      if (!v.k || !v.v) return SD_EINVAL;
+    } else {
+      // q8_0: codes and scales, whole 32-dim blocks
+      if (!v.k_q8 || !v.v_q8 || !v.k_d || !v.v_d) return SD_EINVAL;
+      if (D % 32 != 0) return SD_EINVAL;
+      const int64_t m = attn ? 128 : 32;
+      if (v.ld_tok % m != 0 || v.ld_head % m != 0) return SD_EALIGN;
+      if (attn && (!aligned(v.k_q8, 16) || !aligned(v.v_q8, 16) || !aligned(v.k_d, 8) ||
+                   !aligned(v.v_d, 8)))
+        return SD_EALIGN;
+      if (!aligned(v.k_d, 2) || !aligned(v.v_d, 2)) return SD_EALIGN;
+    }
     if (v.capacity < 1 || v.ctx_len < 1) return SD_EINVAL;
     if (v.window < 0 || (v.ring != 0 && v.ring != 1)) return SD_EINVAL;
     const int T = n_new ? n_new[s] : 1;
@@ -67,10 +84,12 @@ int check_views(const sd_seqview* views, int n_seq, int D, bool attn,
         return SD_EUNSUPPORTED;
     }
     if (v.ld_head < D || v.ld_tok < D) return SD_EINVAL;
-    const size_t al = attn ? 16 : 4;
-    if (!aligned(v.k, al) || !aligned(v.v, al)) return SD_EALIGN;
-    if (attn && (v.ld_tok % 8 != 0 || v.ld_head % 8 != 0)) return SD_EALIGN;
-    if (!attn && (v.ld_tok % 2 != 0 || v.ld_head % 2 != 0)) return SD_EALIGN;
+    if (v.kv_type == SD_KV_F16) {
+      const size_t al = attn ? 16 : 4;
+      if (!aligned(v.k, al) || !aligned(v.v, al)) return SD_EALIGN;
+      if (attn && (v.ld_tok % 8 != 0 || v.ld_head % 8 != 0)) return SD_EALIGN;
+      if (!attn && (v.ld_tok % 2 != 0 || v.ld_head % 2 != 0)) return SD_EALIGN;
+    }
   }
   return SD_OK;
 }
@@ -90,6 +109,13 @@ void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a, const int32_t*
     x.n_new = n_new ? n_new[s] : 1;
     x.window = views[s].window;
     x.ring_cap = views[s].ring ? views[s].capacity : 0;
+    if (views[s].kv_type == SD_KV_Q8_0) {
+      x.q8 = 1;
+      x.kq = views[s].k_q8;
+      x.vq = views[s].v_q8;
+      x.kd = views[s].k_d;
+      x.vd = views[s].v_d;
+    }
     if (views[s].block_table) {
       x.btab = views[s].block_table;
       x.bshift = __builtin_ctz((unsigned)views[s].block_size);
@@ -174,11 +200,23 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_to
                                      n_rot, hs(stream)));
 }
 
+int sd_kv_append_q8_0(const float* k_new, const float* v_new, int64_t ld_new,
+                      const sd_seqview* views, int n_seq, int H_kv, int D, sd_stream_t stream) {
+  if (!k_new || !v_new || H_kv < 1 || D < 32 || D > 4096 || D % 32 != 0) return SD_EINVAL;
+  if (ld_new < (int64_t)H_kv * D) return SD_EINVAL;
+  int rc = check_views(views, n_seq, D, false, nullptr, SD_KV_Q8_0);
+  if (rc != SD_OK) return rc;
+  if (!aligned(k_new, 4) || !aligned(v_new, 4)) return SD_EALIGN;
+  SeqArgs a;
+  fill_seqargs(views, n_seq, &a);
+  return from_hip(launch_kv_append(k_new, v_new, ld_new, a, H_kv, D, hs(stream)));
+}
+
 int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
                      const sd_seqview* views, int n_seq, int H_kv, int D, sd_stream_t stream) {
   if (!k_new || !v_new || H_kv < 1 || D < 2 || D > 4096 || D % 2 != 0) return SD_EINVAL;
   if (ld_new < (int64_t)H_kv * D) return SD_EINVAL;
-  int rc = check_views(views, n_seq, D, false);
+  int rc = check_views(views, n_seq, D, false, nullptr, SD_KV_F16);
   if (rc != SD_OK) return rc;
   if (!aligned(k_new, 4) || !aligned(v_new, 4)) return SD_EALIGN;
   SeqArgs a;

@@ -69,9 +69,17 @@ __device__ __forceinline__ float cross_row_max(float v) {
 }
 
 // fp32 x as the fp16 pair (hi, lo) with hi + lo = x to about 2^-22 |x|.
+// (x - hi is exact in fp32, so the fused form rounds it only once, to fp16.)
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = (_Float16)x;
-  lo = (_Float16)fsub(x, (float)hi);
+  lo = (_Float16)__builtin_fmaf(-1.0f, (float)hi, x);
+}
+
+// exp(x) for x <= 0 as 2^(x log2 e) on the hardware exp2 (about 1e-6 relative
+// over the weights that matter; weights below 2^-126 flush to 0).  One fixed
+// instruction sequence, so a weight's bits depend on x alone.
+__device__ __forceinline__ float exp_w(float x) {
+  return __builtin_amdgcn_exp2f(fmul(x, 1.44269504088896341f));
 }
 
 // Byte layout of one wave's V rows in LDS: row r (64 keys, 256 B each) keeps
@@ -83,6 +91,31 @@ constexpr int kRowBytes = HD * 2;
 constexpr int kWaveKeys = 64;
 constexpr int kWaveVBytes = kWaveKeys * kRowBytes;
 __device__ __forceinline__ int vswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
+// q8_0 caches: a wave's 64 code rows (128 bytes each) sit in LDS with their
+// eight 16-byte segments at positions seg ^ vswz8(r); the transposed byte reads
+// below then touch 16 distinct rows per half-wave at distinct bank offsets.
+constexpr int kRowBytes8 = HD;
+constexpr int kWaveVBytes8 = kWaveKeys * kRowBytes8;
+__device__ __forceinline__ int vswz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x2* lds_i32x2_ptr;
+
+// Eight int8 codes (bytes of w0, then w1) as eight exact fp16 values: byte c
+// becomes the fp16 with bits 0x6400 | (c ^ 0x80), i.e. 1152 + c, minus 1152.
+__device__ __forceinline__ h8 codes_to_h8(uint32_t w0, uint32_t w1) {
+  const uint32_t a0 = w0 ^ 0x80808080u, a1 = w1 ^ 0x80808080u;
+  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const h2 e0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, a0, 0x04010400u)) - bias;
+  const h2 e1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, a0, 0x04030402u)) - bias;
+  const h2 e2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, a1, 0x04010400u)) - bias;
+  const h2 e3 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, a1, 0x04030402u)) - bias;
+  return h8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+}
 
 // One workgroup = (sequence, KV head g, chunk of C keys); wave w owns keys
 // 64w .. 64w+63 of the chunk.  Both contractions run on v_mfma_f32_16x16x32_f16
@@ -96,13 +129,23 @@ __device__ __forceinline__ int vswz(int r) { return (r & 3) | ((r >> 1) & 4); }
 //  * weighted values O^T = V^T P^T: A = 16 dims x 32 keys of V^T, read from the
 //    LDS copy of the wave's V rows with ds_read_b64_tr_b16 (each 16-lane group
 //    gathers 4 keys x 4 dims per read), B = the weights as fp16 hi + lo.
+// q8_0 caches (Q8): the codes enter the same MFMAs as exact fp16 values.  One
+// MFMA's 32 dims are one q8_0 block, so each block's partial score is its own
+// accumulation, scaled by the key's block scale and added in block order.  The
+// value scales fold into the weights: the B operand of dim tile dt is the
+// fp32 product p_j * d_j[dt/2] as fp16 hi + lo.  V^T comes from the codes in
+// LDS by ds_read_b64_tr_b8 (each 16-lane group gathers 8 keys x 16 dims).
 // The four wave partials are added in wave order.  Keys past the end of the
-// sequence get weight 0; their V rows are clamped to the last key, so every
-// product that enters a sum is finite.
+// sequence get weight 0; their V rows (and scales) are clamped to the last key,
+// so every product that enters a sum is finite.
+template <bool Q8>
 __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q, int64_t ld_q,
                                                     SeqArgs seqs, int H_q, float scale,
                                                     float* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v[4 * kWaveVBytes];  // V rows, then O partials
+  constexpr int kVB = Q8 ? kWaveVBytes8 : kWaveVBytes;  // LDS bytes of a wave's V rows (then O partial)
+  static_assert(16 * HD * 4 <= kVB, "a wave's O partial fits its V region");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v[4 * kVB];  // V rows, then O partials
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[Q8 ? 4 * 64 * 4 : 1];  // per wave and key: K, V scales
   __shared__ float s_m[4][16], s_l[4][16];  // per wave and MFMA column (token, head)
 
   const int s = find_seq(seqs, blockIdx.x);
@@ -140,10 +183,6 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 
   // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
   const int jk = wk + 8 * (col >> 2) + (col & 3);
-  const uint16_t* kb = A.k + (int64_t)g * A.ld_head + 8 * kg;
-  // plain caches: row = position, so tile t's rows are a fixed stride apart.
-  // Keys outside jlo .. nk-1 read the nearest key in use: their scores are
-  // replaced by -inf below, so what they load does not matter (it is finite).
   const bool lin = A.ring_cap == 0;
   // plain and paged caches: the wave's 64 positions j0 + wk + x are the 64
   // consecutive rows jrow + wk + x (a block holds a multiple of 64 positions and
@@ -155,50 +194,100 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     jlast = seq_row(A, j0 + nk - 1);
     jrow = wv * kWaveKeys < nk ? seq_row(A, j0 + wv * kWaveKeys) - wv * kWaveKeys : jlast;
   }
-  u32x4a ka[4][4];
-  if (__builtin_expect(lin, 1)) {
-    // plain / paged cache: tile t's rows a fixed stride apart; keys past the end
-    // load zeros, keys below a window are real rows (masked below)
-    const uint16_t* kr = kb + (jrow + jk) * A.ld_tok;
+  // cache row of chunk key jl, clamped into the keys in use (V rows, scales)
+  auto vrow = [&](int jl) -> int64_t {
+    if (__builtin_expect(lin, 1)) return jl < nk ? jrow + jl : jlast;
+    return krow((j0 + jlo) % A.ring_cap, min(max(jl, jlo), nk - 1));
+  };
+  uint8_t* vw = s_v + wave * kVB;
+  if constexpr (Q8) {
+    // ---- V code rows of this wave -> LDS by DMA, issued first (the scores
+    // wait for every load of the wave): instruction i fills rows
+    // 8i .. 8i+7; lane l writes row 8i + l/8 at 16-byte position l%8, which
+    // holds the row's segment (l%8) ^ vswz8(row)
+    const int8_t* vbase = A.vq + (int64_t)g * A.ld_head;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int dj = 32 * (t >> 1) + 4 * (t & 1);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int seg = (lane & 7) ^ vswz8(r);
+      const int8_t* row = vbase + vrow(wk + r) * A.ld_tok;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * seg), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+    }
+  }
+  u32x4a ka[4][4];   // fp16 caches: 8 dims per (tile, block)
+  u32x2a kc[4][4];   // q8_0 caches: 8 codes per (tile, block)
+  if constexpr (!Q8) {
+    const uint16_t* kb = A.k + (int64_t)g * A.ld_head + 8 * kg;
+    if (__builtin_expect(lin, 1)) {
+      // plain / paged cache: keys past the end read the last key, keys below a
+      // window are real rows (both masked below)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        ka[t][kk] = u32x4a{0u, 0u, 0u, 0u};
-        if (jk + dj < nk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + dj * A.ld_tok + 32 * kk);
+      for (int t = 0; t < 4; ++t) {
+        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+        const uint16_t* kr = kb + (jl < nk ? jrow + jl : jlast) * A.ld_tok;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+      }
+    } else {
+      // ring: keys outside jlo .. nk-1 read the nearest key in use (their scores
+      // are replaced by -inf below)
+      const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+        const uint16_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
       }
     }
   } else {
-    // ring: keys outside jlo .. nk-1 read the nearest key in use (their scores
-    // are replaced by -inf below)
-    const int prow0 = (j0 + jlo) % A.ring_cap;
+    const int8_t* kb = A.kq + (int64_t)g * A.ld_head + 8 * kg;
+    if (__builtin_expect(lin, 1)) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
-      const uint16_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+      for (int t = 0; t < 4; ++t) {
+        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+        const int8_t* kr = kb + (jl < nk ? jrow + jl : jlast) * A.ld_tok;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) kc[t][kk] = *reinterpret_cast<const u32x2a*>(kr + 32 * kk);
+      }
+    } else {
+      const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+        const int8_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kc[t][kk] = *reinterpret_cast<const u32x2a*>(kr + 32 * kk);
+      }
     }
+  }
+  // ---- q8_0 scales: lane (col, kg) fetches the K and V scales of key
+  // 8kg + col%8 + 32(col/8) of the wave (the 16 lanes of a group cover the 16
+  // keys whose scores and weights the group holds); they go to LDS below
+  u32x2a ksc = {0u, 0u}, vsc = {0u, 0u};
+  if constexpr (Q8) {
+    const int kw = 8 * kg + (col & 7) + 32 * (col >> 3);
+    const int64_t so = vrow(wk + kw) * (A.ld_tok >> 5) + (int64_t)g * (A.ld_head >> 5);
+    ksc = *reinterpret_cast<const u32x2a*>(A.kd + so);
+    vsc = *reinterpret_cast<const u32x2a*>(A.vd + so);
   }
   // ---- q (score B operands): column col = (token tk, head g*4 + hh), dims 32kk + 8kg ..
+  // (a column past the sequence's tokens reads its last token: all its keys are
+  // masked and its partial is not stored)
   f32x4 qv[4][2];
+  {
+    const f32x4* qp = reinterpret_cast<const f32x4*>(
+        q + (int64_t)(A.row0 + min(tk, T - 1)) * ld_q + (int64_t)(g * kAttnGroup + hh) * HD + 8 * kg);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    qv[kk][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    qv[kk][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (colv) {
-      const f32x4* qp = reinterpret_cast<const f32x4*>(
-          q + (int64_t)(A.row0 + tk) * ld_q + (int64_t)(g * kAttnGroup + hh) * HD + 32 * kk + 8 * kg);
-      qv[kk][0] = qp[0];
-      qv[kk][1] = qp[1];
+    for (int kk = 0; kk < 4; ++kk) {
+      qv[kk][0] = qp[8 * kk];
+      qv[kk][1] = qp[8 * kk + 1];
     }
   }
-  // ---- V rows of this wave -> LDS by DMA: instruction i fills rows 4i .. 4i+3;
-  // lane l writes row 4i + l/16 at 16-byte position l%16, which holds the row's
-  // 16-byte piece (l%16) ^ 2 vswz(row).
-  uint8_t* vw = s_v + wave * kWaveVBytes;
-  {
+  if constexpr (!Q8) {
+    // ---- V rows of this wave -> LDS by DMA: instruction i fills rows 4i .. 4i+3;
+    // lane l writes row 4i + l/16 at 16-byte position l%16, which holds the row's
+    // 16-byte piece (l%16) ^ 2 vswz(row).
     // keys past the end read the last key, and in a ring keys below jlo read
     // key jlo (their weight is 0); a plain cache's keys below a window are
     // real rows and read as they are
@@ -227,6 +316,17 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       }
     }
   }
+  if constexpr (Q8) {
+    // every load is in flight before the first use of a loaded value: the pins
+    // keep the compiler from moving arithmetic (and its waits) between the issues
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qv[kk][0]), "+v"(qv[kk][1]));
+    // the scales, 16 bytes per key (K then V), in the wave's own region; only
+    // this wave reads them back, after its own write
+    uint32_t* sw = s_sc + wave * 256;
+    const int kw = 8 * kg + (col & 7) + 32 * (col >> 3);
+    *reinterpret_cast<u32x4a*>(sw + 4 * kw) = u32x4a{ksc.x, ksc.y, vsc.x, vsc.y};
+  }
 
   // ---- scores
   h8 bhi[4], blo[4];
@@ -246,11 +346,34 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const h8 av = __builtin_bit_cast(h8, ka[t][kk]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], acc, 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const h8 av = __builtin_bit_cast(h8, ka[t][kk]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], acc, 0, 0, 0);
+      }
+    } else {
+      // block kk's partial score, times the key's block-kk scale, in block order
+      const uint32_t* sw = s_sc + wave * 256;
+      f32x4v dk[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const h8 av = codes_to_h8(kc[t][kk].x, kc[t][kk].y);
+        dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], dk[kk], 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kw = 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
+        // (the four fp16 scales as one h4: taking halves of the two dwords
+        // separately made this compiler fold both dwords into the first)
+        const h4 sk = __builtin_bit_cast(h4, *reinterpret_cast<const u32x2a*>(sw + 4 * kw));
+        float a = __builtin_fmaf(dk[0][r], (float)sk[0], 0.0f);
+        a = __builtin_fmaf(dk[1][r], (float)sk[1], a);
+        a = __builtin_fmaf(dk[2][r], (float)sk[2], a);
+        acc[r] = __builtin_fmaf(dk[3][r], (float)sk[3], a);
+      }
     }
     // D slot r of this lane = row 4kg + r = key wk + 32(t/2) + 8kg + 4(t%2) + r, head col
 #pragma unroll
@@ -273,42 +396,119 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const float M = fmaxf(fmaxf(s_m[0][col], s_m[1][col]), fmaxf(s_m[2][col], s_m[3][col]));
   // ---- weights, their sum, and the P^T operands (block b: slot j = tile 2b + j/4, slot j%4)
   h8 phi[2], plo[2];
+  float pw[4][4];
   float lw = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pz = z[t][r] == -INFINITY ? 0.0f : expf(fsub(z[t][r], M));
+      const float pz = z[t][r] == -INFINITY ? 0.0f : exp_w(fsub(z[t][r], M));
       lw = fadd(lw, pz);
-      _Float16 hi, lo;
-      split_f16(pz, hi, lo);
-      phi[t >> 1][4 * (t & 1) + r] = hi;
-      plo[t >> 1][4 * (t & 1) + r] = lo;
+      pw[t][r] = pz;
+      if constexpr (!Q8) {
+        _Float16 hi, lo;
+        split_f16(pz, hi, lo);
+        phi[t >> 1][4 * (t & 1) + r] = hi;
+        plo[t >> 1][4 * (t & 1) + r] = lo;
+      }
     }
   lw = cross_row_sum_fixed(lw);
   if (lane < 16) s_l[wave][lane] = lw;
 
   // ---- weighted values: this wave's V rows have landed in LDS
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // lane (col, kg) reads row 32b + 8kg + 4h + col/4, dims 16dt + 4(col%4) .. +3
-  const int vg = vswz(8 * kg + (col >> 2));
-  const int rbase = (8 * kg + (col >> 2)) * kRowBytes + 8 * (col & 3);
   f32x4v o[8];
+  if constexpr (!Q8) {
+    // lane (col, kg) reads row 32b + 8kg + 4h + col/4, dims 16dt + 4(col%4) .. +3
+    const int vg = vswz(8 * kg + (col >> 2));
+    const int rbase = (8 * kg + (col >> 2)) * kRowBytes + 8 * (col & 3);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-    const int a0 = rbase + ((dt ^ vg) << 5);
+    for (int dt = 0; dt < 8; ++dt) {
+      o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+      const int a0 = rbase + ((dt ^ vg) << 5);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes));
+        const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes + 4 * kRowBytes));
+        const h8 av = __builtin_bit_cast(h8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[b], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);
+      }
+    }
+  } else {
+    // lane (col, kg) of step b reads code row 32b + 8kg + col/2, bytes 16dt +
+    // 8(col%2) .. +7: the transposed read hands lane (m, kg) the codes of keys
+    // 32b + 8kg + 0..7 at dim 16dt + m
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t* sw = s_sc + wave * 256;
+    const int sg = (col >> 1) ^ (kg & 1);  // vswz8 of the rows this lane reads
+    u32x2a sv[2][8];  // V scales of keys 32b + 8kg + j
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[b][j] = *reinterpret_cast<const u32x2a*>(sw + 4 * (32 * b + 8 * kg + j) + 2);
+    // The weights p * d are about d times smaller than p, so their fp16 hi + lo
+    // pair would lose bits to fp16's subnormal range.  Each column scales them
+    // by 2^k, k = 29 - (fp16 exponent of the largest |d| among the keys it
+    // weights in this wave), so p * d * 2^k < 2^15, and scales its partial back
+    // by 2^-k (both exact).  k depends only on keys the column attends to.
+    float up, down;
+    {
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      u16x2 mb = {0, 0};
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u16x2 x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, sv[b][j].x & 0x7fff7fffu),
+                                                    __builtin_bit_cast(u16x2, sv[b][j].y & 0x7fff7fffu));
+          if (pw[2 * b + (j >> 2)][j & 3] > 0.0f) mb = __builtin_elementwise_max(mb, x);
+        }
+      const float mf = cross_row_max((float)(mb.x > mb.y ? mb.x : mb.y));
+      const int kx = 29 - ((int)mf >> 10);
+      up = __builtin_bit_cast(float, (uint32_t)(kx + 127) << 23);
+      down = __builtin_bit_cast(float, (uint32_t)(127 - kx) << 23);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[t][r] = fmul(pw[t][r], up);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes));
-      const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes + 4 * kRowBytes));
-      const h8 av = __builtin_bit_cast(h8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[b], o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);
+      const int rb = (32 * b + 8 * kg + (col >> 1)) * kRowBytes8 + 8 * (col & 1);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        h8 whi, wlo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const h4 sp = __builtin_bit_cast(h4, sv[b][j]);
+          const float w = __builtin_fmaf(pw[2 * b + (j >> 2)][j & 3], (float)sp[bb], 0.0f);
+          _Float16 hi, lo;
+          split_f16(w, hi, lo);
+          whi[j] = hi;
+          wlo[j] = lo;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int dt = 2 * bb + e;
+          const i32x2 cv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2_ptr)((__attribute__((address_space(3))) uint8_t*)vw + rb + 16 * (dt ^ sg)));
+          const h8 av = codes_to_h8((uint32_t)cv.x, (uint32_t)cv.y);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, whi, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wlo, o[dt], 0, 0, 0);
+        }
+      }
     }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[dt][r] = fmul(o[dt][r], down);
   }
+  // every lane of the wave is done reading the wave's V region before it takes
+  // the partial (LDS reads of one wave complete in order)
   // D slot r of lane (col, kg) = dim 16dt + 4kg + r of column col; the wave's
   // own V region (now read) takes its partial O[column][dim]
   float* so = reinterpret_cast<float*>(vw);
@@ -331,7 +531,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     float O = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      O = fadd(O, reinterpret_cast<const float*>(s_v + w * kWaveVBytes)[idx]);
+      O = fadd(O, reinterpret_cast<const float*>(s_v + w * kVB)[idx]);
       L = fadd(L, s_l[w][cc]);
     }
     const float Mh = fmaxf(fmaxf(s_m[0][cc], s_m[1][cc]), fmaxf(s_m[2][cc], s_m[3][cc]));
@@ -452,7 +652,12 @@ hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_
                        hipStream_t st) {
   int units = 0;
   for (int s = 0; s < seqs.n_seq; ++s) units += seqs.s[s].n_chunks * H_kv;
-  hipLaunchKernelGGL(k_attn_chunk, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale, partials);
+  if (seqs.s[0].q8)
+    hipLaunchKernelGGL(k_attn_chunk<true>, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale,
+                       partials);
+  else
+    hipLaunchKernelGGL(k_attn_chunk<false>, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale,
+                       partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int rows = 0;

@@ -45,6 +45,11 @@ struct SeqArg {
   const int32_t* btab;    // paged cache: block table (device), else null
   int32_t bshift;         // log2 of the block size (paged)
   int32_t n_blocks;       // blocks in the pool (paged)
+  int32_t q8;             // 1: q8_0 caches (codes kq / vq, fp16 scales kd / vd at offsets / 32)
+  int8_t* kq;
+  int8_t* vq;
+  uint16_t* kd;
+  uint16_t* vd;
 };
 
 // Cache row of position j (device): plain, ring or paged.

@@ -71,6 +71,34 @@ __global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ k_n
   }
 }
 
+// q8_0 block of 32 consecutive values held by 32 consecutive lanes: lane d
+// stores its code, and the block's first lane stores fp16(d) (nearest even).
+// The scale d = amax / 127 and the codes follow the library's q8 convention.
+__device__ __forceinline__ void put_q8_0(float x, int d, int8_t* codes, uint16_t* scales) {
+  const float amax = group_max<32>(fabsf(x));
+  const float dd = q8_scale(amax);
+  codes[d] = (int8_t)q8_code(x, dd);
+  if ((d & 31) == 0) scales[d >> 5] = f32_to_f16_bits(dd);
+}
+
+// Grid (n_seq, H_kv), 128 threads; D % 32 == 0, so every block of 32 dims is
+// one aligned group of 32 lanes.
+__global__ __launch_bounds__(128) void k_kv_append_q8(const float* __restrict__ k_new,
+                                                      const float* __restrict__ v_new,
+                                                      int64_t ld_new, SeqArgs seqs, int H_kv, int D) {
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const SeqArg& a = seqs.s[s];
+  const int64_t r = seq_row(a, a.ctx_len - 1);
+  const int64_t row = r * a.ld_tok + (int64_t)g * a.ld_head;
+  const int64_t srow = r * (a.ld_tok >> 5) + (int64_t)g * (a.ld_head >> 5);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const int64_t src = (int64_t)s * ld_new + (int64_t)g * D + d;
+    put_q8_0(k_new[src], d, a.kq + row, a.kd + srow);
+    put_q8_0(v_new[src], d, a.vq + row, a.vd + srow);
+  }
+}
+
 // Fused step helper.  Workgroup (t, h) for h < n_heads rotates query head h of
 // token row t in place; for n_heads <= h < n_heads + n_kv it rotates key head
 // g = h - n_heads and writes it, with value head g, into the cache row of the
@@ -104,7 +132,27 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
     for (int i = 1; i < SD_MAX_SEQS; ++i)
       if (i < seqs.n_seq && t >= seqs.s[i].row0) sq = i;
     const SeqArg& a = seqs.s[sq];
-    const int64_t dst = seq_row(a, a.ctx_len - a.n_new + (t - a.row0)) * a.ld_tok + (int64_t)g * a.ld_head;
+    const int64_t crow = seq_row(a, a.ctx_len - a.n_new + (t - a.row0));
+    const int64_t dst = crow * a.ld_tok + (int64_t)g * a.ld_head;
+    if (a.q8) {
+      // rotated key head staged in LDS, then both heads quantized by 32-lane blocks
+      __shared__ float s_k[kAttnHeadDim];
+      for (int i = threadIdx.x; i < half; i += blockDim.x) {
+        float c, s, y0, y1;
+        rope_angle(p, i, n_rot, theta, &c, &s);
+        rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
+        s_k[off + i] = y0;
+        s_k[off + i + half] = y1;
+      }
+      for (int d = threadIdx.x; d < off; d += blockDim.x) s_k[d] = kh[d];
+      __syncthreads();
+      const int64_t sdst = crow * (a.ld_tok >> 5) + (int64_t)g * (a.ld_head >> 5);
+      for (int d = threadIdx.x; d < head_dim; d += blockDim.x) {
+        put_q8_0(s_k[d], d, a.kq + dst, a.kd + sdst);
+        put_q8_0(vh[d], d, a.vq + dst, a.vd + sdst);
+      }
+      return;
+    }
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
       rope_angle(p, i, n_rot, theta, &c, &s);
@@ -130,8 +178,12 @@ hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, in
 
 hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_new,
                             const SeqArgs& seqs, int H_kv, int D, hipStream_t st) {
-  hipLaunchKernelGGL(k_kv_append, dim3(seqs.n_seq, H_kv), dim3(128), 0, st, k_new, v_new, ld_new,
-                     seqs, H_kv, D);
+  if (seqs.s[0].q8)
+    hipLaunchKernelGGL(k_kv_append_q8, dim3(seqs.n_seq, H_kv), dim3(128), 0, st, k_new, v_new,
+                       ld_new, seqs, H_kv, D);
+  else
+    hipLaunchKernelGGL(k_kv_append, dim3(seqs.n_seq, H_kv), dim3(128), 0, st, k_new, v_new, ld_new,
+                       seqs, H_kv, D);
   return hipGetLastError();
 }
 

@@ -81,7 +81,18 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     const sd_step_seq& q = io->seqs[s];
     const int T = q.n_new == 0 ? 1 : q.n_new;
     if (T < 1 || T > SD_ATTN_MAX_NEW) return SD_EINVAL;
-    if (!q.k_cache || !q.v_cache || q.capacity < 1 || q.pos < 0 || (q.ring != 0 && q.ring != 1)) return SD_EINVAL;
+    if (q.capacity < 1 || q.pos < 0 || (q.ring != 0 && q.ring != 1)) return SD_EINVAL;
+    if (q.kv_type != SD_KV_F16 && q.kv_type != SD_KV_Q8_0) return SD_EINVAL;
+    if (q.kv_type != io->seqs[0].kv_type) return SD_EUNSUPPORTED;
+    if (q.kv_type == SD_KV_F16) {
+      if (!q.k_cache || !q.v_cache) return SD_EINVAL;
+      if (((uintptr_t)q.k_cache % 16) || ((uintptr_t)q.v_cache % 16)) return SD_EALIGN;
+    } else {
+      if (!q.k_q8 || !q.v_q8 || !q.k_d || !q.v_d) return SD_EINVAL;
+      if (((uintptr_t)q.k_q8 % 16) || ((uintptr_t)q.v_q8 % 16) || ((uintptr_t)q.k_d % 8) ||
+          ((uintptr_t)q.v_d % 8))
+        return SD_EALIGN;
+    }
     if (q.pos > 0x7fffffff - T) return SD_EINVAL;
     if (q.block_table) {
       // paged pool: whole blocks of 64, 128 or 256 rows
@@ -102,7 +113,6 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
       if ((q.pos + T - 1) / SD_ATTN_CHUNK - lo0 / SD_ATTN_CHUNK + 1 > SD_MAX_CTX / SD_ATTN_CHUNK)
         return SD_EUNSUPPORTED;
     }
-    if (((uintptr_t)q.k_cache % 16) || ((uintptr_t)q.v_cache % 16)) return SD_EALIGN;
     {
       // attention chunks of this sequence are at most those of max_ctx keys
       const int lo0 = m->window ? (q.pos - m->window + 1 > 0 ? q.pos - m->window + 1 : 0) : 0;
@@ -144,6 +154,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     sa.s[s].n_new = T;
     sa.s[s].window = m->window;
     sa.s[s].ring_cap = io->seqs[s].ring ? io->seqs[s].capacity : 0;
+    sa.s[s].q8 = io->seqs[s].kv_type == SD_KV_Q8_0;
     if (io->seqs[s].block_table) {
       sa.s[s].btab = io->seqs[s].block_table;
       sa.s[s].bshift = __builtin_ctz((unsigned)io->seqs[s].block_size);
@@ -161,11 +172,19 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   for (int l = 0; l < m->n_layers; ++l) {
     const sd_layer_weights& L = m->layers[l];
     for (int s = 0; s < n_seq; ++s) {
-      const int64_t off = (int64_t)l * io->seqs[s].capacity * layer_elems_per_tok;
-      sa.s[s].k = io->seqs[s].k_cache + off;
-      sa.s[s].v = io->seqs[s].v_cache + off;
-      sa.s[s].k_w = io->seqs[s].k_cache + off;
-      sa.s[s].v_w = io->seqs[s].v_cache + off;
+      const sd_step_seq& q = io->seqs[s];
+      const int64_t off = (int64_t)l * q.capacity * layer_elems_per_tok;
+      if (sa.s[s].q8) {
+        sa.s[s].kq = q.k_q8 + off;
+        sa.s[s].vq = q.v_q8 + off;
+        sa.s[s].kd = q.k_d + off / 32;
+        sa.s[s].vd = q.v_d + off / 32;
+      } else {
+        sa.s[s].k = q.k_cache + off;
+        sa.s[s].v = q.v_cache + off;
+        sa.s[s].k_w = q.k_cache + off;
+        sa.s[s].v_w = q.v_cache + off;
+      }
     }
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
     SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));

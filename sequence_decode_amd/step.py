@@ -103,6 +103,34 @@ class SeqCache:
                    synth.torch_normal_f16(gen, (n_layers, capacity, H_kv, D), device))
 
 
+class SeqCacheQ8:
+    """One sequence's q8_0 caches: codes kq, vq int8 [n_layers][capacity][H_kv][D]
+    and fp16 block scales kd, vd [n_layers][capacity][H_kv][D/32]."""
+
+    def __init__(self, kq, kd, vq, vd):
+        self.kq, self.kd, self.vq, self.vd = kq, kd, vq, vd
+        self.capacity = kq.shape[1]
+
+    @classmethod
+    def from_host(cls, kq, kd_bits, vq, vd_bits, device="cuda"):
+        import torch
+        t = lambda a: torch.from_numpy(a).to(device)
+        f = lambda a: torch.from_numpy(a).view(torch.float16).to(device)
+        return cls(t(kq), f(kd_bits), t(vq), f(vd_bits))
+
+    @classmethod
+    def random_device(cls, gen, n_layers, capacity, H_kv, D, device="cuda"):
+        """Codes uniform in [-127, 127], scales those of N(0,1) blocks (about 2.5/127)."""
+        import torch
+        def codes():
+            return torch.randint(-127, 128, (n_layers, capacity, H_kv, D), generator=gen,
+                                 device=device, dtype=torch.int32).to(torch.int8)
+        def scales():
+            u = torch.rand((n_layers, capacity, H_kv, D // 32), generator=gen, device=device)
+            return ((u + 2.0) / 127.0).to(torch.float16)
+        return cls(codes(), scales(), codes(), scales())
+
+
 class StepRunner:
     """Preallocated inputs/outputs/workspace for repeated sd_decode_step calls.
 
@@ -143,9 +171,14 @@ class StepRunner:
         self._seqs = (_lib.StepSeq * n)()
         for s, c in enumerate(self.caches):
             bt = 0 if self.block_tables is None else self.block_tables[s].data_ptr()
-            self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0, self.n_new[s],
-                                         1 if ring else 0, bt,
-                                         int(block_size) if bt else 0, 0)
+            if isinstance(c, SeqCacheQ8):
+                self._seqs[s] = _lib.StepSeq(0, 0, c.capacity, 0, self.n_new[s], 1 if ring else 0, bt,
+                                             int(block_size) if bt else 0, 1, c.kq.data_ptr(),
+                                             c.vq.data_ptr(), c.kd.data_ptr(), c.vd.data_ptr())
+            else:
+                self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0,
+                                             self.n_new[s], 1 if ring else 0, bt,
+                                             int(block_size) if bt else 0, 0)
         self.io = _lib.StepIO(n, ctypes.cast(self._seqs, ctypes.c_void_p), self.tokens.data_ptr(),
                               self.positions.data_ptr(), self.logits.data_ptr(),
                               self.next_tokens.data_ptr(), self.ws.data_ptr(), need)

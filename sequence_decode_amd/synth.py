@@ -10,6 +10,10 @@ input formats; it holds none of the method's arithmetic.  Distributions:
 * activations: fp32 standard normal.
 * K/V caches: fp32 standard normal rounded to fp16 (RNE), layout
   [capacity][H_kv][D].
+* q8_0 K/V caches: int8 codes uniform on {-127, ..., 127}, layout
+  [capacity][H_kv][D]; one fp16 scale per 32 dims, drawn uniform on
+  [2/127, 3/127] (the scale of a block of N(0,1) values, whose maximum of 32 is
+  about 2 to 3) and rounded to fp16, layout [capacity][H_kv][D/32].
 * queries: fp32 standard normal.
 
 Host generators use numpy's PCG64; the device generators (large benchmark
@@ -53,6 +57,13 @@ def kv_cache(g: np.random.Generator, capacity: int, H_kv: int, D: int) -> np.nda
     """fp16 bit patterns [capacity][H_kv][D] of N(0,1) values."""
     x = g.standard_normal(size=(capacity, H_kv, D), dtype=np.float32)
     return x.astype(np.float16).view(np.uint16)
+
+
+def kv_cache_q8(g: np.random.Generator, capacity: int, H_kv: int, D: int):
+    """(codes int8 [capacity][H_kv][D], fp16 scale bits [capacity][H_kv][D/32])."""
+    codes = g.integers(-127, 128, size=(capacity, H_kv, D), dtype=np.int8)
+    d = g.uniform(2.0 / 127.0, 3.0 / 127.0, size=(capacity, H_kv, D // BLOCK))
+    return codes, d.astype(np.float16).view(np.uint16)
 
 
 def queries(g: np.random.Generator, n_seq: int, H_q: int, D: int) -> np.ndarray:

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 4
+    assert L.sd_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -164,6 +164,35 @@ def test_paged_rejections(L):
     assert kv(FAKE, FAKE, 1024, view(100, 1000, 64), 1, 8, 128, None) == SD_EINVAL
 
 
+def test_q8_0_view_rejections(L):
+    a = L.sd_decode_attn_multiseq
+    def view(ctx=100, cap=128, kq=FAKE, kd=FAKE, ld_tok=1024, kv_type=1):
+        return _lib.SeqView(0, 0, ctx, cap, ld_tok, 128, 0, 0, None, 0, kv_type,
+                            kq.value, FAKE.value, kd.value, FAKE.value)
+    one = lambda v: (_lib.SeqView * 1)(v)
+    ok = one(view())
+    need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
+    assert need == 32 * 132 * 4
+    assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
+    for bad, rc in ((view(kq=ctypes.c_void_p(0)), SD_EINVAL),     # missing codes
+                    (view(kd=ctypes.c_void_p(0)), SD_EINVAL),     # missing scales
+                    (view(kv_type=2), SD_EINVAL),                 # unknown type
+                    (view(kq=ODD), SD_EALIGN),
+                    (view(kd=ctypes.c_void_p(0x10004)), SD_EALIGN),  # scales need 8 bytes
+                    (view(ld_tok=1056), SD_EALIGN)):              # strides: multiples of 128
+        assert a(FAKE, 4096, one(bad), 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == rc
+    # one kv_type per call
+    mixed = (_lib.SeqView * 2)(view(), _lib.SeqView(FAKE.value, FAKE.value, 100, 128, 1024, 128))
+    assert a(FAKE, 4096, mixed, 2, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EUNSUPPORTED
+    # each append takes its own type
+    kv8, kv16 = L.sd_kv_append_q8_0, L.sd_kv_append_f16
+    assert kv16(FAKE, FAKE, 1024, ok, 1, 8, 128, None) == SD_EINVAL
+    plain = one(_lib.SeqView(FAKE.value, FAKE.value, 100, 128, 1024, 128))
+    assert kv8(FAKE, FAKE, 1024, plain, 1, 8, 128, None) == SD_EINVAL
+    assert kv8(FAKE, FAKE, 1024, ok, 1, 8, 100, None) == SD_EINVAL        # D % 32
+    assert kv8(FAKE, FAKE, 1024, one(view(ld_tok=1040)), 1, 8, 128, None) == SD_EALIGN
+
+
 def test_rope_kv_and_glue_rejections(L):
     r = L.sd_rope_posvec
     assert r(FAKE, 4, 32, 128, 4096, 128, FAKE, 1e6, 127, None) == SD_EINVAL
@@ -215,6 +244,20 @@ def test_step_rejections(L):
         paged[0].block_size, paged[0].capacity, paged[0].ring = bs, cap, ring
         paged[0].block_table = table.value
         assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(iop), None) == rc
+    q8 = (_lib.StepSeq * 2)(_lib.StepSeq(0, 0, 256, 10, 1, 0, None, 0, 1, FAKE.value, FAKE.value,
+                                         FAKE.value, FAKE.value),
+                            _lib.StepSeq(0, 0, 256, 10, 1, 0, None, 0, 1, FAKE.value, FAKE.value,
+                                         FAKE.value, FAKE.value))
+    io8 = _lib.StepIO(2, ctypes.cast(q8, ctypes.c_void_p), FAKE.value, FAKE.value, FAKE.value,
+                      FAKE.value, 0x100000, 16)
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EWORKSPACE
+    q8[1].kv_type = 0                 # one kv_type per step
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EUNSUPPORTED
+    q8[1].kv_type = 1
+    q8[1].k_d = 0x10004               # scales need 8-byte alignment
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EALIGN
+    q8[1].k_d = 0
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EINVAL
     five = (_lib.StepSeq * 5)(*[_lib.StepSeq(FAKE.value, FAKE.value, 64, 3, 4) for _ in range(5)])
     io5 = _lib.StepIO(5, ctypes.cast(five, ctypes.c_void_p), FAKE.value, FAKE.value, FAKE.value,
                       FAKE.value, 0x100000, 1 << 30)

@@ -287,3 +287,65 @@ def test_paged_pool_step_equals_plain(sd, model):
     for s, c in enumerate(plain):
         kh, vh = host(c.k), host(c.v)
         assert np.array_equal(pkh[:, rows[s]], kh) and np.array_equal(pvh[:, rows[s]], vh), s
+
+
+def _q8_caches_host(n, seed):
+    """q8_0 caches [n_layers][CAP][H_kv][D] codes and [..][D/32] fp16 scale bits."""
+    g = synth.rng(seed)
+    L_, Hkv, Dh = DIMS["n_layers"], DIMS["n_kv_heads"], DIMS["head_dim"]
+    out = []
+    for _ in range(n):
+        kq, kd = synth.kv_cache_q8(g, L_ * CAP, Hkv, Dh)
+        vq, vd = synth.kv_cache_q8(g, L_ * CAP, Hkv, Dh)
+        out.append(tuple(a.reshape((L_, CAP) + a.shape[1:]) for a in (kq, kd, vq, vd)))
+    return out
+
+
+def test_q8_kv_step_oracle_invariance_and_verify(sd, model, model_host):
+    """Steps over q8_0 caches: agreement with the oracle's step over the same
+    caches; each sequence alone gives the batched bits (logits and cache rows);
+    a verify step equals the sequential one-token steps."""
+    import torch
+    from sequence_decode_amd.step import SeqCacheQ8
+    say("q8 KV step")
+    h = model_host
+    m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
+                    h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
+                    h["w_lm"], h["layers"])
+    ch = _q8_caches_host(4, 3600)
+    toks, pos = [4, 77, 600, 999], [0, 63, 256, 319]
+
+    def run(caches_h, tokens, positions, n_new=None):
+        cs = [SeqCacheQ8.from_host(*c) for c in caches_h]
+        r = StepRunner(model, cs, max_ctx=CAP, n_new=n_new)
+        r.tokens.copy_(torch.tensor(tokens, dtype=torch.int32))
+        r.set_positions(positions)
+        r.step()
+        return host(r.logits), host(r.next_tokens), [tuple(host(t) for t in (c.kq, c.kd, c.vq, c.vd)) for c in cs]
+
+    lg, nt, cs = run(ch, toks, pos)
+    ocache = [tuple(a.copy() for a in c) for c in ch]
+    olg, ont = ostep.decode_step(m, ocache, toks, pos)
+    rel = np.linalg.norm(lg - olg) / np.linalg.norm(olg)
+    say(f"  q8 logits normwise relative error vs oracle: {rel:.3e}")
+    assert rel <= 1e-3
+    for s in range(4):
+        l1, n1, c1 = run([ch[s]], [toks[s]], [pos[s]])
+        assert np.array_equal(bits(l1[0]), bits(lg[s])) and n1[0] == nt[s], s
+        for a, b in zip(c1[0], cs[s]):
+            assert np.array_equal(a, b), s
+    # verify step of 3 + 2 tokens against sequential one-token steps
+    news, vpos, vt = [3, 2], [100, 255], [[5, 6, 7], [8, 9]]
+    lv, nv, cv = run(ch[:2], vt[0] + vt[1], vpos, n_new=news)
+    row = 0
+    for s in range(2):
+        c = [SeqCacheQ8.from_host(*ch[s])]
+        rr = StepRunner(model, c, max_ctx=CAP)
+        for i in range(news[s]):
+            rr.tokens.copy_(torch.tensor([vt[s][i]], dtype=torch.int32))
+            rr.set_positions([vpos[s] + i])
+            rr.step()
+            assert np.array_equal(bits(host(rr.logits)[0]), bits(lv[row])), (s, i)
+            row += 1
+        for a, b in zip((c[0].kq, c[0].kd, c[0].vq, c[0].vd), cv[s]):
+            assert np.array_equal(host(a), b), s

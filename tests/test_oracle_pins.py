@@ -509,3 +509,67 @@ def test_fp16_rounding_and_argmax_conventions(oracle_mod):
     assert list(bits) == [0x3C00, 0x3C02, 0x7C00, 0x0000]   # ties to even, overflow
     lg = np.array([[1.0, 3.0, 3.0, -1.0], [0.0, 0.0, 0.0, 0.0]], np.float32)
     assert list(oracle_mod.argmax_rows(lg)) == [1, 0]
+
+
+# ------------------------------------------------------------------ q8_0 KV cache
+
+def test_kv_q8_0_quantizer_hand_values(oracle_mod):
+    """amax 1: d = fp32(1/127), stored as fp16 0x2008 (2^-7 * (1 + 8/1024), the
+    nearest fp16 to 0.0078740); codes of 1, -1, 0.5, 0.25, 0.1 are 127, -127,
+    round(63.5) = 64 (half away from zero), round(31.75) = 32, round(12.7) = 13.
+    An all-zero block gets codes 0 and scale +0."""
+    x = np.zeros((2, 64), np.float32)
+    x[0, :6] = [1.0, -1.0, 0.5, -0.5, 0.25, 0.1]
+    x[0, 32] = 3.0
+    codes, sb = oracle_mod.quantize_kv_q8_0(x)
+    assert sb.shape == (2, 2) and sb.dtype == np.uint16
+    assert sb[0, 0] == 0x2008
+    assert list(codes[0, :6]) == [127, -127, 64, -64, 32, 13]
+    assert not codes[0, 6:32].any()
+    assert codes[0, 32] == 127 and not codes[0, 33:].any()
+    assert sb[1, 0] == 0 and sb[1, 1] == 0 and not codes[1].any()
+
+
+def test_kv_q8_0_round_trip_bounds(oracle_mod):
+    """Values c * 2^-4 with a 127 in every block come back exactly; N(0,1) rows
+    come back within d/2 + 127 |d - fp16(d)| per element."""
+    g = synth.rng(90)
+    c = g.integers(-127, 128, size=(5, 2, 64)).astype(np.float32)
+    c[..., 0] = 127.0
+    c[..., 32] = -127.0
+    x = c * np.float32(2.0 ** -4)
+    codes, sb = oracle_mod.quantize_kv_q8_0(x)
+    assert np.array_equal(codes.astype(np.float32), c)
+    assert np.all(sb == np.float16(2.0 ** -4).view(np.uint16))
+    assert np.array_equal(oracle_mod.dequant_kv_q8_0(codes, sb), x.astype(np.float64))
+    y = g.standard_normal((40, 3, 128), dtype=np.float32)
+    codes, sb = oracle_mod.quantize_kv_q8_0(y)
+    back = oracle_mod.dequant_kv_q8_0(codes, sb)
+    amax = np.abs(y.astype(np.float64)).reshape(40, 3, 4, 32).max(axis=-1)
+    d = amax / 127.0
+    d16 = sb.view(np.float16).astype(np.float64)
+    bound = np.repeat(0.5 * d + 127.0 * np.abs(d - d16) + 1e-12, 32, axis=-1)
+    assert np.all(np.abs(back - y) <= bound)
+
+
+def test_attn_q8_0_equals_fp16_on_exact_values(oracle_mod):
+    """A q8_0 cache whose values d * c are exactly fp16 numbers gives the bits of
+    the fp16-cache attention over those numbers (dequantization and the fp64
+    attention add nothing); and a scale change of one block moves the result."""
+    g = synth.rng(91)
+    L, H_q, H_kv, Dh = 37, 4, 2, 64
+    kc = g.integers(-127, 128, size=(L, H_kv, Dh), dtype=np.int8)
+    vc = g.integers(-127, 128, size=(L, H_kv, Dh), dtype=np.int8)
+    kd = np.full((L, H_kv, Dh // 32), np.float16(2.0 ** -6).view(np.uint16), np.uint16)
+    vd = np.full((L, H_kv, Dh // 32), np.float16(2.0 ** -5).view(np.uint16), np.uint16)
+    k16 = (kc.astype(np.float32) * 2.0 ** -6).astype(np.float16).view(np.uint16)
+    v16 = (vc.astype(np.float32) * 2.0 ** -5).astype(np.float16).view(np.uint16)
+    q = g.standard_normal((3, H_q, Dh), dtype=np.float32)
+    a8 = oracle_mod.attn_verify(q, [(kc, kd, vc, vd)], [L], [3], 0.7)
+    a16 = oracle_mod.attn_verify(q, [(k16, v16)], [L], [3], 0.7)
+    assert np.array_equal(a8, a16)
+    vd2 = vd.copy()
+    vd2[L - 1, 0, 1] = np.float16(2.0 ** -4).view(np.uint16)
+    a8b = oracle_mod.attn_verify(q, [(kc, kd, vc, vd2)], [L], [3], 0.7)
+    assert not np.array_equal(a8b[:, :2, 32:], a8[:, :2, 32:])
+    assert np.array_equal(a8b[:, :2, :32], a8[:, :2, :32]) and np.array_equal(a8b[:, 2:], a8[:, 2:])

@@ -378,7 +378,7 @@ def attention_bench(torch, reps=20):
                 sets.append(views)
             q = torch.randn((len(lens), H_q, D), generator=g, device="cuda")
             o = torch.empty_like(q)
-            ws = torch.empty(max(16, sd.decode_attn_workspace_bytes(sets[0], H_q, D)),
+            ws = torch.zeros(max(16, sd.decode_attn_workspace_bytes(sets[0], H_q, D)),
                              dtype=torch.uint8, device="cuda")
             def four():  # one call per cache set, captured in one graph
                 for v in sets:

@@ -15,7 +15,8 @@ __all__ = [
     "kv_append_f16", "seqview", "decode_attn_workspace_bytes", "decode_attn_multiseq",
     "decode_attn_verify", "ATTN_MAX_NEW",
     "rmsnorm_q8", "swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
-    "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA",
+    "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "kv_append_q8_0",
+    "KV_F16", "KV_Q8_0",
 ]
 
 MAX_TOKENS = 16
@@ -192,7 +193,7 @@ def decode_attn_multiseq(q, views, H_kv, scale, out=None, ws=None, stream=None):
     arr = _views(views)
     need = _lib.load().sd_decode_attn_workspace_bytes(arr, len(views), H_q, D)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     out = torch.empty_like(q) if out is None else out
     _check("sd_decode_attn_multiseq", _lib.load().sd_decode_attn_multiseq(
         _p(q), H_q * D, arr, len(views), H_q, H_kv, D, float(scale), _p(out), _p(ws),
@@ -212,7 +213,7 @@ def decode_attn_verify(q, views, n_new, H_kv, scale, out=None, ws=None, stream=N
     nn = (ctypes.c_int32 * len(n_new))(*[int(v) for v in n_new])
     need = _lib.load().sd_decode_attn_verify_workspace_bytes(arr, nn, len(views), H_q, D)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     out = torch.empty_like(q) if out is None else out
     _check("sd_decode_attn_verify", _lib.load().sd_decode_attn_verify(
         _p(q), H_q * D, arr, nn, len(views), H_q, H_kv, D, float(scale), _p(out), _p(ws),

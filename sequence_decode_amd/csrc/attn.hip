@@ -142,7 +142,7 @@ template <bool Q8>
 __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q, int64_t ld_q,
                                                     SeqArgs seqs, int H_q, float scale,
                                                     float* __restrict__ part) {
-  constexpr int kVB = Q8 ? kWaveVBytes8 : kWaveVBytes;  // LDS bytes of a wave's V rows (then O partial)
+  constexpr int kVB = Q8 ? kWaveVBytes8 : kWaveVBytes / 2;  // LDS bytes of a wave's V rows (then O partial)
   static_assert(16 * HD * 4 <= kVB, "a wave's O partial fits its V region");
   __shared__ __attribute__((aligned(1024))) uint8_t s_v[4 * kVB];  // V rows, then O partials
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[Q8 ? 4 * 64 * 4 : 1];  // per wave and key: K, V scales
@@ -284,13 +284,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       qv[kk][1] = qp[8 * kk + 1];
     }
   }
-  if constexpr (!Q8) {
-    // ---- V rows of this wave -> LDS by DMA: instruction i fills rows 4i .. 4i+3;
-    // lane l writes row 4i + l/16 at 16-byte position l%16, which holds the row's
-    // 16-byte piece (l%16) ^ 2 vswz(row).
-    // keys past the end read the last key, and in a ring keys below jlo read
-    // key jlo (their weight is 0); a plain cache's keys below a window are
-    // real rows and read as they are
+  // fp16: the wave's V rows go to LDS in two halves of 32 rows (8 KiB), the
+  // second after the first has been read
+  auto dma_v = [&](int h) {
     const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
     const int jv = wk + (lane >> 4);
     if (__builtin_expect(lin, 1)) {
@@ -298,24 +294,27 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + jlast * A.ld_tok);
       const int64_t step4 = 4 * A.ld_tok * 2;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int ii = 0; ii < 8; ++ii) {
+        const int i = 8 * h + ii;
         const int r = 4 * i + (lane >> 4);
         const int piece = (lane & 15) ^ (2 * vswz(r));
         const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, 0);
       }
     } else {
       const int prow0 = (j0 + jlo) % A.ring_cap;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int ii = 0; ii < 8; ++ii) {
+        const int i = 8 * h + ii;
         const int r = 4 * i + (lane >> 4);
         const int piece = (lane & 15) ^ (2 * vswz(r));
         const int jl = min(max(jv + 4 * i, jlo), nk - 1);
         const uint8_t* row = reinterpret_cast<const uint8_t*>(vbase + (int64_t)krow(prow0, jl) * A.ld_tok);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, 0);
       }
     }
-  }
+  };
+  if constexpr (!Q8) dma_v(0);
   if constexpr (Q8) {
     // every load is in flight before the first use of a loaded value: the pins
     // keep the compiler from moving arithmetic (and its waits) between the issues
@@ -423,15 +422,22 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     const int vg = vswz(8 * kg + (col >> 2));
     const int rbase = (8 * kg + (col >> 2)) * kRowBytes + 8 * (col & 3);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-      const int a0 = rbase + ((dt ^ vg) << 5);
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b) {
+      if (b == 1) {
+        // every read of the first half has returned before its rows are replaced
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        dma_v(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int a0 = rbase + ((dt ^ vg) << 5);
         const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes));
+            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0));
         const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + b * 32 * kRowBytes + 4 * kRowBytes));
+            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + 4 * kRowBytes));
         const h8 av = __builtin_bit_cast(h8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[b], o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);

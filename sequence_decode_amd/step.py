@@ -156,7 +156,7 @@ class StepRunner:
         need = _lib.load().sd_decode_step_workspace_bytes(ctypes.byref(model.struct), rows, max_ctx)
         if need == 0:
             raise ValueError("model or batch not supported by sd_decode_step")
-        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         self.logits = torch.empty((rows, V), dtype=torch.float32, device=dev)
         self.next_tokens = torch.empty(rows, dtype=torch.int32, device=dev)
         self.tokens = torch.zeros(rows, dtype=torch.int32, device=dev)

@@ -114,3 +114,28 @@ def test_attention_invariance_permutation_isolation(sd):
     o = _gpu(sd, np.repeat(q[:1], 4, axis=0), [devkv[0]] * 4, [lens[0]] * 4)
     for s in range(4):
         assert np.array_equal(bits(o[s]), bits(base[0]))
+
+
+def test_workspace_reuse_across_shapes(sd):
+    """One workspace serves successive calls of different shapes, and the
+    results are those of calls on fresh workspaces (nothing carries over)."""
+    import torch
+    say("attention workspace reuse")
+    cases = [([2050, 3072, 16384, 32768], [1, 1, 1, 1]), ([1, 300], [1, 1]), ([700, 65, 5000], [4, 2, 3])]
+    size = 0
+    prepared = []
+    for i, (lens, news) in enumerate(cases):
+        kv = [_seq(6000 + 10 * i + j, L) for j, L in enumerate(lens)]
+        devkv = [_upload(x) for x in kv]
+        views = [sd.seqview(k, v, L) for (k, v), L in zip(devkv, lens)]
+        q = dev(synth.queries(synth.rng(6100 + i), sum(news), H_Q, D))
+        need = sd._lib.load().sd_decode_attn_verify_workspace_bytes(
+            sd._views(views), (__import__("ctypes").c_int32 * len(news))(*news), len(views), H_Q, D)
+        size = max(size, need)
+        prepared.append((views, news, q, devkv))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for i, (views, news, q, _) in enumerate(prepared):
+            shared = host(sd.decode_attn_verify(q, views, news, H_KV, SCALE, ws=ws))
+            fresh = host(sd.decode_attn_verify(q, views, news, H_KV, SCALE))
+            assert np.array_equal(bits(shared), bits(fresh)), (rnd, i)

@@ -403,6 +403,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="only the decode-step tok/s")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="only the attention timings (fp16, q8_0 and paged caches)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
@@ -417,6 +419,16 @@ def main():
     torch.cuda.set_device(0)
     if args.decode_only:
         print(json.dumps(decode_bench(torch, steps=max(8, args.steps), warmup=args.warmup)), flush=True)
+        return
+    if args.attention_only:
+        if args.calibrate_copy:
+            a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+            del a, b
+        print(json.dumps(attention_bench(torch)), flush=True)
         return
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

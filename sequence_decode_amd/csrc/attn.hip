@@ -554,8 +554,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 // Grid (query rows * H_q), 256 threads.  Merges the chunk partials of one
 // (sequence, token, head) -- its chunks are those up to the token's position: M = max_c m_c; w_c = exp(m_c - M); L = sum_c l_c w_c by a
 // fixed tree over chunk index; O[d] = sum_c o_c[d] w_c with chunks split into
-// two interleaved halves (threads 0..127 take even chunks, 128..255 odd ones,
-// each in chunk order) that are then added.  Every shape depends only on the
+// eight interleaved groups (group j takes chunks j, j+8, ..., in chunk order)
+// that are then added by a fixed tree.  Every shape depends only on the
 // sequence's chunk count.  Optionally also emits the q8 blocks of the output
 // row (the quantized input of the output projection).
 constexpr int kMaxChunks = SD_MAX_CTX / SD_ATTN_CHUNK;
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
                                                       float* __restrict__ out, int8_t* oq, float* od) {
   __shared__ float s_w[kMaxChunks];
   __shared__ float s_red[256];
-  __shared__ float s_o[HD];
+  __shared__ __attribute__((aligned(16))) float s_o[8 * HD];
   const int row = blockIdx.x / H_q;
   const int h = blockIdx.x - row * H_q;
   const int tid = threadIdx.x;
@@ -600,28 +600,44 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
   if ((tid & 63) == 0) s_red[tid >> 6] = lp;
   __syncthreads();
   const float L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
-  // values: two interleaved halves of the chunks, each in chunk order
-  const int d = tid & (HD - 1);
-  const int half = tid >> 7;
-  float O = 0.0f;
+  // values: eight interleaved groups of chunks (group j: chunks j, j+8, ...),
+  // each summed in chunk order by 32 threads of 4 dims (one 16-byte load per
+  // chunk, 16 chunks in flight), then the groups added by a fixed tree
   {
-    int c = half;
-    for (; c + 6 < nc; c += 8) {
-      const float a0 = base[(int64_t)c * PF + 4 + d];
-      const float a1 = base[(int64_t)(c + 2) * PF + 4 + d];
-      const float a2 = base[(int64_t)(c + 4) * PF + 4 + d];
-      const float a3 = base[(int64_t)(c + 6) * PF + 4 + d];
-      O = fadd(O, fmul(a0, s_w[c]));
-      O = fadd(O, fmul(a1, s_w[c + 2]));
-      O = fadd(O, fmul(a2, s_w[c + 4]));
-      O = fadd(O, fmul(a3, s_w[c + 6]));
+    const int j = tid >> 5;          // chunk group
+    const int d4 = (tid & 31) * 4;   // dims d4 .. d4+3
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    int c = j;
+    for (; c + 8 * 15 < nc; c += 8 * 16) {
+      f32x4 a[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)(c + 8 * i) * PF + 4 + d4);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float w = s_w[c + 8 * i];
+        acc.x = fadd(acc.x, fmul(a[i].x, w));
+        acc.y = fadd(acc.y, fmul(a[i].y, w));
+        acc.z = fadd(acc.z, fmul(a[i].z, w));
+        acc.w = fadd(acc.w, fmul(a[i].w, w));
+      }
     }
-    for (; c < nc; c += 2) O = fadd(O, fmul(base[(int64_t)c * PF + 4 + d], s_w[c]));
+    for (; c < nc; c += 8) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(base + (int64_t)c * PF + 4 + d4);
+      const float w = s_w[c];
+      acc.x = fadd(acc.x, fmul(a.x, w));
+      acc.y = fadd(acc.y, fmul(a.y, w));
+      acc.z = fadd(acc.z, fmul(a.z, w));
+      acc.w = fadd(acc.w, fmul(a.w, w));
+    }
+    *reinterpret_cast<f32x4*>(s_o + j * HD + d4) = acc;
   }
-  if (half == 1) s_o[d] = O;
   __syncthreads();
-  if (half == 0) {
-    const float v = fdiv(fadd(O, s_o[d]), L);
+  if (tid < HD) {
+    const int d = tid;
+    const float* g8 = s_o + d;
+    const float O = fadd(fadd(fadd(g8[0], g8[HD]), fadd(g8[2 * HD], g8[3 * HD])),
+                         fadd(fadd(g8[4 * HD], g8[5 * HD]), fadd(g8[6 * HD], g8[7 * HD])));
+    const float v = fdiv(O, L);
     const int64_t idx = ((int64_t)row * H_q + h) * HD + d;
     out[idx] = v;
     if (oq) {

@@ -139,3 +139,31 @@ def test_workspace_reuse_across_shapes(sd):
             shared = host(sd.decode_attn_verify(q, views, news, H_KV, SCALE, ws=ws))
             fresh = host(sd.decode_attn_verify(q, views, news, H_KV, SCALE))
             assert np.array_equal(bits(shared), bits(fresh)), (rnd, i)
+
+
+def test_attention_maximum_context(sd):
+    """The largest supported span, SD_MAX_CTX = 524288 keys (2048 chunks), in
+    one sequence beside a short one: sampled heads against the oracle, and the
+    long sequence alone gives the same bits."""
+    import torch
+    L_max = 2048 * 256
+    say(f"attention at the maximum context {L_max}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6200)
+    k = torch.randn((L_max, H_KV, D), generator=g, device="cuda").half()
+    v = torch.randn((L_max, H_KV, D), generator=g, device="cuda").half()
+    ks, vs = _upload(_seq(6201, 300))
+    q = synth.queries(synth.rng(6202), 2, H_Q, D)
+    views = [sd.seqview(k, v, L_max), sd.seqview(ks, vs, 300)]
+    o = host(sd.decode_attn_multiseq(dev(q), views, H_KV, SCALE))
+    kh, vh = host(k), host(v)
+    for gi in (0, 3, 7):  # KV heads 0, 3, 7 and their four query heads each
+        ref = oracle.attn_decode_one(q[0][gi * 4:gi * 4 + 4], np.ascontiguousarray(kh[:, gi:gi + 1]),
+                                     np.ascontiguousarray(vh[:, gi:gi + 1]), L_max, SCALE)
+        _check_parity(o[0][gi * 4:gi * 4 + 4], ref)
+    solo = host(sd.decode_attn_multiseq(dev(q[:1]), views[:1], H_KV, SCALE))
+    assert np.array_equal(bits(solo[0]), bits(o[0]))
+    # one key more than the maximum span is refused
+    too_long = sd.SeqView(k.data_ptr(), v.data_ptr(), L_max + 1, L_max + 1, H_KV * D, D)
+    with pytest.raises(sd.SdError):
+        sd.decode_attn_multiseq(dev(q[:1]), [too_long], H_KV, SCALE, ws=torch.zeros(16, dtype=torch.uint8, device="cuda"))

@@ -79,6 +79,8 @@ struct GemvPlan {
   bool mfma;         // matrix-core kernel (tiles of 16 rows)
   bool use_reg;      // activations held in registers (1..8 tokens, <= 4 chunks)
   int sp;            // waves per row in the register kernel (1, 2 or 4)
+  bool stage;        // register kernel: activations staged once per workgroup in LDS
+  int nw;            // register kernel: waves per workgroup (8 staged, else 4)
   int slice_pairs;   // pairs staged per LDS slice (multiple of 64, or all)
   int n_slices;
   size_t lds_bytes;

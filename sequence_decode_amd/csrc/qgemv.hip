@@ -149,22 +149,41 @@ __device__ __forceinline__ void store_out(float v, int n, int t, const float* re
 // ---------------------------------------------------------------------------
 // 1..8 tokens, K <= 16384 (at most 4 chunks): the streaming kernel.
 //
-// Wave w of the workgroup takes chunk w % SP (SP = chunks rounded up to 1, 2
-// or 4) of row slot w / SP.  Weights never pass through registers on their
-// way in: every wave streams the 64-pair segments of its rows (<= 4352 bytes,
-// contiguous in memory) with global_load_lds_dwordx4 into a private ring of
-// DEPTH LDS slots, so the bytes in flight per CU are set by the ring, not by
-// the register budget.  A lane then reads its pair (17 dwords) from LDS; its
-// pair's activations for all tokens were loaded once into registers.  With
-// SP > 1 the chunk sums of a row meet in LDS and one thread adds them in chunk
-// order.  Outputs collect in a small LDS table and are written every kTable
-// items: on gfx9 stores share the in-order vmcnt counter with the DMAs, so a
-// store inside the loop would make each wait for weights also wait for it.
+// NW waves per workgroup; wave w takes chunk w % SP (SP = chunks rounded up to
+// 1, 2 or 4) of row slot w / SP.  Weights never pass through registers on
+// their way in: every wave streams the 64-pair segments of its rows (<= 4352
+// bytes, contiguous in memory) with global_load_lds_dwordx4 into a private
+// ring of kRing LDS slots, so the bytes in flight per CU are set by the ring,
+// not by the register budget.  A lane then reads its pair (17 dwords) from
+// LDS; its pair's activations for all tokens sit in registers.  With SP > 1
+// the chunk sums of a row meet in LDS and one thread adds them in chunk order.
+// Outputs collect in a small LDS table and are written every kTable items: on
+// gfx9 stores share the in-order vmcnt counter with the DMAs, so a store
+// inside the loop would make each wait for weights also wait for it.
+//
+// Activations.  Every workgroup needs the same few KiB of activations, and
+// at 4 tokens the copies that all waves fetch from L2 at the start rival the
+// weights themselves.  So when they fit (STAGE), one workgroup of 8 waves runs
+// per CU and its waves DMA the activations of the workgroup's chunks into LDS
+// once, contiguously, before the first weights; each lane then takes its
+// pair's share from there.  Otherwise (4 waves, 5..8 tokens over 4 chunks)
+// each lane loads its pair's activations itself.
 constexpr int kRing = 2;
 constexpr int kTable = 32;
 // rows per streaming item (one row per item measured best: deeper or wider
 // items lowered the bytes in flight per CU)
 constexpr int dma_rows(int nt) { return nt > 0 ? 1 : 1; }
+// staged activation bytes per chunk and token: 4096 code bytes + 128 fp32 scales
+constexpr int kStageX = 4096;
+constexpr int kStageD = 512;
+// 8 waves with their rings, the staged activations of sp chunks and the
+// output table fit the 160 KiB of LDS (up to 4 tokens over 4 chunks, all 8
+// over 1 or 2)
+constexpr bool stage_fits(int sp, int nt) {
+  return 8 * kRing * dma_rows(nt) * 64 * kPairBytes + sp * nt * (kStageX + kStageD) <= kGemvLdsMax &&
+         8 * kRing * dma_rows(nt) * 64 * kPairBytes + sp * nt * (kStageX + kStageD) +
+                 kTable * 8 * dma_rows(nt) * nt * 4 <= 160 * 1024;
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -193,11 +212,12 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
   }
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 // Issues the DMA of one chunk segment (seg_bytes <= 4352) of one row.  A full
 // segment is 4 whole 1 KiB instructions plus one for lanes 0..15; a shorter
 // (last) segment is cut at the lane granularity.  Returns the instructions issued.
 __device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg_bytes, int lane) {
-  typedef __attribute__((address_space(3))) void* lds_ptr;
   if (seg_bytes == 64 * kPairBytes) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -216,8 +236,8 @@ __device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg
   return n;
 }
 
-template <int NT, int SP, int R>
-__global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_dma(
+template <int NT, int SP, int R, int NW, bool STAGE>
+__global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd,
     const float* residual, float* y, int64_t ldy, int S) {
@@ -225,8 +245,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_dma(
   // chunk sums of the last kTable items, [item % kTable][wave][row * NT + token];
   // written without barriers (one row per item), combined and stored every
   // kTable items
-  __shared__ float table[kTable][4][R * NT];
-  constexpr int SLOTS = 4 / SP;
+  __shared__ float table[kTable][NW][R * NT];
+  constexpr int SLOTS = NW / SP;
   constexpr int SEG = 64 * kPairBytes;  // bytes of a full chunk segment
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -238,6 +258,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_dma(
   const int seg_bytes = seg_pairs * kPairBytes;
   const int n_ins = seg_bytes == SEG ? 5 : (seg_bytes + 1023) / 1024;
   uint8_t* ring = lds_dyn + wave * (kRing * R * SEG);
+  // staged activations: codes [SP][NT][kStageX], then scales [SP][NT][kStageD]
+  uint8_t* stage = lds_dyn + NW * (kRing * R * SEG);
+  const int nb = 2 * P;
 
   // item k of slot sl covers rows (blockIdx.x + k * gridDim.x) * SLOTS * R + sl * R + [0, R)
   const int stride = (int)gridDim.x * SLOTS * R;
@@ -261,12 +284,70 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_dma(
         dma_segment(w + (int64_t)(r0 + r) * row_bytes + (int64_t)chunk * SEG, l + r * SEG, seg_bytes, lane);
   };
 
+  if constexpr (STAGE) {
+    // The workgroup's activation copies, as a list of (chunk, token, part)
+    // with parts 0..3 the 1 KiB quarters of the codes and parts 4..5 the two
+    // 256-byte halves of the scales (4-byte DMAs: scales are only 4-byte
+    // aligned), dealt to the waves round robin; lanes past the chunk's end
+    // issue nothing.  Issued ahead of the weights, so waiting for them leaves
+    // the weights in flight.
+    for (int i = wave; i < min(S, SP) * NT * 6; i += NW) {
+      const int c = i / (NT * 6);
+      const int t = (i / 6) % NT;
+      const int part = i % 6;
+      const int cp = min(64, P - 64 * c);  // pairs of chunk c
+      if (part < 4) {
+        const int off = part * 1024 + lane * 16;
+        if (off < cp * 64)
+          __builtin_amdgcn_global_load_lds(
+              static_cast<const void*>(xq + (int64_t)t * K + 4096 * (int64_t)c + off),
+              (lds_ptr)(stage + (c * NT + t) * kStageX + part * 1024), 16, 0, 0);
+      } else {
+        const int e = (part - 4) * 64 + lane;  // scale index within the chunk
+        if (e < 2 * cp)
+          __builtin_amdgcn_global_load_lds(
+              static_cast<const void*>(xd + (int64_t)t * nb + 128 * (int64_t)c + e),
+              (lds_ptr)(stage + SP * NT * kStageX + (c * NT + t) * kStageD + (part - 4) * 256), 4, 0, 0);
+      }
+    }
+  }
+
   for (int d = 0; d < kRing - 1; ++d) issue(d);
 
   uint32_t act[NT][kPairDw];
   float dxA[NT], dxB[NT];
-  {
-    const int nb = 2 * P;
+  if constexpr (STAGE) {
+    // own copies landed (only the weights of the items issued above may be
+    // younger), then everyone's
+    int younger = 0;
+#pragma unroll
+    for (int d = 0; d < kRing - 1; ++d) younger += ins_of(d);
+    wait_vmcnt_rt(younger);
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = pv ? chunk : 0;
+      const u32x4a* src = reinterpret_cast<const u32x4a*>(stage + (c * NT + t) * kStageX + 64 * lane);
+      const float* sd = reinterpret_cast<const float*>(stage + SP * NT * kStageX + (c * NT + t) * kStageD);
+      uint32_t a[16];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4a q = src[v];
+        a[4 * v + 0] = pv ? q.x : 0u;
+        a[4 * v + 1] = pv ? q.y : 0u;
+        a[4 * v + 2] = pv ? q.z : 0u;
+        a[4 * v + 3] = pv ? q.w : 0u;
+      }
+      dxA[t] = pv ? sd[2 * lane] : 0.0f;
+      dxB[t] = pv ? sd[2 * lane + 1] : 0.0f;
+      act[t][0] = a[0] << 16;
+#pragma unroll
+      for (int c2 = 1; c2 < 8; ++c2) act[t][c2] = (a[c2 - 1] >> 16) | (a[c2] << 16);
+      act[t][8] = a[7] >> 16;
+#pragma unroll
+      for (int c2 = 0; c2 < 8; ++c2) act[t][9 + c2] = a[8 + c2];
+    }
+  } else {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (pv) {
@@ -300,7 +381,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_dma(
   // chunk sums added in chunk order.
   auto flush = [&](int kb, int cnt) {
     __syncthreads();
-    for (int i = threadIdx.x; i < cnt * SLOTS * R * NT; i += kGemvThreads) {
+    for (int i = threadIdx.x; i < cnt * SLOTS * R * NT; i += 64 * NW) {
       const int ki = i / (SLOTS * R * NT);
       const int rem = i - ki * (SLOTS * R * NT);
       const int sl = rem / (R * NT);
@@ -697,18 +778,18 @@ hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, 
   return hipGetLastError();
 }
 
-template <int NT, int SP>
+template <int NT, int SP, int NW, bool STAGE>
 hipError_t launch_dma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                       const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st) {
   constexpr int R = dma_rows(NT);
-  static bool lds_raised = false;  // rings of R rows take up to 70 KiB
+  static bool lds_raised = false;  // rings and staged activations take up to 140 KiB
   if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R>), dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, st,
+  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
                      xq, K, xd, residual, y, ldy, pl.chunks);
   return hipGetLastError();
@@ -735,11 +816,15 @@ constexpr int lds_rows(int nt) { return nt <= 8 ? 2 : 4; }
 template <int NT>
 hipError_t launch_dma_nt(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                          const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st) {
-  switch (pl.sp) {
-    case 1: return launch_dma<NT, 1>(pl, w, N, K, xq, xd, residual, y, ldy, st);
-    case 2: return launch_dma<NT, 2>(pl, w, N, K, xq, xd, residual, y, ldy, st);
-    default: return launch_dma<NT, 4>(pl, w, N, K, xq, xd, residual, y, ldy, st);
+  if (pl.stage) {
+    switch (pl.sp) {
+      case 1: return launch_dma<NT, 1, 8, true>(pl, w, N, K, xq, xd, residual, y, ldy, st);
+      case 2: return launch_dma<NT, 2, 8, true>(pl, w, N, K, xq, xd, residual, y, ldy, st);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (pl.sp == 4) return launch_dma<NT, 4, 4, false>(pl, w, N, K, xq, xd, residual, y, ldy, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -749,7 +834,7 @@ size_t mfma_lds_bytes() { return (size_t)kMfmaActBytes + kMfmaScBytes + kMfmaZer
 bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan) {
   if (N < 1 || K < 256 || K % 256 != 0 || n_tok < 1 || n_tok > SD_MAX_TOKENS) return false;
   if (N > (int64_t)1 << 30 || K > (int64_t)1 << 24) return false;
-  GemvPlan p;
+  GemvPlan p{};
   p.pairs = (int)(K / 64);
   p.chunks = (p.pairs + 63) / 64;
   const size_t per_pair = (size_t)n_tok * kActDw * 4;
@@ -773,16 +858,21 @@ bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan) {
   p.use_reg = n_tok <= 8 && p.chunks <= 4;
   if (p.use_reg) {
     p.sp = p.chunks == 1 ? 1 : (p.chunks == 2 ? 2 : 4);
+    // staging paid off with 1 or 2 chunks; over 4 chunks the direct loads of
+    // two 4-wave workgroups per CU measured faster
+    p.stage = p.sp <= 2 && stage_fits(p.sp, n_tok);
+    p.nw = p.stage ? 8 : 4;
     p.rows_per_wave = dma_rows(n_tok);
     p.slice_pairs = p.pairs;
     p.n_slices = 1;
-    const int slots = 4 / p.sp;
+    const int slots = p.nw / p.sp;
     p.n_blocks = (int)((N + p.rows_per_wave - 1) / p.rows_per_wave);
     const int64_t wg_needed = (p.n_blocks + slots - 1) / slots;
-    const int64_t max_grid = 256 * 2;
+    const int64_t max_grid = p.stage ? 256 : 256 * 2;  // one or two workgroups per CU
     const int64_t iters = (wg_needed + max_grid - 1) / max_grid;
     p.grid = (int)((wg_needed + iters - 1) / iters);
-    p.lds_bytes = (size_t)4 * kRing * p.rows_per_wave * 64 * kPairBytes;
+    p.lds_bytes = (size_t)p.nw * kRing * p.rows_per_wave * 64 * kPairBytes +
+                  (p.stage ? (size_t)p.sp * n_tok * (kStageX + kStageD) : 0);
     *plan = p;
     return true;
   } else {

@@ -85,6 +85,7 @@ def test_gemv_single_and_two_block_terms_bitwise(sd):
 @pytest.mark.parametrize("N,K,n_tok", [
     (1, 256, 1), (7, 256, 3), (1000, 512, 4), (257, 768, 2), (513, 4096, 5),
     (96, 1280, 16), (130, 14336, 4), (64, 14336, 16), (1024, 4096, 8), (300, 2304, 12),
+    (300, 8192, 3), (77, 6144, 7), (5000, 4352, 4),
 ])
 def test_gemv_parity_small(sd, N, K, n_tok):
     say(f"gemv parity N={N} K={K} n_tok={n_tok}")

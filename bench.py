@@ -407,6 +407,38 @@ def attention_bench(torch, reps=20):
     return out
 
 
+def step_only(torch, n_seq, steps, warmup):
+    """Decode steps of n_seq sequences at the ragged contexts {2050, 3072, 16384,
+    32768}[:n_seq] and nothing else: the run a kernel trace of one step's
+    kernels is taken on (per-kernel totals / (warmup + steps) = one step)."""
+    from sequence_decode_amd.step import DecodeModel, SeqCache, StepRunner
+    dims = dict(n_layers=32, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=14336,
+                vocab=151936, eps=1e-6, theta=1e6)
+    model = DecodeModel.random_device(11, dims)
+    ctxs = [2050, 3072, 16384, 32768][:n_seq]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    span = warmup + steps + 4
+    caches = [SeqCache.random_device(g, 32, ctx + span, 8, 128) for ctx in ctxs]
+    r = StepRunner(model, caches, max_ctx=max(ctxs) + span)
+    r.tokens.copy_(torch.arange(n_seq, dtype=torch.int32) + 7)
+    r.set_positions([c - 1 for c in ctxs])
+    for _ in range(warmup):
+        r.step()
+        r.advance()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+        r.advance()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    log(f"decode ragged n_seq={n_seq}: {n_seq / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step), "
+        f"{warmup + steps} steps in the run")
+    return {"step_only": {"n_seq": n_seq, "contexts": ctxs, "tok_s": round(n_seq / dt, 2),
+                          "ms_per_step": round(dt * 1e3, 3), "steps_in_run": warmup + steps}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,6 +449,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="only the decode-step tok/s")
+    ap.add_argument("--step-only", type=int, default=0, metavar="N_SEQ",
+                    help="only decode steps of N_SEQ ragged sequences (for a kernel trace of the step)")
     ap.add_argument("--attention-only", action="store_true",
                     help="only the attention timings (fp16, q8_0 and paged caches)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -431,6 +465,9 @@ def main():
     import sequence_decode_amd as sd
     sd.load()
     torch.cuda.set_device(0)
+    if args.step_only:
+        print(json.dumps(step_only(torch, args.step_only, args.steps, args.warmup)), flush=True)
+        return
     if args.decode_only:
         print(json.dumps(decode_bench(torch, steps=max(8, args.steps), warmup=args.warmup)), flush=True)
         return

@@ -251,8 +251,13 @@ def decode_bench(torch, steps, warmup):
                 r.advance()
             torch.cuda.synchronize()
             dt = (time.perf_counter() - t0) / steps
+            # bytes a step must read: every projection and LM-head weight once, every sequence's K and V
+            # (8 heads x 128 dims x 2 B, twice) in every layer
+            step_bytes = model.weight_bytes + sum(ctxs[:n]) * 4096 * dims["n_layers"]
             res[f"{label}_n{n}"] = {"tok_s": round(n / dt, 2), "ms_per_step": round(dt * 1e3, 3),
-                                    "host_enqueue_ms": round(host / steps * 1e3, 3)}
+                                    "host_enqueue_ms": round(host / steps * 1e3, 3),
+                                    "step_bytes": step_bytes,
+                                    "frac_hbm_peak": round(step_bytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"decode {label} n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step, "
                 f"host enqueue {host / steps * 1e3:.3f} ms)")
     # verify steps: every sequence brings n_new proposed tokens (causal within the burst);
@@ -400,7 +405,8 @@ def attention_bench(torch, reps=20):
             us = time_graph(torch, four, reps, 2) * 1e6 / 4
             per_key = 2176 if kind == "q8_0" else 4096
             gbs = sum(lens) * per_key / us / 1e3
-            out[f"{cname}_{kind}"] = {"us": round(us, 2), "GB_s": round(gbs, 1)}
+            out[f"{cname}_{kind}"] = {"us": round(us, 2), "GB_s": round(gbs, 1),
+                                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
             log(f"attention {cname} {kind}: {us:.2f} us, {gbs:.1f} GB/s of cache bytes")
             del keep, sets
             torch.cuda.empty_cache()

@@ -166,19 +166,18 @@ __device__ __forceinline__ void store_out(float v, int n, int t, const float* re
 // weights themselves.  So when they fit (STAGE), one workgroup of 8 waves runs
 // per CU and its waves DMA the activations of the workgroup's chunks into LDS
 // once, contiguously, before the first weights; each lane then takes its
-// pair's share from there.  Otherwise (4 waves, 5..8 tokens over 4 chunks)
-// each lane loads its pair's activations itself.
+// pair's share from there.  Over 3 or 4 chunks (4 waves, two workgroups per
+// CU) each lane loads its pair's activations itself.
 constexpr int kRing = 2;
 constexpr int kTable = 32;
 // rows per streaming item (one row per item measured best: deeper or wider
 // items lowered the bytes in flight per CU)
-constexpr int dma_rows(int nt) { return nt > 0 ? 1 : 1; }
+constexpr int dma_rows(int) { return 1; }
 // staged activation bytes per chunk and token: 4096 code bytes + 128 fp32 scales
 constexpr int kStageX = 4096;
 constexpr int kStageD = 512;
 // 8 waves with their rings, the staged activations of sp chunks and the
-// output table fit the 160 KiB of LDS (up to 4 tokens over 4 chunks, all 8
-// over 1 or 2)
+// output table fit the 160 KiB of LDS (all 8 tokens over 1 or 2 chunks)
 constexpr bool stage_fits(int sp, int nt) {
   return 8 * kRing * dma_rows(nt) * 64 * kPairBytes + sp * nt * (kStageX + kStageD) <= kGemvLdsMax &&
          8 * kRing * dma_rows(nt) * 64 * kPairBytes + sp * nt * (kStageX + kStageD) +

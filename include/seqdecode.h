@@ -47,7 +47,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 5
+#define SD_ABI_VERSION 6
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -329,6 +329,25 @@ int sd_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D, const float
  */
 int sd_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F,
                  int8_t* xq, float* xd, float* y, sd_stream_t stream);
+
+/*
+ * sd_qgemv_q8_0_swiglu_q8 -- the FFN's gate|up projection and its SwiGLU in
+ * one launch (ds4 pull request 604, "Commit walkthrough / Graph driver": the
+ * FFN runs on the whole batch; the quantizer fused into its producer keeps
+ * the consumer's convention, as "#1209 Speed up concurrent generation, fix
+ * QFUSE, and improve prefill monitoring", "What changed and why" item 2,
+ * requires).  Bitwise equal to sd_qgemv_q8_0_batch(w, 2F, K, ...) into gu
+ * followed by sd_swiglu_q8(gu, 2F, n_tok, F, xq_out, xd_out, NULL); gu is
+ * never written.
+ *   w       q8_0 [2F][K]: F gate rows, then F up rows (as sd_qgemv_q8_0_batch).
+ *   xq, xd  q8 activations of n_tok tokens (as sd_qgemv_q8_0_batch).
+ *   xq_out  [n_tok][F] int8; xd_out [n_tok][F/32] fp32.
+ * Requires 1 <= n_tok <= 8, K % 256 == 0, K <= 4096, F % 32 == 0,
+ * 32 <= F <= 2^29; otherwise SD_EINVAL / SD_EUNSUPPORTED and nothing runs.
+ */
+int sd_qgemv_q8_0_swiglu_q8(const void* w, int64_t F, int64_t K, const int8_t* xq,
+                            const float* xd, int n_tok, int8_t* xq_out, float* xd_out,
+                            sd_stream_t stream);
 
 /*
  * sd_embed_f16 -- x[t][:] = fp32(table[tokens[t]][:]) (exact widening).

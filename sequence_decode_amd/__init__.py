@@ -14,7 +14,7 @@ __all__ = [
     "SdError", "load", "abi_version", "quantize_q8_act", "qgemv_q8_0_batch", "rope_posvec",
     "kv_append_f16", "seqview", "decode_attn_workspace_bytes", "decode_attn_multiseq",
     "decode_attn_verify", "ATTN_MAX_NEW",
-    "rmsnorm_q8", "swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
+    "rmsnorm_q8", "swiglu_q8", "qgemv_q8_0_swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
     "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "kv_append_q8_0",
     "KV_F16", "KV_Q8_0",
 ]
@@ -244,6 +244,22 @@ def swiglu_q8(gu, F, want_y=False, stream=None):
     _check("sd_swiglu_q8", _lib.load().sd_swiglu_q8(
         _p(gu), gu.shape[1], n_tok, F, _p(xq), _p(xd), _p(y), _stream(stream)))
     return (xq, xd, y) if want_y else (xq, xd)
+
+
+def qgemv_q8_0_swiglu_q8(w, F, K, xq, xd, stream=None):
+    """gate|up projection (w: 2F q8_0 rows of K) and SwiGLU in one launch ->
+    (xq_out int8 [n_tok][F], xd_out fp32 [n_tok][F/32]); bitwise equal to
+    qgemv_q8_0_batch followed by swiglu_q8."""
+    import torch
+    _need(w, torch.uint8, "w")
+    _need(xq, torch.int8, "xq")
+    _need(xd, torch.float32, "xd")
+    n_tok = xq.shape[0]
+    oq = torch.empty((n_tok, F), dtype=torch.int8, device=xq.device)
+    od = torch.empty((n_tok, F // 32), dtype=torch.float32, device=xq.device)
+    _check("sd_qgemv_q8_0_swiglu_q8", _lib.load().sd_qgemv_q8_0_swiglu_q8(
+        _p(w), F, K, _p(xq), _p(xd), n_tok, _p(oq), _p(od), _stream(stream)))
+    return oq, od
 
 
 def embed_f16(table, tokens, stream=None):

@@ -268,6 +268,16 @@ int sd_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F, int8_t* xq
   return from_hip(launch_swiglu_q8(gu, ldgu, n_tok, F, xq, xd, y, hs(stream)));
 }
 
+int sd_qgemv_q8_0_swiglu_q8(const void* w, int64_t F, int64_t K, const int8_t* xq, const float* xd,
+                            int n_tok, int8_t* xq_out, float* xd_out, sd_stream_t stream) {
+  if (!w || !xq || !xd || !xq_out || !xd_out) return SD_EINVAL;
+  if (n_tok < 1 || n_tok > SD_MAX_TOKENS || F < 32 || F > ((int64_t)1 << 29) || K < 1) return SD_EINVAL;
+  if (K % 256 != 0 || K > ((int64_t)1 << 24) || F % 32 != 0) return SD_EUNSUPPORTED;
+  if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(xd_out, 4)) return SD_EALIGN;
+  if (!swiglu_fusable(F, K, n_tok)) return SD_EUNSUPPORTED;  // beyond the one-chunk staged kernel
+  return from_hip(launch_qgemv_swiglu(w, F, K, xq, xd, n_tok, xq_out, xd_out, hs(stream)));
+}
+
 int sd_embed_f16(const uint16_t* table, int64_t V, int64_t H, const int32_t* tokens, int n_tok,
                  float* x, sd_stream_t stream) {
   if (!table || !tokens || !x || V < 1 || H < 1 || n_tok < 1 || n_tok > 65535) return SD_EINVAL;

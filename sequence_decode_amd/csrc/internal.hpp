@@ -93,6 +93,10 @@ bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan);
 hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
                         int n_tok, const float* residual, float* y, int64_t ldy, hipStream_t st,
                         int path = SD_GEMV_AUTO);
+// gate|up projection fused with SwiGLU + q8 quantization (see qgemv.hip)
+bool swiglu_fusable(int64_t F, int64_t K, int n_tok);
+hipError_t launch_qgemv_swiglu(const void* w, int64_t F, int64_t K, const int8_t* xq, const float* xd,
+                               int n_tok, int8_t* oq, float* od, hipStream_t st);
 
 hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok,
                               int64_t ld_head, const int32_t* pos, double theta, int n_rot,

@@ -235,11 +235,16 @@ __device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg
   return n;
 }
 
-template <int NT, int SP, int R, int NW, bool STAGE>
+// SWI (gate|up rows, one chunk, staged): instead of y, the kernel emits the
+// SwiGLU of its outputs as q8 blocks (oq, od), each block from one unit of 32
+// gate rows and the matching 32 up rows that one workgroup computes.
+template <int NT, int SP, int R, int NW, bool STAGE, bool SWI = false>
 __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd,
-    const float* residual, float* y, int64_t ldy, int S) {
+    const float* residual, float* y, int64_t ldy, int S, int8_t* __restrict__ oq,
+    float* __restrict__ od) {
+  static_assert(!SWI || (SP == 1 && R == 1 && NW == 8 && STAGE), "SwiGLU output: one chunk, staged");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   // chunk sums of the last kTable items, [item % kTable][wave][row * NT + token];
   // written without barriers (one row per item), combined and stored every
@@ -261,21 +266,34 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   uint8_t* stage = lds_dyn + NW * (kRing * R * SEG);
   const int nb = 2 * P;
 
-  // item k of slot sl covers rows (blockIdx.x + k * gridDim.x) * SLOTS * R + sl * R + [0, R)
+  // item k of slot sl covers rows (blockIdx.x + k * gridDim.x) * SLOTS * R + sl * R + [0, R);
+  // with SWI, unit u = blockIdx.x + (k / 8) * gridDim.x, and local row
+  // lr = 8 (k % 8) + sl is gate row 32u + lr (lr < 32) or up row F + 32u + lr - 32
   const int stride = (int)gridDim.x * SLOTS * R;
   const int row0 = (int)blockIdx.x * SLOTS * R;
-  const int iters = (N - row0 + stride - 1) / stride;  // uniform in the workgroup
+  const int F = N / 2;
+  const int units = F / 32;
+  const int iters = SWI ? ((int)blockIdx.x < units ? 8 * ((units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) : 0)
+                        : (N - row0 + stride - 1) / stride;  // uniform in the workgroup
+  auto row_of = [&](int k) {
+    if constexpr (SWI) {
+      const int u = (int)blockIdx.x + (k >> 3) * (int)gridDim.x;
+      const int lr = ((k & 7) << 3) + slot;
+      return lr < 32 ? 32 * u + lr : F + 32 * u + lr - 32;
+    }
+    return row0 + k * stride + slot * R;
+  };
 
   // DMA instructions this wave issues for item k
   auto ins_of = [&](int k) {
     if (k >= iters || seg_bytes == 0) return 0;
-    const int r0 = row0 + k * stride + slot * R;
+    const int r0 = row_of(k);
     const int nr = min(R, N - r0);
     return nr > 0 ? nr * n_ins : 0;
   };
   auto issue = [&](int k) {
     if (ins_of(k) == 0) return;
-    const int r0 = row0 + k * stride + slot * R;
+    const int r0 = row_of(k);
     uint8_t* l = ring + (k % kRing) * (R * SEG);
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -398,12 +416,18 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   for (int k = 0; k < iters; ++k) {
     issue(k + kRing - 1);
     // wait for item k: the only VMEM operations younger than its DMAs are the
-    // DMAs of the items issued after it (no global store happens in the loop)
+    // DMAs of the items issued after it (and, with SWI, the block stores below;
+    // no other global store happens in the loop)
     int younger = 0;
 #pragma unroll
     for (int d = 1; d < kRing; ++d) younger += ins_of(k + d);
+    if constexpr (SWI) {
+      // the previous unit's block stores (a code and a scale store in each
+      // wave that holds a (token, dim) of it) came after this item's DMAs
+      if (k > 0 && (k & 7) == 0 && wave * 64 < NT * 32) younger += 2;
+    }
     wait_vmcnt_rt(younger);
-    const int r0 = row0 + k * stride + slot * R;
+    const int r0 = row_of(k);
     const uint8_t* st = ring + (k % kRing) * (R * SEG);
     float v[R][NT];
 #pragma unroll
@@ -433,12 +457,37 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < NT; ++t) table[k % kTable][wave][r * NT + t] = v[r][t];
-    if (k - kb == kTable - 1) {
+    if constexpr (SWI) {
+      if ((k & 7) == 7) {
+        // the unit's 64 rows are in the table: m = silu(g) * u for 32 dims and
+        // every token, quantized as one q8 block per token (32 lanes each).
+        // LDS-only barrier: the weights of the next items stay in flight.  A
+        // later item reuses these table entries only after two more such
+        // barriers, which every reader here reaches first.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int u = (int)blockIdx.x + (k >> 3) * (int)gridDim.x;
+        if ((int)threadIdx.x < NT * 32) {
+          const int t = threadIdx.x >> 5;
+          const int i = threadIdx.x & 31;
+          const int kb8 = k - 7;
+          const float g = table[(kb8 + (i >> 3)) % kTable][i & 7][t];
+          const float up = table[(kb8 + 4 + (i >> 3)) % kTable][i & 7][t];
+          const float silu = fdiv(g, fadd(1.0f, expf(-g)));
+          const float m = fmul(silu, up);
+          const float amax = group_max<32>(fabsf(m));
+          const float d = q8_scale(amax);
+          oq[(int64_t)t * F + 32 * u + i] = (int8_t)q8_code(m, d);
+          if (i == 0) od[(int64_t)t * units + u] = d;
+        }
+      }
+    } else if (k - kb == kTable - 1) {
       flush(kb, kTable);
       kb = k + 1;
     }
   }
-  if (kb < iters) flush(kb, iters - kb);
+  if constexpr (!SWI) {
+    if (kb < iters) flush(kb, iters - kb);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -777,20 +826,21 @@ hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, 
   return hipGetLastError();
 }
 
-template <int NT, int SP, int NW, bool STAGE>
+template <int NT, int SP, int NW, bool STAGE, bool SWI = false>
 hipError_t launch_dma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
-                      const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st) {
+                      const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st,
+                      int8_t* oq = nullptr, float* od = nullptr) {
   constexpr int R = dma_rows(NT);
   static bool lds_raised = false;  // rings and staged activations take up to 140 KiB
   if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
+  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
-                     xq, K, xd, residual, y, ldy, pl.chunks);
+                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od);
   return hipGetLastError();
 }
 
@@ -920,6 +970,36 @@ hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, c
   case n: return launch_lds<n, lds_rows(n)>(pl, w, N, K, xq, xd, residual, y, ldy, st);
     SD_CASE(1) SD_CASE(2) SD_CASE(3) SD_CASE(4) SD_CASE(5) SD_CASE(6) SD_CASE(7) SD_CASE(8)
     SD_CASE(9) SD_CASE(10) SD_CASE(11) SD_CASE(12) SD_CASE(13) SD_CASE(14) SD_CASE(15) SD_CASE(16)
+#undef SD_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The gate|up projection (N = 2F rows: gate rows, then up rows) with the
+// SwiGLU of its outputs quantized in the same launch: oq / od get exactly what
+// launch_swiglu_q8 would make of the projection's outputs.  Needs the staged
+// one-chunk streaming kernel (n_tok <= 8, K <= 4096) and F % 32 == 0; else
+// hipErrorInvalidValue and nothing is launched.
+bool swiglu_fusable(int64_t F, int64_t K, int n_tok) {
+  GemvPlan pl;
+  if (F < 32 || F % 32 != 0 || F > ((int64_t)1 << 29)) return false;
+  if (!plan_qgemv(2 * F, K, n_tok, SD_GEMV_NARROW, &pl)) return false;
+  return pl.use_reg && pl.stage && pl.sp == 1;
+}
+
+hipError_t launch_qgemv_swiglu(const void* w, int64_t F, int64_t K, const int8_t* xq, const float* xd,
+                               int n_tok, int8_t* oq, float* od, hipStream_t st) {
+  if (!swiglu_fusable(F, K, n_tok)) return hipErrorInvalidValue;
+  GemvPlan pl;
+  plan_qgemv(2 * F, K, n_tok, SD_GEMV_NARROW, &pl);
+  // one unit (32 gate rows and their 32 up rows, 8 items per wave) at a time
+  const int64_t units = F / 32;
+  const int64_t per = (units + 255) / 256;
+  pl.grid = (int)((units + per - 1) / per);
+  switch (n_tok) {
+#define SD_CASE(n) \
+  case n: return launch_dma<n, 1, 8, true, true>(pl, w, 2 * F, K, xq, xd, nullptr, nullptr, 0, st, oq, od);
+    SD_CASE(1) SD_CASE(2) SD_CASE(3) SD_CASE(4) SD_CASE(5) SD_CASE(6) SD_CASE(7) SD_CASE(8)
 #undef SD_CASE
     default: return hipErrorInvalidValue;
   }

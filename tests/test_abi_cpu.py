@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 5
+    assert L.sd_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -66,6 +66,20 @@ def test_gemv_path_rejections(L):
         assert g(FAKE, 64, 256, FAKE, FAKE, 17, None, FAKE, 64, path, None) == SD_EINVAL
         assert g(FAKE, 64, 4000, FAKE, FAKE, 1, None, FAKE, 64, path, None) == SD_EUNSUPPORTED
         assert g(ODD, 64, 256, FAKE, FAKE, 1, None, FAKE, 64, path, None) == SD_EALIGN
+
+
+def test_gemv_swiglu_rejections(L):
+    f = L.sd_qgemv_q8_0_swiglu_q8
+    assert f(None, 64, 256, FAKE, FAKE, 1, FAKE, FAKE, None) == SD_EINVAL
+    assert f(FAKE, 64, 256, FAKE, FAKE, 0, FAKE, FAKE, None) == SD_EINVAL
+    assert f(FAKE, 64, 256, FAKE, FAKE, 1, None, FAKE, None) == SD_EINVAL
+    assert f(FAKE, 16, 256, FAKE, FAKE, 1, FAKE, FAKE, None) == SD_EINVAL
+    assert f(FAKE, 48, 256, FAKE, FAKE, 1, FAKE, FAKE, None) == SD_EUNSUPPORTED    # F % 32
+    assert f(FAKE, 64, 4000, FAKE, FAKE, 1, FAKE, FAKE, None) == SD_EUNSUPPORTED   # K % 256
+    assert f(FAKE, 64, 8192, FAKE, FAKE, 4, FAKE, FAKE, None) == SD_EUNSUPPORTED   # two chunks
+    assert f(FAKE, 64, 4096, FAKE, FAKE, 9, FAKE, FAKE, None) == SD_EUNSUPPORTED   # > 8 tokens
+    assert f(ODD, 64, 256, FAKE, FAKE, 1, FAKE, FAKE, None) == SD_EALIGN
+    assert f(FAKE, 64, 256, ODD, FAKE, 1, FAKE, FAKE, None) == SD_EALIGN
 
 
 def test_quantize_rejections(L):

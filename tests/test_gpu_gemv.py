@@ -218,3 +218,22 @@ def test_gemv_repeat_determinism(sd):
     first = _run_gemv(sd, bdev, N, K, xq, xd)
     for _ in range(50):
         assert np.array_equal(bits(_run_gemv(sd, bdev, N, K, xq, xd)), bits(first))
+
+
+@pytest.mark.parametrize("F,K", [(32, 256), (800, 1024), (768, 512), (14336, 4096)])
+def test_gemv_swiglu_fused_equals_chain(sd, F, K):
+    """The gate|up projection with SwiGLU in one launch gives exactly the codes
+    and scales of the projection followed by sd_swiglu_q8, at every width the
+    fused kernel takes (1 unit, ragged unit counts over the grid, the FFN)."""
+    say(f"gemv+swiglu F={F} K={K}")
+    blob, x = _case(900 + F + K, 2 * F, K, 8)
+    rq, rd = oracle.quantize_q8_act(x)
+    bdev = dev(blob)
+    for n in range(1, 9):
+        xq, xd = dev(rq[:n]), dev(rd[:n])
+        oq, od = sd.qgemv_q8_0_swiglu_q8(bdev, F, K, xq, xd)
+        gu = sd.qgemv_q8_0_batch(bdev, 2 * F, K, xq, xd)
+        cq, cd = sd.swiglu_q8(gu, F)
+        assert np.array_equal(host(oq), host(cq)), n
+        assert np.array_equal(bits(host(od)), bits(host(cd))), n
+

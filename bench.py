@@ -534,7 +534,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": round(tb / launches),
-                     "kernel": f"k_qgemv_q8_0_dma<{n}, SP, 1, NW, STAGE> (QKV, O, gate|up: SP=1, 8 waves, staged; down: SP=4, 4 waves)", "launches": launches,
+                     "kernel": f"k_qgemv_q8_0_dma<{n}, SP, 1, NW, STAGE, false> (QKV, O, gate|up: SP=1, 8 waves, staged; down: SP=4, 4 waves)", "launches": launches,
                      "launch_floor_us": round(floor, 3),
                      "avg_launch_us": round(tms / launches * 1e3, 3), "per_shape": per_shape},
     }

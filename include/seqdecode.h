@@ -341,7 +341,8 @@ int sd_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F,
  * never written.
  *   w       q8_0 [2F][K]: F gate rows, then F up rows (as sd_qgemv_q8_0_batch).
  *   xq, xd  q8 activations of n_tok tokens (as sd_qgemv_q8_0_batch).
- *   xq_out  [n_tok][F] int8; xd_out [n_tok][F/32] fp32.
+ *   xq_out  [n_tok][F] int8; xd_out [n_tok][F/32] fp32.  Neither may overlap
+ *           xq or xd: workgroups still read the activations while others write.
  * Requires 1 <= n_tok <= 8, K % 256 == 0, K <= 4096, F % 32 == 0,
  * 32 <= F <= 2^29; otherwise SD_EINVAL / SD_EUNSUPPORTED and nothing runs.
  */

@@ -461,9 +461,9 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
       if ((k & 7) == 7) {
         // the unit's 64 rows are in the table: m = silu(g) * u for 32 dims and
         // every token, quantized as one q8 block per token (32 lanes each).
-        // LDS-only barrier: the weights of the next items stay in flight.  A
-        // later item reuses these table entries only after two more such
-        // barriers, which every reader here reaches first.
+        // LDS-only barrier: the weights of the next items stay in flight.  The
+        // table entries read here are rewritten only 4 units later, after
+        // this barrier's successors, which every reader here reaches first.
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const int u = (int)blockIdx.x + (k >> 3) * (int)gridDim.x;
         if ((int)threadIdx.x < NT * 32) {

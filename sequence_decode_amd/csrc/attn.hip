@@ -59,6 +59,13 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) s4* lds_s4_ptr;
 
+// Cache policy of the V DMAs: non-temporal (nt).  In a decode step a layer's
+// cache is read once between the rest of the model's bytes (several GB), so
+// the 256 MB Infinity Cache never serves it again; with nt the four ragged
+// contexts' step runs about 1.5% faster.  (K stays on the default policy: nt
+// there gained nothing more.)
+constexpr int kVCpol = 2;
+
 __device__ __forceinline__ float cross_row_max(float v) {
   auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
                                             __builtin_bit_cast(uint32_t, v), false, false);
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       const int r = 8 * i + (lane >> 3);
       const int seg = (lane & 7) ^ vswz8(r);
       const int8_t* row = vbase + vrow(wk + r) * A.ld_tok;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * seg), (lds_ptr)(vw + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * seg), (lds_ptr)(vw + i * 1024), 16, 0, kVCpol);
     }
   }
   u32x4a ka[4][4];   // fp16 caches: 8 dims per (tile, block)
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
         const int r = 4 * i + (lane >> 4);
         const int piece = (lane & 15) ^ (2 * vswz(r));
         const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, kVCpol);
       }
     } else {
       const int prow0 = (j0 + jlo) % A.ring_cap;
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
         const int piece = (lane & 15) ^ (2 * vswz(r));
         const int jl = min(max(jv + 4 * i, jlo), nk - 1);
         const uint8_t* row = reinterpret_cast<const uint8_t*>(vbase + (int64_t)krow(prow0, jl) * A.ld_tok);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, kVCpol);
       }
     }
   };

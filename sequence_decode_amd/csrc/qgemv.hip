@@ -213,6 +213,12 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Cache policy of the weight DMAs: non-temporal (nt).  Each weight byte is
+// read once per pass and a model's weights are many times the 256 MB
+// Infinity Cache, so keeping them there buys nothing; with nt the 8B-class
+// sweep streams 4-5% faster at 1-4 tokens (same bytes, same outputs).
+constexpr int kWeightCpol = 2;
+
 // Issues the DMA of one chunk segment (seg_bytes <= 4352) of one row.  A full
 // segment is 4 whole 1 KiB instructions plus one for lanes 0..15; a shorter
 // (last) segment is cut at the lane granularity.  Returns the instructions issued.
@@ -221,17 +227,17 @@ __device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + j * 1024 + lane * 16),
-                                       (lds_ptr)(l + j * 1024), 16, 0, 0);
+                                       (lds_ptr)(l + j * 1024), 16, 0, kWeightCpol);
     if (lane < 16)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + 4096 + lane * 16),
-                                       (lds_ptr)(l + 4096), 16, 0, 0);
+                                       (lds_ptr)(l + 4096), 16, 0, kWeightCpol);
     return 5;
   }
   const int n = (seg_bytes + 1023) / 1024;
   for (int j = 0; j < n; ++j)
     if (j * 1024 + lane * 16 < seg_bytes)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + j * 1024 + lane * 16),
-                                       (lds_ptr)(l + j * 1024), 16, 0, 0);
+                                       (lds_ptr)(l + j * 1024), 16, 0, kWeightCpol);
   return n;
 }
 

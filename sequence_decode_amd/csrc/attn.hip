@@ -588,57 +588,99 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
   const float* base =
       part + ((int64_t)A.partial_begin + ((int64_t)t * H_q + h) * A.n_chunks + (lo / C - A.c0)) * PF;
 
-  // maximum of the chunk maxima (exact, order-free)
-  float mx = -INFINITY;
-  for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, base[(int64_t)c * PF]);
-  mx = group_max<64>(mx);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
-  // weights, and L by a fixed tree: thread partials over c = tid, tid+256, ...
-  float lp = 0.0f;
-  for (int c = tid; c < nc; c += 256) {
-    const float w = expf(fsub(base[(int64_t)c * PF], M));
-    s_w[c] = w;
-    lp = fadd(lp, fmul(base[(int64_t)c * PF + 1], w));
-  }
-  lp = wave_sum_fixed(lp);
-  if ((tid & 63) == 0) s_red[tid >> 6] = lp;
-  __syncthreads();
-  const float L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
-  // values: eight interleaved groups of chunks (group j: chunks j, j+8, ...),
-  // each summed in chunk order by 32 threads of 4 dims (one 16-byte load per
-  // chunk, 16 chunks in flight), then the groups added by a fixed tree
-  {
-    const int j = tid >> 5;          // chunk group
-    const int d4 = (tid & 31) * 4;   // dims d4 .. d4+3
+  float L;
+  const int j = tid >> 5;         // chunk group of the value sums
+  const int d4 = (tid & 31) * 4;  // dims d4 .. d4+3
+  if (nc <= 8 * 16) {
+    // Up to 128 chunks (32768 keys): every load is issued up front, (m, l) of
+    // chunk tid and the values of chunks j, j + 8, ..., so the merge waits for
+    // memory once.  Loads past the last chunk read chunk nc - 1 and are never
+    // used; the sums below are those of the general path, term for term.
+    const float* mlp = base + (int64_t)min(tid, nc - 1) * PF;
+    const float m_c = mlp[0], l_c = mlp[1];
+    f32x4 a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      a[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(j + 8 * i, nc - 1) * PF + 4 + d4);
+    float mx = group_max<64>(tid < nc ? m_c : -INFINITY);
+    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    float lp = 0.0f;
+    if (tid < nc) {
+      const float w = expf(fsub(m_c, M));
+      s_w[tid] = w;
+      lp = fadd(lp, fmul(l_c, w));
+    }
+    lp = wave_sum_fixed(lp);
+    if ((tid & 63) == 0) s_red[tid >> 6] = lp;
+    __syncthreads();
+    L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    int c = j;
-    for (; c + 8 * 15 < nc; c += 8 * 16) {
-      f32x4 a[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)(c + 8 * i) * PF + 4 + d4);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float w = s_w[c + 8 * i];
+    for (int i = 0; i < 16; ++i) {
+      if (j + 8 * i < nc) {
+        const float w = s_w[j + 8 * i];
         acc.x = fadd(acc.x, fmul(a[i].x, w));
         acc.y = fadd(acc.y, fmul(a[i].y, w));
         acc.z = fadd(acc.z, fmul(a[i].z, w));
         acc.w = fadd(acc.w, fmul(a[i].w, w));
       }
     }
-    for (; c < nc; c += 8) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(base + (int64_t)c * PF + 4 + d4);
-      const float w = s_w[c];
-      acc.x = fadd(acc.x, fmul(a.x, w));
-      acc.y = fadd(acc.y, fmul(a.y, w));
-      acc.z = fadd(acc.z, fmul(a.z, w));
-      acc.w = fadd(acc.w, fmul(a.w, w));
-    }
     *reinterpret_cast<f32x4*>(s_o + j * HD + d4) = acc;
+    __syncthreads();
+  } else {
+    // maximum of the chunk maxima (exact, order-free)
+    float mx = -INFINITY;
+    for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, base[(int64_t)c * PF]);
+    mx = group_max<64>(mx);
+    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    // weights, and L by a fixed tree: thread partials over c = tid, tid+256, ...
+    float lp = 0.0f;
+    for (int c = tid; c < nc; c += 256) {
+      const float w = expf(fsub(base[(int64_t)c * PF], M));
+      s_w[c] = w;
+      lp = fadd(lp, fmul(base[(int64_t)c * PF + 1], w));
+    }
+    lp = wave_sum_fixed(lp);
+    if ((tid & 63) == 0) s_red[tid >> 6] = lp;
+    __syncthreads();
+    L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
+    // values: eight interleaved groups of chunks (group j: chunks j, j+8, ...),
+    // each summed in chunk order by 32 threads of 4 dims (one 16-byte load per
+    // chunk, 16 chunks in flight), then the groups added by a fixed tree
+    {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      int c = j;
+      for (; c + 8 * 15 < nc; c += 8 * 16) {
+        f32x4 a[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)(c + 8 * i) * PF + 4 + d4);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float w = s_w[c + 8 * i];
+          acc.x = fadd(acc.x, fmul(a[i].x, w));
+          acc.y = fadd(acc.y, fmul(a[i].y, w));
+          acc.z = fadd(acc.z, fmul(a[i].z, w));
+          acc.w = fadd(acc.w, fmul(a[i].w, w));
+        }
+      }
+      for (; c < nc; c += 8) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(base + (int64_t)c * PF + 4 + d4);
+        const float w = s_w[c];
+        acc.x = fadd(acc.x, fmul(a.x, w));
+        acc.y = fadd(acc.y, fmul(a.y, w));
+        acc.z = fadd(acc.z, fmul(a.z, w));
+        acc.w = fadd(acc.w, fmul(a.w, w));
+      }
+      *reinterpret_cast<f32x4*>(s_o + j * HD + d4) = acc;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (tid < HD) {
     const int d = tid;
     const float* g8 = s_o + d;

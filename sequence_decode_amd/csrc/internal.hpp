@@ -109,7 +109,7 @@ hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_n
 // n_rot dims of each head rotate.
 hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int rows, int n_heads, int n_kv,
                                int head_dim, int n_rot, const int32_t* pos, double theta,
-                               const SeqArgs& seqs, hipStream_t st);
+                               const SeqArgs& seqs, float* cs_tab, int tab_mode, hipStream_t st);
 
 // Fills per-sequence chunk bookkeeping (n_new must be set); returns workspace
 // floats needed.

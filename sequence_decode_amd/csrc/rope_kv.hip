@@ -104,21 +104,39 @@ __global__ __launch_bounds__(128) void k_kv_append_q8(const float* __restrict__ 
 // g = h - n_heads and writes it, with value head g, into the cache row of the
 // row's position.  Only the last n_rot dims of a head rotate (the same pairs
 // and angles as k_rope_posvec); the others pass through.
+//
+// The angles depend on the positions alone, which every layer of a step shares:
+// with tab_mode 1 the kernel takes them from rope_angle and workgroup h = 0
+// keeps them in cs_tab ([row][pair] as (cos, sin)); with tab_mode 2 it reads
+// them back from there (the first layer writes, the later ones read).  The
+// stored values are the fp32 results themselves, so every mode rotates with
+// the same bits.
 __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv, int n_heads,
                                                      int n_kv, int head_dim, int n_rot,
                                                      const int32_t* __restrict__ pos,
-                                                     double theta, SeqArgs seqs) {
+                                                     double theta, SeqArgs seqs,
+                                                     float2* cs_tab, int tab_mode) {
   const int t = blockIdx.x;
   const int h = blockIdx.y;
   const int off = head_dim - n_rot;
   const int half = n_rot / 2;
   const int p = pos[t];
   float* row = qkv + (int64_t)t * ld_qkv;
+  auto angle = [&](int i, float* c, float* s) {
+    if (tab_mode == 2) {
+      const float2 cs = cs_tab[(int64_t)t * half + i];
+      *c = cs.x;
+      *s = cs.y;
+      return;
+    }
+    rope_angle(p, i, n_rot, theta, c, s);
+    if (tab_mode == 1 && h == 0) cs_tab[(int64_t)t * half + i] = make_float2(*c, *s);
+  };
   if (h < n_heads) {
     float* v = row + (int64_t)h * head_dim + off;
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
-      rope_angle(p, i, n_rot, theta, &c, &s);
+      angle(i, &c, &s);
       rotate(v[i], v[i + half], c, s, &y0, &y1);
       v[i] = y0;
       v[i + half] = y1;
@@ -139,7 +157,7 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
       __shared__ float s_k[kAttnHeadDim];
       for (int i = threadIdx.x; i < half; i += blockDim.x) {
         float c, s, y0, y1;
-        rope_angle(p, i, n_rot, theta, &c, &s);
+        angle(i, &c, &s);
         rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
         s_k[off + i] = y0;
         s_k[off + i + half] = y1;
@@ -155,7 +173,7 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
     }
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
-      rope_angle(p, i, n_rot, theta, &c, &s);
+      angle(i, &c, &s);
       rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
       a.k_w[dst + off + i] = f32_to_f16_bits(y0);
       a.k_w[dst + off + i + half] = f32_to_f16_bits(y1);
@@ -189,9 +207,10 @@ hipError_t launch_kv_append(const float* k_new, const float* v_new, int64_t ld_n
 
 hipError_t launch_rope_kv_step(float* qkv, int64_t ld_qkv, int rows, int n_heads, int n_kv,
                                int head_dim, int n_rot, const int32_t* pos, double theta,
-                               const SeqArgs& seqs, hipStream_t st) {
+                               const SeqArgs& seqs, float* cs_tab, int tab_mode, hipStream_t st) {
   hipLaunchKernelGGL(k_rope_kv_step, dim3(rows, n_heads + n_kv), dim3(64), 0, st, qkv,
-                     ld_qkv, n_heads, n_kv, head_dim, n_rot, pos, theta, seqs);
+                     ld_qkv, n_heads, n_kv, head_dim, n_rot, pos, theta, seqs,
+                     reinterpret_cast<float2*>(cs_tab), tab_mode);
   return hipGetLastError();
 }
 

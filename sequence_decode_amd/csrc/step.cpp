@@ -22,7 +22,7 @@ namespace {
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct StepLayout {
-  size_t x, aq, ad, qkv, attn_o, gu, part, arg, total;
+  size_t x, aq, ad, qkv, attn_o, gu, part, arg, rope, total;
 };
 
 bool model_ok(const sd_model* m) {
@@ -57,6 +57,7 @@ StepLayout layout(const sd_model* m, int n, int max_ctx) {
   L.gu = off;     off = align_up(off + (size_t)n * 2 * m->ffn * 4, 256);
   L.part = off;   off = align_up(off + (size_t)n * chunks * m->n_heads * kAttnPartialFloats * 4, 256);
   L.arg = off;    off = align_up(off + argmax_ws_bytes(n, m->vocab), 256);
+  L.rope = off;   off = align_up(off + (size_t)n * (m->head_dim / 2) * 8, 256);
   L.total = off;
   return L;
 }
@@ -137,6 +138,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   float* attn_o = reinterpret_cast<float*>(ws + W.attn_o);
   float* gu = reinterpret_cast<float*>(ws + W.gu);
   float* part = reinterpret_cast<float*>(ws + W.part);
+  float* rope_tab = reinterpret_cast<float*>(ws + W.rope);  // (cos, sin) per row and pair
 
   const int H = m->hidden, Hq = m->n_heads, Hkv = m->n_kv_heads, D = m->head_dim, F = m->ffn;
   const int64_t QKV = (int64_t)(Hq + 2 * Hkv) * D;
@@ -195,7 +197,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
     SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
     SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, m->n_rot ? m->n_rot : D, io->positions,
-                               m->rope_theta, sa, st));
+                               m->rope_theta, sa, rope_tab, l == 0 ? 1 : 2, st));
     SD_TRY(launch_attn(qkv, QKV, sa, Hq, Hkv, scale, attn_o, part, aq, ad, st));
     SD_TRY(launch_qgemv(L.w_o, H, HqD, aq, ad, n, x, x, H, st));
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));

@@ -241,6 +241,45 @@ __device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg
   return n;
 }
 
+// The fixed 64-lane tree of wave_sum_fixed for 2..4 token cells at once
+// (transposed butterfly).  At the first level (partners lane ^ 1) a lane keeps
+// two of the four tokens and hands the other two to its partner; at the
+// second (lane ^ 2) it keeps one.  Every addition combines the same two
+// subtree sums as wave_sum_fixed applied to each token, so each token's total
+// has the same bits, but the tree costs one pass instead of one per token.
+// Lane l ends with the total of token tree_token(l): the assignment repeats
+// every 8 lanes and is symmetric under l -> 7 - l, so the mirrored partners of
+// the later levels always hold the same token.  Tokens past NT are zeros whose
+// sums are never used.
+__device__ __forceinline__ int tree_token(int lane, int nt) {
+  const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
+  return nt == 2 ? (b0 ^ b2) : 2 * (b0 ^ b2) + (b1 ^ b2);
+}
+
+template <int NT>
+__device__ __forceinline__ float wave_sum_fixed_tr(const float (&v)[NT], int lane) {
+  static_assert(NT >= 2 && NT <= 4, "2..4 tokens");
+  const bool lo1 = ((lane ^ (lane >> 2)) & 1) == 0;  // keeps tokens {0, 1} (NT 2: token 0)
+  float e;
+  if constexpr (NT == 2) {
+    const float keep = lo1 ? v[0] : v[1];
+    const float send = lo1 ? v[1] : v[0];
+    e = fadd(keep, dpp_mov<0xB1>(send));
+    e = fadd(e, dpp_mov<0x4E>(e));
+  } else {
+    const float v3 = NT == 4 ? v[NT == 4 ? 3 : 0] : 0.0f;
+    const float k0 = lo1 ? v[0] : v[2], k1 = lo1 ? v[1] : v3;
+    const float s0 = lo1 ? v[2] : v[0], s1 = lo1 ? v3 : v[1];
+    const float a = fadd(k0, dpp_mov<0xB1>(s0));
+    const float b = fadd(k1, dpp_mov<0xB1>(s1));
+    const bool lo2 = (((lane >> 1) ^ (lane >> 2)) & 1) == 0;  // keeps the first of its pair
+    e = fadd(lo2 ? a : b, dpp_mov<0x4E>(lo2 ? b : a));
+  }
+  e = fadd(e, dpp_mov<0x141>(e));  // row_half_mirror
+  e = fadd(e, dpp_mov<0x140>(e));  // row_mirror
+  return cross_row_sum_fixed(e);
+}
+
 // SWI (gate|up rows, one chunk, staged): instead of y, the kernel emits the
 // SwiGLU of its outputs as q8 blocks (oq, od), each block from one unit of 32
 // gate rows and the matching 32 up rows that one workgroup computes.
@@ -454,15 +493,24 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
         for (int t = 0; t < NT; ++t) v[r][t] = 0.0f;
       }
     }
+    if constexpr (NT >= 2 && NT <= 4) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) v[r][t] = wave_sum_fixed(v[r][t]);
-    if (lane == 0)
+      for (int r = 0; r < R; ++r) {
+        const float tot = wave_sum_fixed_tr<NT>(v[r], lane);
+        const int tt = tree_token(lane, NT);
+        if (lane < (NT == 2 ? 2 : 4) && tt < NT) table[k % kTable][wave][r * NT + tt] = tot;
+      }
+    } else {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) table[k % kTable][wave][r * NT + t] = v[r][t];
+        for (int t = 0; t < NT; ++t) v[r][t] = wave_sum_fixed(v[r][t]);
+      if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) table[k % kTable][wave][r * NT + t] = v[r][t];
+    }
     if constexpr (SWI) {
       if ((k & 7) == 7) {
         // the unit's 64 rows are in the table: m = silu(g) * u for 32 dims and

@@ -241,27 +241,51 @@ __device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg
   return n;
 }
 
-// The fixed 64-lane tree of wave_sum_fixed for 2..4 token cells at once
+// The fixed 64-lane tree of wave_sum_fixed for 2..8 token cells at once
 // (transposed butterfly).  At the first level (partners lane ^ 1) a lane keeps
-// two of the four tokens and hands the other two to its partner; at the
-// second (lane ^ 2) it keeps one.  Every addition combines the same two
-// subtree sums as wave_sum_fixed applied to each token, so each token's total
-// has the same bits, but the tree costs one pass instead of one per token.
-// Lane l ends with the total of token tree_token(l): the assignment repeats
-// every 8 lanes and is symmetric under l -> 7 - l, so the mirrored partners of
-// the later levels always hold the same token.  Tokens past NT are zeros whose
-// sums are never used.
+// half of the tokens and hands the other half to its partner, at the second
+// (lane ^ 2) half of the rest, and with 5..8 tokens at the third (lane 7 - l
+// within 8) the last one.  Every addition combines the same two subtree sums
+// as wave_sum_fixed applied to each token, so each token's total has the same
+// bits, but the tree costs one pass instead of one per token.  Lane l ends
+// with the total of token tree_token(l).  The keep/hand-over choices are
+// parities of lane bits (b0 ^ b2, then b1 ^ b2, then b0 ^ b3), chosen so that
+// each level's partner holds the opposite choice at its own level and the same
+// at every other, and the mirrored partners of the later levels (7 - l, 15 - l)
+// hold the same token.  Tokens past NT are zeros whose sums are never used.
 __device__ __forceinline__ int tree_token(int lane, int nt) {
-  const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
-  return nt == 2 ? (b0 ^ b2) : 2 * (b0 ^ b2) + (b1 ^ b2);
+  const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
+  if (nt == 2) return b0 ^ b2;
+  if (nt <= 4) return 2 * (b0 ^ b2) + (b1 ^ b2);
+  return 4 * (b0 ^ b2) + 2 * (b1 ^ b2) + (b0 ^ b3);
 }
+
+// lanes whose totals are stored, one per token (tree_token of lanes 0 .. n-1)
+constexpr int tree_writers(int nt) { return nt == 2 ? 2 : (nt <= 4 ? 4 : 8); }
 
 template <int NT>
 __device__ __forceinline__ float wave_sum_fixed_tr(const float (&v)[NT], int lane) {
-  static_assert(NT >= 2 && NT <= 4, "2..4 tokens");
-  const bool lo1 = ((lane ^ (lane >> 2)) & 1) == 0;  // keeps tokens {0, 1} (NT 2: token 0)
+  static_assert(NT >= 2 && NT <= 8, "2..8 tokens");
+  const bool lo1 = ((lane ^ (lane >> 2)) & 1) == 0;  // keeps the first half of the tokens
   float e;
-  if constexpr (NT == 2) {
+  if constexpr (NT > 4) {
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = i < NT ? v[i < NT ? i : 0] : 0.0f;
+    float k[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      k[i] = fadd(lo1 ? w[i] : w[4 + i], dpp_mov<0xB1>(lo1 ? w[4 + i] : w[i]));
+    const bool lo2 = (((lane >> 1) ^ (lane >> 2)) & 1) == 0;  // keeps the first two of its four
+    float m[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      m[i] = fadd(lo2 ? k[i] : k[2 + i], dpp_mov<0x4E>(lo2 ? k[2 + i] : k[i]));
+    const bool lo3 = ((lane ^ (lane >> 3)) & 1) == 0;  // keeps the first of its two
+    e = fadd(lo3 ? m[0] : m[1], dpp_mov<0x141>(lo3 ? m[1] : m[0]));
+    e = fadd(e, dpp_mov<0x140>(e));  // row_mirror
+    return cross_row_sum_fixed(e);
+  } else if constexpr (NT == 2) {
     const float keep = lo1 ? v[0] : v[1];
     const float send = lo1 ? v[1] : v[0];
     e = fadd(keep, dpp_mov<0xB1>(send));
@@ -493,12 +517,12 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
         for (int t = 0; t < NT; ++t) v[r][t] = 0.0f;
       }
     }
-    if constexpr (NT >= 2 && NT <= 4) {
+    if constexpr (NT >= 2 && NT <= 8) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float tot = wave_sum_fixed_tr<NT>(v[r], lane);
         const int tt = tree_token(lane, NT);
-        if (lane < (NT == 2 ? 2 : 4) && tt < NT) table[k % kTable][wave][r * NT + tt] = tot;
+        if (lane < tree_writers(NT) && tt < NT) table[k % kTable][wave][r * NT + tt] = tot;
       }
     } else {
 #pragma unroll

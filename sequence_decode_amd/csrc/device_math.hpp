@@ -83,11 +83,29 @@ __device__ __forceinline__ float cross_row_sum_fixed(float v) {
 
 __device__ __forceinline__ float wave_sum_fixed(float v) { return cross_row_sum_fixed(row16_sum_fixed(v)); }
 
-// Maximum over a contiguous group of `width` lanes (exact and order-free).
+// Maximum over an aligned group of `width` (32 or 64) lanes, exact and
+// order-free, so any pairing gives the same result: the quad and row
+// patterns of the sums above (within 16 lanes), then the lanes 16 (and 32)
+// apart.  DPP and permlane moves stay in registers; a lane shuffle through
+// the LDS crossbar would cost a round trip per level.  Every lane of the group
+// must be active.
 template <int width>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = width / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  static_assert(width == 32 || width == 64, "groups of 32 or 64 lanes");
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  {
+    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  }
+  if constexpr (width == 64) {
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                              __builtin_bit_cast(uint32_t, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  }
   return v;
 }
 

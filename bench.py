@@ -194,28 +194,43 @@ def verify_widths(torch, sweep, steps):
 
 
 def cpu_baseline(torch, sweep, n_tok, budget_s):
-    import numpy as np
+    """The oracle's GEMV on host copies of the sweep's matrices: GB/s of
+    algorithmic bytes on all the threads OpenMP gives it (budget_s of oracle
+    time), and on one thread (a quarter of that budget)."""
     import oracle
-    done_bytes, t_used, layers = 0, 0.0, 0
     x = sweep.x[:n_tok].cpu().numpy()
     host = []  # host copies of the layers already visited (copies are not timed)
-    while t_used < budget_s:
-        for li, L in enumerate(sweep.w):
-            if li == len(host):
-                host.append({name: L[name].cpu().numpy() for name, _, _ in SHAPES})
-            for name, N, K in SHAPES:
-                q, d = oracle.quantize_q8_act(x[:, :K])
-                t0 = time.perf_counter()
-                oracle.qgemv_q8_0(host[li][name], N, K, q, d)
-                t_used += time.perf_counter() - t0
-                done_bytes += gemv_bytes(N, K, n_tok)
-            layers += 1
-            if t_used >= budget_s:
-                break
-    return {"value": round(done_bytes / t_used / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{layers} layer passes over the 32 layers (4 projections each) at "
-                      f"n_tok={n_tok}, {done_bytes / 1e9:.2f} GB of weights, {t_used:.1f} s"}
+
+    def run(budget):
+        done_bytes, t_used, layers = 0, 0.0, 0
+        while t_used < budget:
+            for li, L in enumerate(sweep.w):
+                if li == len(host):
+                    host.append({name: L[name].cpu().numpy() for name, _, _ in SHAPES})
+                for name, N, K in SHAPES:
+                    q, d = oracle.quantize_q8_act(x[:, :K])
+                    t0 = time.perf_counter()
+                    oracle.qgemv_q8_0(host[li][name], N, K, q, d)
+                    t_used += time.perf_counter() - t0
+                    done_bytes += gemv_bytes(N, K, n_tok)
+                layers += 1
+                if t_used >= budget:
+                    break
+        return done_bytes, t_used, layers
+
+    cores = oracle.num_threads()
+    b_all, t_all, l_all = run(budget_s)
+    oracle.set_num_threads(1)
+    try:
+        b_one, t_one, l_one = run(budget_s / 4)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(b_all / t_all / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{l_all} layer passes over the 32 layers (4 projections each) at "
+                      f"n_tok={n_tok}, {b_all / 1e9:.2f} GB of weights, {t_all:.1f} s",
+            "single_core": {"value": round(b_one / t_one / 1e9, 3), "unit": "GB/s", "cores": 1,
+                            "sample": f"{l_one} layer passes, {b_one / 1e9:.2f} GB of weights, "
+                                      f"{t_one:.1f} s"}}
 
 
 def decode_bench(torch, steps, warmup):

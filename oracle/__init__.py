@@ -30,6 +30,7 @@ def lib():
         P = ctypes.c_void_p
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = f64
         L.oracle_f16_decode.argtypes = [P, i64, P]
@@ -59,6 +60,11 @@ def _req(a, dtype):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops (for timing on fewer cores)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def f16_decode(bits: np.ndarray) -> np.ndarray:

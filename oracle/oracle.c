@@ -47,6 +47,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count of the oracle's later parallel loops (timing only; the
+ * arithmetic of every output does not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* IEEE binary16 -> double, decoded from its fields (exact). */
 double oracle_f16_to_f64(uint16_t h) {
   int sign = (h >> 15) & 1;

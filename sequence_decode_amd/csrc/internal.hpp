@@ -2,10 +2,13 @@
 // Not part of the public interface (include/seqdecode.h is).
 #pragma once
 
+#include <math.h>
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include "device_math.hpp"
 #include "seqdecode.h"
 
 namespace sd {
@@ -67,6 +70,37 @@ struct SeqArgs {
   int32_t n_seq;
 };
 
+// Angle pos * theta^(-2i/n_rot) of RoPE pair i, its cosine and sine in fp64,
+// rounded to fp32 (every RoPE kernel takes its angles from here).
+__device__ inline void rope_angle(int pos, int i, int n_rot, double theta, float* c, float* s) {
+  const double inv_freq = pow(theta, (double)(-2 * i) / (double)n_rot);
+  const double a = (double)pos * inv_freq;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// The rotation of one pair: four fp32 products and two sums, unfused.
+__device__ inline void rope_rotate(float x0, float x1, float c, float s, float* y0, float* y1) {
+  *y0 = fsub(fmul(x0, c), fmul(x1, s));
+  *y1 = fadd(fmul(x0, s), fmul(x1, c));
+}
+
+// QKV projection with RoPE and the fp16 KV write in its epilogue (the step's
+// fp16 caches, heads of 128 dims rotated whole).  tab_mode as in
+// launch_rope_kv_step: 1 computes the angles and keeps them in cs_tab
+// ([row][pair] (cos, sin)), 2 reads them from there.
+struct RopeArgs {
+  const int32_t* pos;
+  double theta;
+  float* cs_tab;
+  int32_t tab_mode;
+  int32_t n_heads;
+  int32_t n_kv;
+  SeqArgs seqs;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
 hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
@@ -97,6 +131,13 @@ hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, c
 bool swiglu_fusable(int64_t F, int64_t K, int n_tok);
 hipError_t launch_qgemv_swiglu(const void* w, int64_t F, int64_t K, const int8_t* xq, const float* xd,
                                int n_tok, int8_t* oq, float* od, hipStream_t st);
+// QKV projection (N = (n_heads + 2 n_kv) * 128 rows) with RoPE of q and k and
+// the fp16 K/V cache write in the same launch: the q rows of y and the cache
+// rows get exactly what launch_rope_kv_step makes of the plain projection's
+// outputs; the k and v rows of y stay unrotated, as there.
+bool qkv_rope_fusable(int64_t N, int64_t K, int n_tok);
+hipError_t launch_qgemv_qkv_rope(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
+                                 int n_tok, float* y, int64_t ldy, const RopeArgs& ra, hipStream_t st);
 
 hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok,
                               int64_t ld_head, const int32_t* pos, double theta, int n_rot,

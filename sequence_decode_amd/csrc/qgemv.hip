@@ -307,13 +307,19 @@ __device__ __forceinline__ float wave_sum_fixed_tr(const float (&v)[NT], int lan
 // SWI (gate|up rows, one chunk, staged): instead of y, the kernel emits the
 // SwiGLU of its outputs as q8 blocks (oq, od), each block from one unit of 32
 // gate rows and the matching 32 up rows that one workgroup computes.
-template <int NT, int SP, int R, int NW, bool STAGE, bool SWI = false>
+//
+// ROPE (QKV rows, one chunk, staged): item k of a workgroup takes the 8 rows
+// of pair group g = blockIdx.x + k * gridDim.x, head g / 16: slots 0..3 hold
+// rows 4 (g % 16) + 0..3 of the head and slots 4..7 their rotation partners
+// 64 rows on, so both halves of every RoPE pair meet in the workgroup's table.
+template <int NT, int SP, int R, int NW, bool STAGE, bool SWI = false, bool ROPE = false>
 __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd,
     const float* residual, float* y, int64_t ldy, int S, int8_t* __restrict__ oq,
-    float* __restrict__ od) {
+    float* __restrict__ od, RopeArgs ra) {
   static_assert(!SWI || (SP == 1 && R == 1 && NW == 8 && STAGE), "SwiGLU output: one chunk, staged");
+  static_assert(!ROPE || (SP == 1 && R == 1 && NW == 8 && STAGE && !SWI), "RoPE epilogue: one chunk, staged");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   // chunk sums of the last kTable items, [item % kTable][wave][row * NT + token];
   // written without barriers (one row per item), combined and stored every
@@ -344,14 +350,19 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   const int units = F / 32;
   const int iters = SWI ? ((int)blockIdx.x < units ? 8 * ((units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) : 0)
                         : (N - row0 + stride - 1) / stride;  // uniform in the workgroup
-  auto row_of = [&](int k) {
+  auto row_at = [&](int k, int sl) {
     if constexpr (SWI) {
       const int u = (int)blockIdx.x + (k >> 3) * (int)gridDim.x;
-      const int lr = ((k & 7) << 3) + slot;
+      const int lr = ((k & 7) << 3) + sl;
       return lr < 32 ? 32 * u + lr : F + 32 * u + lr - 32;
     }
-    return row0 + k * stride + slot * R;
+    if constexpr (ROPE) {
+      const int g = (int)blockIdx.x + k * (int)gridDim.x;
+      return 128 * (g >> 4) + 4 * (g & 15) + (sl < 4 ? sl : 60 + sl);
+    }
+    return row0 + k * stride + sl * R;
   };
+  auto row_of = [&](int k) { return row_at(k, slot); };
 
   // DMA instructions this wave issues for item k
   auto ins_of = [&](int k) {
@@ -463,6 +474,44 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     }
   }
 
+  // ROPE epilogue for output v of row `row`, token t, whose RoPE partner
+  // (64 rows away in the same head) has output pv: the arithmetic of
+  // k_rope_kv_step (same angles, same rotation, same fp16 rounding).
+  auto rope_out = [&](float v, float pv, int row, int t) {
+    const int hd = row >> 7, d = row & 127, ip = d & 63;
+    const bool lo = d < 64;
+    float r = v;
+    if (hd < ra.n_heads + ra.n_kv) {
+      float c, s;
+      if (ra.tab_mode == 2) {
+        c = ra.cs_tab[2 * (t * 64 + ip)];
+        s = ra.cs_tab[2 * (t * 64 + ip) + 1];
+      } else {
+        rope_angle(ra.pos[t], ip, 128, ra.theta, &c, &s);
+        if (ra.tab_mode == 1 && hd == 0 && lo) {
+          ra.cs_tab[2 * (t * 64 + ip)] = c;
+          ra.cs_tab[2 * (t * 64 + ip) + 1] = s;
+        }
+      }
+      float y0, y1;
+      rope_rotate(lo ? v : pv, lo ? pv : v, c, s, &y0, &y1);
+      r = lo ? y0 : y1;
+    }
+    y[(int64_t)t * ldy + row] = hd < ra.n_heads ? r : v;
+    if (hd >= ra.n_heads) {
+      int sq = 0;
+#pragma unroll
+      for (int i = 1; i < SD_MAX_SEQS; ++i)
+        if (i < ra.seqs.n_seq && t >= ra.seqs.s[i].row0) sq = i;
+      const SeqArg& a = ra.seqs.s[sq];
+      const int64_t crow = seq_row(a, a.ctx_len - a.n_new + (t - a.row0));
+      const bool is_k = hd < ra.n_heads + ra.n_kv;
+      const int g = hd - ra.n_heads - (is_k ? 0 : ra.n_kv);
+      uint16_t* dst = (is_k ? a.k_w : a.v_w) + crow * a.ld_tok + (int64_t)g * a.ld_head + d;
+      *dst = f32_to_f16_bits(r);
+    }
+  };
+
   // Combines and stores the outputs of items [kb, kb + cnt): each row gets its
   // chunk sums added in chunk order.
   auto flush = [&](int kb, int cnt) {
@@ -472,11 +521,15 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
       const int rem = i - ki * (SLOTS * R * NT);
       const int sl = rem / (R * NT);
       const int j = rem - sl * (R * NT);
-      const int row = row0 + (kb + ki) * stride + sl * R + j / NT;
+      const int row = row_at(kb + ki, sl) + j / NT;
       const int e = (kb + ki) % kTable;
       float tot = table[e][sl * SP][j];
       for (int c = 1; c < S; ++c) tot = fadd(tot, table[e][sl * SP + c][j]);
-      if (row < N) store_out(tot, row, j % NT, residual, y, ldy);
+      if constexpr (ROPE) {
+        if (row < N) rope_out(tot, table[e][sl ^ 4][j], row, j);
+      } else {
+        if (row < N) store_out(tot, row, j % NT, residual, y, ldy);
+      }
     }
     __syncthreads();
   };
@@ -904,21 +957,21 @@ hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, 
   return hipGetLastError();
 }
 
-template <int NT, int SP, int NW, bool STAGE, bool SWI = false>
+template <int NT, int SP, int NW, bool STAGE, bool SWI = false, bool ROPE = false>
 hipError_t launch_dma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                       const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st,
-                      int8_t* oq = nullptr, float* od = nullptr) {
+                      int8_t* oq = nullptr, float* od = nullptr, const RopeArgs* ra = nullptr) {
   constexpr int R = dma_rows(NT);
   static bool lds_raised = false;  // rings and staged activations take up to 140 KiB
   if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
+  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
-                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od);
+                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od, ra ? *ra : RopeArgs{});
   return hipGetLastError();
 }
 
@@ -1077,6 +1130,35 @@ hipError_t launch_qgemv_swiglu(const void* w, int64_t F, int64_t K, const int8_t
   switch (n_tok) {
 #define SD_CASE(n) \
   case n: return launch_dma<n, 1, 8, true, true>(pl, w, 2 * F, K, xq, xd, nullptr, nullptr, 0, st, oq, od);
+    SD_CASE(1) SD_CASE(2) SD_CASE(3) SD_CASE(4) SD_CASE(5) SD_CASE(6) SD_CASE(7) SD_CASE(8)
+#undef SD_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// QKV projection with RoPE of q and k and the fp16 K/V write (see
+// internal.hpp).  Needs the staged one-chunk streaming kernel (n_tok <= 8,
+// K <= 4096) and heads of 128 rows; else hipErrorInvalidValue and nothing is
+// launched.
+bool qkv_rope_fusable(int64_t N, int64_t K, int n_tok) {
+  GemvPlan pl;
+  if (N < 128 || N % 128 != 0 || N > ((int64_t)1 << 29)) return false;
+  if (!plan_qgemv(N, K, n_tok, SD_GEMV_NARROW, &pl)) return false;
+  return pl.use_reg && pl.stage && pl.sp == 1 && pl.chunks == 1;
+}
+
+hipError_t launch_qgemv_qkv_rope(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
+                                 int n_tok, float* y, int64_t ldy, const RopeArgs& ra, hipStream_t st) {
+  if (!qkv_rope_fusable(N, K, n_tok)) return hipErrorInvalidValue;
+  GemvPlan pl;
+  plan_qgemv(N, K, n_tok, SD_GEMV_NARROW, &pl);
+  // one pair group (8 rows) per item, as many items per workgroup as the plain launch
+  const int64_t groups = N / 8;
+  const int64_t per = (groups + 255) / 256;
+  pl.grid = (int)((groups + per - 1) / per);
+  switch (n_tok) {
+#define SD_CASE(n) \
+  case n: return launch_dma<n, 1, 8, true, false, true>(pl, w, N, K, xq, xd, nullptr, y, ldy, st, nullptr, nullptr, &ra);
     SD_CASE(1) SD_CASE(2) SD_CASE(3) SD_CASE(4) SD_CASE(5) SD_CASE(6) SD_CASE(7) SD_CASE(8)
 #undef SD_CASE
     default: return hipErrorInvalidValue;

@@ -22,21 +22,6 @@ namespace sd {
 
 namespace {
 
-__device__ __forceinline__ void rope_angle(int pos, int i, int n_rot, double theta, float* c,
-                                           float* s) {
-  const double inv_freq = pow(theta, (double)(-2 * i) / (double)n_rot);
-  const double a = (double)pos * inv_freq;
-  double sn, cs;
-  sincos(a, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn;
-}
-
-__device__ __forceinline__ void rotate(float x0, float x1, float c, float s, float* y0, float* y1) {
-  *y0 = fsub(fmul(x0, c), fmul(x1, s));
-  *y1 = fadd(fmul(x0, s), fmul(x1, c));
-}
-
 // Grid (n_tok * n_heads); threads loop over the n_rot/2 pairs of one head.
 __global__ __launch_bounds__(128) void k_rope_posvec(float* x, int n_heads, int head_dim,
                                                      int64_t ld_tok, int64_t ld_head,
@@ -50,7 +35,7 @@ __global__ __launch_bounds__(128) void k_rope_posvec(float* x, int n_heads, int 
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     float c, s, y0, y1;
     rope_angle(p, i, n_rot, theta, &c, &s);
-    rotate(v[i], v[i + half], c, s, &y0, &y1);
+    rope_rotate(v[i], v[i + half], c, s, &y0, &y1);
     v[i] = y0;
     v[i + half] = y1;
   }
@@ -137,7 +122,7 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
       angle(i, &c, &s);
-      rotate(v[i], v[i + half], c, s, &y0, &y1);
+      rope_rotate(v[i], v[i + half], c, s, &y0, &y1);
       v[i] = y0;
       v[i + half] = y1;
     }
@@ -158,7 +143,7 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
       for (int i = threadIdx.x; i < half; i += blockDim.x) {
         float c, s, y0, y1;
         angle(i, &c, &s);
-        rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
+        rope_rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
         s_k[off + i] = y0;
         s_k[off + i + half] = y1;
       }
@@ -174,7 +159,7 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
       float c, s, y0, y1;
       angle(i, &c, &s);
-      rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
+      rope_rotate(kh[off + i], kh[off + i + half], c, s, &y0, &y1);
       a.k_w[dst + off + i] = f32_to_f16_bits(y0);
       a.k_w[dst + off + i + half] = f32_to_f16_bits(y1);
     }

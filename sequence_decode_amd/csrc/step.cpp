@@ -176,6 +176,10 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     if ((call) != hipSuccess) return SD_EHIP; \
   } while (0)
 
+  // QKV projection, RoPE and K/V write as one launch where the streaming
+  // kernel allows it (fp16 caches, whole 128-dim heads rotated, 1..8 rows)
+  bool qkv_rope = D == 128 && (m->n_rot == 0 || m->n_rot == D) && qkv_rope_fusable(QKV, H, n);
+  for (int s = 0; s < n_seq; ++s) qkv_rope = qkv_rope && !sa.s[s].q8;
   SD_TRY(launch_embed(m->tok_embd, m->vocab, H, io->tokens, n, x, st));
   for (int l = 0; l < m->n_layers; ++l) {
     const sd_layer_weights& L = m->layers[l];
@@ -195,9 +199,15 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
       }
     }
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
-    SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
-    SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, m->n_rot ? m->n_rot : D, io->positions,
-                               m->rope_theta, sa, rope_tab, l == 0 ? 1 : 2, st));
+    if (qkv_rope) {
+      // RoPE and the fp16 K/V write in the projection's epilogue (one launch)
+      RopeArgs ra{io->positions, m->rope_theta, rope_tab, l == 0 ? 1 : 2, Hq, Hkv, sa};
+      SD_TRY(launch_qgemv_qkv_rope(L.w_qkv, QKV, H, aq, ad, n, qkv, QKV, ra, st));
+    } else {
+      SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
+      SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, m->n_rot ? m->n_rot : D, io->positions,
+                                 m->rope_theta, sa, rope_tab, l == 0 ? 1 : 2, st));
+    }
     SD_TRY(launch_attn(qkv, QKV, sa, Hq, Hkv, scale, attn_o, part, aq, ad, st));
     SD_TRY(launch_qgemv(L.w_o, H, HqD, aq, ad, n, x, x, H, st));
     SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));

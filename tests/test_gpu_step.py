@@ -189,19 +189,21 @@ def test_verify_step_equals_one_token_steps(sd, model, model_host):
         assert rel <= 1e-3, (i, rel)
 
 
-def test_window_rope_tail_step_vs_oracle_and_ring(sd):
-    """A model with a 100-position attention window and RoPE on the last 64 of
-    128 head dims: the step agrees with the oracle's step, and the same steps on
-    ring caches of window + 3 rows give bitwise the plain-cache logits, for
-    one-token steps and for a verify step."""
+@pytest.mark.parametrize("n_rot", [64, 128])
+def test_window_rope_tail_step_vs_oracle_and_ring(sd, n_rot):
+    """A model with a 100-position attention window and RoPE on the last n_rot
+    of 128 head dims (64: the separate RoPE/KV launch; 128: RoPE and the K/V
+    write in the QKV projection's epilogue): the step agrees with the oracle's
+    step, and the same steps on ring caches of window + 3 rows give bitwise the
+    plain-cache logits, for one-token steps and for a verify step."""
     import torch
-    say("window + rope tail step, ring == plain")
+    say(f"window + rope (n_rot {n_rot}) step, ring == plain")
     h = synth.model_host(3400, **DIMS)
-    h["n_rot"], h["window"] = 64, 100
+    h["n_rot"], h["window"] = n_rot, 100
     model = DecodeModel.from_host(h)
     m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
                     h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
-                    h["w_lm"], h["layers"], n_rot=64, window=100)
+                    h["w_lm"], h["layers"], n_rot=n_rot, window=100)
     ch = _caches_host(2, seed=3401)
     toks, pos = [3, 700], [150, 290]
     lg, nt, cs = _run(model, ch, toks, pos)

@@ -5,8 +5,10 @@
  * Every entry point enqueues HIP kernels on the caller's stream and returns
  * without synchronizing.  Pointers are DEVICE pointers unless marked [host].
  * The caller owns every buffer; the library allocates no device memory and
- * keeps no state between calls, so concurrent calls on different streams are
- * independent.
+ * keeps no device state between calls, so concurrent calls on different
+ * streams are independent.  Its only process state is each kernel's raised
+ * LDS limit, set once on a kernel's first launch under std::call_once (safe
+ * when several host threads make their first calls at once).
  *
  * Errors: arguments are validated on the host before any HIP call.  On failure
  * a negative sd_status is returned, nothing is launched and no output is

@@ -31,6 +31,9 @@
 // * Exact integer part.  A block dot is at most 32*127*127 in magnitude, an
 //   exact int32 and an exact fp32; s_b = (d_w * d_x) * isum is two fp32
 //   multiplies, never fused.
+#include <mutex>
+#include <type_traits>
+
 #include "device_math.hpp"
 #include "internal.hpp"
 
@@ -304,6 +307,12 @@ __device__ __forceinline__ float wave_sum_fixed_tr(const float (&v)[NT], int lan
   return cross_row_sum_fixed(e);
 }
 
+// Kernel argument of the RoPE epilogue: the whole RopeArgs (about 620 bytes)
+// only for the ROPE instantiation, an empty struct for every other launch.
+struct NoRope {};
+template <bool ROPE>
+using RopeParam = std::conditional_t<ROPE, RopeArgs, NoRope>;
+
 // SWI (gate|up rows, one chunk, staged): instead of y, the kernel emits the
 // SwiGLU of its outputs as q8 blocks (oq, od), each block from one unit of 32
 // gate rows and the matching 32 up rows that one workgroup computes.
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd,
     const float* residual, float* y, int64_t ldy, int S, int8_t* __restrict__ oq,
-    float* __restrict__ od, RopeArgs ra) {
+    float* __restrict__ od, RopeParam<ROPE> ra) {
   static_assert(!SWI || (SP == 1 && R == 1 && NW == 8 && STAGE), "SwiGLU output: one chunk, staged");
   static_assert(!ROPE || (SP == 1 && R == 1 && NW == 8 && STAGE && !SWI), "RoPE epilogue: one chunk, staged");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
@@ -478,6 +487,7 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   // (64 rows away in the same head) has output pv: the arithmetic of
   // k_rope_kv_step (same angles, same rotation, same fp16 rounding).
   auto rope_out = [&](float v, float pv, int row, int t) {
+   if constexpr (ROPE) {
     const int hd = row >> 7, d = row & 127, ip = d & 63;
     const bool lo = d < 64;
     float r = v;
@@ -510,6 +520,7 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
       uint16_t* dst = (is_k ? a.k_w : a.v_w) + crow * a.ld_tok + (int64_t)g * a.ld_head + d;
       *dst = f32_to_f16_bits(r);
     }
+   }
   };
 
   // Combines and stores the outputs of items [kb, kb + cnt): each row gets its
@@ -941,16 +952,24 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
   }
 }
 
+// Raises a kernel's dynamic LDS limit to kGemvLdsMax, once per kernel and
+// process (thread-safe: concurrent first calls wait for the one that sets it).
+template <auto Kern>
+hipError_t raise_lds_once() {
+  static std::once_flag once;
+  static hipError_t err = hipSuccess;
+  std::call_once(once, [] {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kGemvLdsMax);
+  });
+  return err;
+}
+
 hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                        const float* xd, int n_tok, const float* residual, float* y, int64_t ldy,
                        hipStream_t st) {
-  static bool lds_raised = false;  // up to 80 KiB of dynamic LDS
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_mfma),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // up to 80 KiB of dynamic LDS
+  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_mfma>(); e != hipSuccess) return e;
   hipLaunchKernelGGL(k_qgemv_q8_0_mfma, dim3(pl.grid), dim3(kMfmaThreads), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
                      xq, K, xd, n_tok, residual, y, ldy, pl.n_blocks);
@@ -962,29 +981,22 @@ hipError_t launch_dma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, c
                       const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st,
                       int8_t* oq = nullptr, float* od = nullptr, const RopeArgs* ra = nullptr) {
   constexpr int R = dma_rows(NT);
-  static bool lds_raised = false;  // rings and staged activations take up to 140 KiB
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // rings and staged activations take up to 140 KiB
+  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>>(); e != hipSuccess)
+    return e;
+  RopeParam<ROPE> rp{};
+  if constexpr (ROPE) rp = *ra;
   hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
-                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od, ra ? *ra : RopeArgs{});
+                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od, rp);
   return hipGetLastError();
 }
 
 template <int NT, int R>
 hipError_t launch_lds(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                       const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st) {
-  static bool lds_raised = false;  // allow more than 64 KiB of dynamic LDS (160 KiB on gfx950)
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qgemv_q8_0_lds<NT, R>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // allow more than 64 KiB of dynamic LDS (160 KiB on gfx950)
+  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_lds<NT, R>>(); e != hipSuccess) return e;
   hipLaunchKernelGGL((k_qgemv_q8_0_lds<NT, R>), dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
                      xq, K, xd, residual, y, ldy, pl.slice_pairs, pl.n_slices, pl.n_blocks);

@@ -10,6 +10,7 @@ rounded fp32 result, because fp64 carries more than 2*24+2 significand bits
 """
 from decimal import Decimal, getcontext
 from fractions import Fraction
+import cmath
 import math
 
 import numpy as np
@@ -156,3 +157,50 @@ def swiglu_decimal(g, u):
 
 def ulp32(v):
     return np.spacing(np.abs(np.asarray(v, np.float32)).astype(np.float32))
+
+
+# ------------------------------------------------------------ step composition
+
+def unpack_q8_0(blob, N, K):
+    """(codes int8 [N][K], fp16 scale bits uint16 [N][K/32]) of a q8_0 blob:
+    each 34-byte block is a little-endian fp16 scale then 32 int8 codes."""
+    b = np.asarray(blob, np.uint8).reshape(N, K // 32, 34)
+    bits = b[:, :, 0].astype(np.uint16) | (b[:, :, 1].astype(np.uint16) << 8)
+    codes = b[:, :, 2:].copy().view(np.int8).reshape(N, K)
+    return codes, bits
+
+
+def qgemv_exact_vec(codes, scale_bits, xq, xd, residual=None):
+    """qgemv_exact vectorized over rows and tokens: exact int64 block sums, then
+    emulated fp32 single operations in block order (same semantics)."""
+    N, K = codes.shape
+    nb = K // 32
+    n_tok = xq.shape[0]
+    c = codes.astype(np.int64).reshape(N, nb, 32)
+    x = xq.astype(np.int64).reshape(n_tok, nb, 32)
+    isum = np.einsum("nbi,tbi->tnb", c, x)              # exact integers
+    dw = scale_bits.view(np.float16).astype(np.float64)  # [N][nb], exact
+    acc = np.zeros((n_tok, N), np.float32)
+    for b in range(nb):
+        sc = (dw[None, :, b] * xd[:, b, None].astype(np.float64)).astype(np.float32)
+        s = (sc.astype(np.float64) * isum[:, :, b].astype(np.float64)).astype(np.float32)
+        acc = (acc.astype(np.float64) + s.astype(np.float64)).astype(np.float32)
+    if residual is not None:
+        acc = (residual.astype(np.float64) + acc.astype(np.float64)).astype(np.float32)
+    return acc
+
+
+def rope_complex(x, pos, theta, n_rot):
+    """x [n][H][D] -> copy whose last n_rot dims of every head are rotated:
+    dims (off + i, off + i + n_rot/2) form the complex number a + ib, multiplied
+    by e^{i pos theta^(-2i/n_rot)} (Python complex arithmetic), rounded to fp32."""
+    x = np.array(x, np.float32, copy=True)
+    n, H, Dd = x.shape
+    off, half = Dd - n_rot, n_rot // 2
+    for t in range(n):
+        for h in range(H):
+            for i in range(half):
+                ang = float(pos[t]) * float(theta) ** (-2.0 * i / n_rot)
+                z = complex(float(x[t, h, off + i]), float(x[t, h, off + i + half])) * cmath.exp(1j * ang)
+                x[t, h, off + i], x[t, h, off + i + half] = np.float32(z.real), np.float32(z.imag)
+    return x

@@ -185,7 +185,7 @@ def test_gemv_identical_rows_permutation_isolation(sd):
 
 def test_gemv_batch_layouts(sd):
     """All ordered selections of 1..4 rows from a pool of 8 (2,080 layouts)
-    against each row's solo output, plus 400 seeded layouts of 5..16 rows."""
+    against each row's solo output, plus 2,000 seeded layouts of 5..16 rows."""
     say("gemv layouts")
     N, K = 64, 512
     blob, x = _case(900, N, K, 8)
@@ -202,7 +202,7 @@ def test_gemv_batch_layouts(sd):
             count += 1
     assert count == 2080
     g = synth.rng(901)
-    for _ in range(400):
+    for _ in range(2000):
         n = int(g.integers(5, 17))
         s = list(g.integers(0, 8, n))
         y = _run_gemv(sd, bdev, N, K, xq[s].contiguous(), xd[s].contiguous())

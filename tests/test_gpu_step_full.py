@@ -1,0 +1,262 @@
+"""The decode step at its full size: 32 layers, hidden 4096, 32 query / 8 KV
+heads of 128 dims, FFN 14336, vocabulary 151,936, fp16 caches at the ragged
+contexts {2050, 3072, 16384, 32768}.
+
+The smaller step tests run a 2-layer, hidden-512 model, where the QKV
+projection with its RoPE/K/V epilogue gives every workgroup one item, the LM
+head has 1000 rows and no attention call spans more than a few chunks.  Here
+every launch has its real geometry:
+
+* batch invariance ("feat(qwen4exp): exact 4-slot concurrent serving",
+  "Tests": the N = 2/3/4 contract and the soak): each sequence's logits
+  [151936] and greedy tokens, over 8 fed-back steps, are bitwise those of the
+  sequence decoding alone, for 2, 3 and 4 sequences in two orders;
+* the widened verify step ("#1209 Speed up concurrent generation, fix QFUSE,
+  and improve prefill monitoring", "What changed and why", item 1): 4
+  sequences x 4 proposed tokens = 16 rows (matrix-core projections, unfused
+  SwiGLU) give for every row bitwise the logits of one-token steps taken one
+  after another over the same tokens;
+* agreement with the oracle's step on the first two layers of the same model
+  (full width, full vocabulary, the four ragged contexts);
+* the QKV projection with RoPE and the K/V write in its epilogue at the real
+  6144-row shape (768 pair groups, 3 per workgroup) on ring and paged caches:
+  bitwise the plain-cache step, and each verify row bitwise the one-token
+  steps.
+"""
+import numpy as np
+import pytest
+
+from helpers import say
+from sequence_decode_amd.step import DecodeModel, SeqCache, StepRunner
+
+pytestmark = pytest.mark.gpu
+
+FULL = dict(n_layers=32, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=14336,
+            vocab=151936, eps=1e-6, theta=1e6)
+CTX = [2050, 3072, 16384, 32768]
+STEPS = 8
+SPAN = 16
+
+
+def _same(a, b):
+    import torch
+    return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+
+
+@pytest.fixture(scope="module")
+def full(sd):
+    import torch
+    say("full-size model: 8.08 GB of q8_0 weights and 7.1 GB of fp16 caches on the device")
+    model = DecodeModel.random_device(11, FULL)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    caches = [SeqCache.random_device(g, FULL["n_layers"], c + SPAN, 8, 128) for c in CTX]
+    torch.cuda.synchronize()
+    yield model, caches
+    del model, caches
+    torch.cuda.empty_cache()
+
+
+def _decode(model, caches, order, first_tokens, steps):
+    """steps fed-back one-token steps of the sequences `order` (indices into
+    caches, CTX), starting at position CTX[s] - 1; returns per step the logits
+    rows and tokens (device clones), row i = sequence order[i]."""
+    import torch
+    r = StepRunner(model, [caches[s] for s in order], max_ctx=max(CTX) + SPAN)
+    r.tokens.copy_(torch.tensor([first_tokens[s] for s in order], dtype=torch.int32))
+    r.set_positions([CTX[s] - 1 for s in order])
+    out = []
+    for _ in range(steps):
+        r.step()
+        out.append((r.logits.clone(), r.next_tokens.clone()))
+        r.advance()
+    torch.cuda.synchronize()
+    return out
+
+
+def test_full_step_batched_equals_solo_over_fed_back_steps(sd, full):
+    """One step at a time the sequences write rows CTX[s] - 1 + i, which every
+    run writes with the same bits (that is what is checked), and attention at
+    step i reads only rows up to there, so the runs can share the caches."""
+    model, caches = full
+    first = [7, 1000, 151935, 42]
+    say("full step: solo runs")
+    solo = {s: _decode(model, caches, [s], first, STEPS) for s in range(4)}
+    for order in ([0, 1, 2, 3], [3, 1, 0, 2], [2, 0, 1], [1, 3]):
+        say(f"full step: batch {order}")
+        got = _decode(model, caches, order, first, STEPS)
+        for i in range(STEPS):
+            lg, nt = got[i]
+            for row, s in enumerate(order):
+                ls, ns = solo[s][i]
+                assert _same(lg[row], ls[0]), (order, i, s)
+                assert int(nt[row]) == int(ns[0]), (order, i, s)
+
+
+def test_full_verify_step_16_rows_equals_one_token_steps(sd, full):
+    """4 sequences x 4 proposed tokens (16 rows) in one verify step; the last
+    burst crosses the 256-key chunk edge at 32768.  Row (s, i) equals the
+    logits of the one-token step at CTX[s] - 1 + i fed token i, after the
+    steps fed tokens 0 .. i-1; the caches end up the same."""
+    import torch
+    model, caches = full
+    toks = [[5, 17, 151935, 2], [999, 0, 64, 65], [41, 42, 43, 44], [100000, 3, 3, 3]]
+    say("full verify step: 16 rows")
+    r = StepRunner(model, caches, max_ctx=max(CTX) + SPAN, n_new=[4] * 4)
+    r.tokens.copy_(torch.tensor(sum(toks, []), dtype=torch.int32))
+    r.set_positions([c - 1 for c in CTX])
+    r.step()
+    lv, nv = r.logits.clone(), r.next_tokens.clone()
+    k_after = [c.k[:, c0 - 1:c0 + 3].clone() for c, c0 in zip(caches, CTX)]
+    say("full verify step: one-token steps")
+    one = StepRunner(model, caches, max_ctx=max(CTX) + SPAN)
+    for i in range(4):
+        one.tokens.copy_(torch.tensor([toks[s][i] for s in range(4)], dtype=torch.int32))
+        one.set_positions([c - 1 + i for c in CTX])
+        one.step()
+        for s in range(4):
+            assert _same(one.logits[s], lv[4 * s + i]), (s, i)
+            assert int(one.next_tokens[s]) == int(nv[4 * s + i]), (s, i)
+    for c, c0, ka in zip(caches, CTX, k_after):
+        assert _same(c.k[:, c0 - 1:c0 + 3], ka)
+
+
+def _two_layer(model):
+    d = dict(FULL, n_layers=2)
+    return DecodeModel(d, model.layers[:2], model.tok_embd, model.out_norm, model.w_lm)
+
+
+def test_full_width_two_layers_vs_oracle(sd, full):
+    """The first two layers of the full model with the real LM head, four
+    sequences at the ragged contexts, against the oracle's step on host copies
+    of the same weights and caches: logits within 1e-3 normwise, tokens equal
+    where the top-2 margin is clear, cache rows within fp16 rounding."""
+    import torch
+    import oracle
+    from oracle import step as ostep
+    model, _ = full
+    m2 = _two_layer(model)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    caches = [SeqCache.random_device(g, 2, c + 4, 8, 128) for c in CTX]
+    toks = [9, 70000, 151935, 1]
+    pos = [c - 1 for c in CTX]
+    r = StepRunner(m2, caches, max_ctx=max(CTX) + 4)
+    r.tokens.copy_(torch.tensor(toks, dtype=torch.int32))
+    r.set_positions(pos)
+    r.step()
+    torch.cuda.synchronize()
+    lg = r.logits.cpu().numpy()
+    nt = r.next_tokens.cpu().numpy()
+    say("full width, 2 layers: oracle step on host copies")
+
+    def hcopy(t):
+        return t.cpu().numpy()
+
+    layers = [{"w_qkv": hcopy(L["w_qkv"]), "w_o": hcopy(L["w_o"]), "w_gu": hcopy(L["w_gu"]),
+               "w_down": hcopy(L["w_down"]), "attn_norm": hcopy(L["attn_norm"]),
+               "ffn_norm": hcopy(L["ffn_norm"])} for L in m2.layers]
+    om = ostep.Model(4096, 32, 8, 128, 14336, 151936, 1e-6, 1e6,
+                     m2.tok_embd.cpu().view(torch.int16).numpy().view(np.uint16),
+                     hcopy(m2.out_norm), hcopy(m2.w_lm), layers)
+    # the oracle writes row pos of each cache; the rows below are the GPU's inputs
+    oc = []
+    for c in caches:
+        k = c.k.cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        v = c.v.cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        oc.append((k, v))
+    gpu_rows = [(oc[s][0][:, pos[s]].copy(), oc[s][1][:, pos[s]].copy()) for s in range(4)]
+    olg, ont = ostep.decode_step(om, oc, toks, pos)
+    rel = np.linalg.norm(lg - olg) / np.linalg.norm(olg)
+    say(f"  logits normwise relative error vs oracle: {rel:.3e}")
+    assert rel <= 1e-3
+    for s in range(4):
+        top = np.sort(olg[s])[-2:]
+        if top[1] - top[0] > 1e-3 * abs(top[1]):
+            assert nt[s] == ont[s], s
+        for j in range(2):
+            gk = gpu_rows[s][j].view(np.float16).astype(np.float32)
+            ok = oc[s][j][:, pos[s]].view(np.float16).astype(np.float32)
+            assert np.max(np.abs(gk - ok)) <= 2e-2 * max(1.0, float(np.max(np.abs(ok)))), (s, j)
+
+
+def test_full_width_fused_qkv_ring_and_paged(sd, full):
+    """Two full-width layers with a 400-position window, 4 sequences x 2 tokens
+    = 8 rows (the widest batch the fused QKV/RoPE/K/V launch takes) over plain,
+    ring (512 rows) and paged (64-row blocks) caches:
+    the three give bitwise the same logits and rows, and each row equals the
+    one-token steps; then one-token steps at 1..4 sequences on the ring and
+    the pool equal the plain caches."""
+    import torch
+    model, _ = full
+    # a 400-position window, so that ring caches of 512 rows hold every key
+    # a token attends to (ring caches need a window)
+    m2 = DecodeModel(dict(FULL, n_layers=2, window=400), model.layers[:2], model.tok_embd,
+                     model.out_norm, model.w_lm)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(14)
+    ctx = [300, 700, 1030, 2050]
+    cap, rcap = 2304, 512
+    plain = [SeqCache.random_device(g, 2, cap, 8, 128) for _ in ctx]
+    ring = []
+    for c, c0 in zip(plain, ctx):
+        j = torch.arange(max(0, c0 + 2 - rcap), c0 + 2, device="cuda")
+        rk = torch.zeros((2, rcap, 8, 128), dtype=torch.float16, device="cuda")
+        rv = torch.zeros_like(rk)
+        rk[:, j % rcap] = c.k[:, j]
+        rv[:, j % rcap] = c.v[:, j]
+        ring.append(SeqCache(rk, rv))
+    bs = 64
+    nb = cap // bs
+    place = torch.randperm(4 * nb + 3, generator=torch.Generator().manual_seed(15)).to(torch.int32)
+    tabs = [place[s * nb:(s + 1) * nb].contiguous().cuda() for s in range(4)]
+    pool = SeqCache(torch.zeros((2, (4 * nb + 3) * bs, 8, 128), dtype=torch.float16, device="cuda"),
+                    torch.zeros((2, (4 * nb + 3) * bs, 8, 128), dtype=torch.float16, device="cuda"))
+    rows = [(tabs[s].long()[torch.arange(cap, device="cuda") // bs] * bs
+             + torch.arange(cap, device="cuda") % bs) for s in range(4)]
+    for s in range(4):
+        pool.k[:, rows[s]] = plain[s].k
+        pool.v[:, rows[s]] = plain[s].v
+    toks = [3, 4, 150000, 151935, 12, 13, 99, 98]
+    runners = {
+        "plain": StepRunner(m2, plain, max_ctx=cap, n_new=[2] * 4),
+        "ring": StepRunner(m2, ring, max_ctx=cap, n_new=[2] * 4, ring=True),
+        "paged": StepRunner(m2, [pool] * 4, max_ctx=cap, n_new=[2] * 4, block_tables=tabs,
+                            block_size=bs),
+    }
+    out = {}
+    for name, r in runners.items():
+        say(f"full width fused QKV, 8 rows: {name}")
+        r.tokens.copy_(torch.tensor(toks, dtype=torch.int32))
+        r.set_positions([c - 1 for c in ctx])
+        r.step()
+        out[name] = r.logits.clone()
+    assert _same(out["plain"], out["ring"]) and _same(out["plain"], out["paged"])
+    for s in range(4):
+        for j in range(2):
+            p = ctx[s] - 1 + j
+            pr, rr = int(rows[s][p]), p % rcap
+            assert _same(pool.k[:, pr], plain[s].k[:, p]) and _same(ring[s].k[:, rr], plain[s].k[:, p])
+            assert _same(pool.v[:, pr], plain[s].v[:, p]) and _same(ring[s].v[:, rr], plain[s].v[:, p])
+    one = StepRunner(m2, plain, max_ctx=cap)
+    for i in range(2):
+        one.tokens.copy_(torch.tensor([toks[2 * s + i] for s in range(4)], dtype=torch.int32))
+        one.set_positions([c - 1 + i for c in ctx])
+        one.step()
+        for s in range(4):
+            assert _same(one.logits[s], out["plain"][2 * s + i]), (s, i)
+    # one-token steps at 1..4 sequences (1..4 rows) after the burst
+    for n in (1, 2, 3, 4):
+        res = []
+        for kind in ("plain", "ring", "paged"):
+            if kind == "plain":
+                r = StepRunner(m2, plain[:n], max_ctx=cap)
+            elif kind == "ring":
+                r = StepRunner(m2, ring[:n], max_ctx=cap, ring=True)
+            else:
+                r = StepRunner(m2, [pool] * n, max_ctx=cap, block_tables=tabs[:n], block_size=bs)
+            r.tokens.copy_(torch.tensor([5 + s for s in range(n)], dtype=torch.int32))
+            r.set_positions([c + 1 for c in ctx[:n]])
+            r.step()
+            res.append(r.logits.clone())
+        assert _same(res[0], res[1]) and _same(res[0], res[2]), n

@@ -21,6 +21,10 @@ from sequence_decode_amd.step import DecodeModel, SeqCache, StepRunner
 pytestmark = pytest.mark.gpu
 
 DIMS = dict(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128, ffn=768, vocab=1000)
+# the real head shape: QKV 6144 x 4096 (768 RoPE pair groups, 3 per workgroup
+# of the fused launch), FFN 14336, the full 151,936-row LM head
+REAL = dict(n_layers=1, hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=14336,
+            vocab=151936)
 CAP = 600
 
 
@@ -42,18 +46,19 @@ def _check_quant(xq, xd, y):
     assert np.array_equal(xq, rq) and np.array_equal(bits(xd), bits(rd))
 
 
-def test_layer_ops_teacher_forced_and_fused_step(sd):
+@pytest.mark.parametrize("dims", [DIMS, REAL], ids=["small", "real_heads"])
+def test_layer_ops_teacher_forced_and_fused_step(sd, dims):
     import torch
-    say("teacher-forced step ops")
-    h = synth.model_host(3700, **DIMS)
+    say(f"teacher-forced step ops {dims}")
+    h = synth.model_host(3700, **dims)
     model = DecodeModel.from_host(h)
-    H, Hq, Hkv, Dh, F, V = (DIMS[k] for k in ("hidden", "n_heads", "n_kv_heads", "head_dim", "ffn",
+    H, Hq, Hkv, Dh, F, V = (dims[k] for k in ("hidden", "n_heads", "n_kv_heads", "head_dim", "ffn",
                                              "vocab"))
     QKV = (Hq + 2 * Hkv) * Dh
     eps, theta = np.float32(h["eps"]), h["theta"]
     scale = np.float32(1.0) / np.sqrt(np.float32(Dh))
     g = synth.rng(3701)
-    caches = [synth.prefilled_cache(g, DIMS["n_layers"], CAP, Hkv, Dh) for _ in range(3)]
+    caches = [synth.prefilled_cache(g, dims["n_layers"], CAP, Hkv, Dh) for _ in range(3)]
     toks = np.array([17, 999, 3], np.int32)
     pos = np.array([0, 257, 599], np.int32)
     n = len(toks)

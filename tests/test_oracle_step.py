@@ -85,3 +85,162 @@ def test_first_layer_key_row_is_rotated_projection():
     kproj = oracle.qgemv_q8_0(m.layers[0]["w_qkv"], (Hq + 2 * Hkv) * D, m.hidden, aq, ad, rows=rows)
     k = oracle.rope_posvec(kproj.reshape(1, Hkv, D), [pos], m.theta)
     assert np.array_equal(caches[0][0][0, pos], oracle.f32_to_f16_bits(k[0]))
+
+
+# ---------------------------------------------------------------------------
+# The wiring of the layer, pinned against a recomputation that never calls the
+# oracle: exact-semantics brute primitives (tests/brute.py) composed in the
+# order of the dense pre-norm block (ds4 pull request 604, "2. Single-GPU
+# decode batches don't scale" and "Commit walkthrough / Graph driver": dense
+# projections, per-sequence RoPE and cache append, attention, feed-forward,
+# output head with one logits row per sequence).
+
+import brute
+
+SMALL = dict(n_layers=2, hidden=128, n_heads=4, n_kv_heads=2, head_dim=32, ffn=256, vocab=64)
+
+
+def _small_model(seed, **over):
+    d = dict(SMALL, **over)
+    h = synth.model_host(seed, **d)
+    m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
+                    h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
+                    h["w_lm"], h["layers"])
+    return h, m
+
+
+def _bq(x):
+    return brute.quantize_rows_vectorized(np.asarray(x, np.float32))
+
+
+def _bgemv(blob, N, K, xq, xd, residual=None):
+    codes, bits = brute.unpack_q8_0(blob, N, K)
+    return brute.qgemv_exact_vec(codes, bits, xq, xd, residual)
+
+
+def _bnorm(x, gamma, eps):
+    return brute.rmsnorm_decimal(x, gamma, eps).astype(np.float32)
+
+
+def brute_step(h, caches, tokens, pos, window=0):
+    """The decode step from brute primitives only; caches [(k_bits, v_bits)] are
+    updated in place like the oracle's.  Returns (logits, tokens)."""
+    n = len(tokens)
+    H, Hq, Hkv, Dh, F = h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"]
+    G = Hq // Hkv
+    scale = np.float32(1.0) / np.sqrt(np.float32(Dh))
+    x = h["tok_embd_bits"][np.asarray(tokens)].view(np.float16).astype(np.float32)
+    for li, L in enumerate(h["layers"]):
+        aq, ad = _bq(_bnorm(x, L["attn_norm"], h["eps"]))
+        qkv = _bgemv(L["w_qkv"], (Hq + 2 * Hkv) * Dh, H, aq, ad)
+        q = brute.rope_complex(qkv[:, :Hq * Dh].reshape(n, Hq, Dh), pos, h["theta"], Dh)
+        k = brute.rope_complex(qkv[:, Hq * Dh:(Hq + Hkv) * Dh].reshape(n, Hkv, Dh), pos, h["theta"], Dh)
+        v = qkv[:, (Hq + Hkv) * Dh:].reshape(n, Hkv, Dh)
+        o = np.zeros((n, Hq, Dh), np.float32)
+        for s in range(n):
+            caches[s][0][li, pos[s]] = k[s].astype(np.float16).view(np.uint16)
+            caches[s][1][li, pos[s]] = v[s].astype(np.float16).view(np.uint16)
+            lo = max(0, pos[s] - window + 1) if window else 0
+            kk = caches[s][0][li, lo:pos[s] + 1].view(np.float16).astype(np.float64)
+            vv = caches[s][1][li, lo:pos[s] + 1].view(np.float16).astype(np.float64)
+            o[s] = brute.attn_decimal(q[s], kk, vv, pos[s] + 1 - lo, scale, G).astype(np.float32)
+        oq, od = _bq(o.reshape(n, Hq * Dh))
+        hres = _bgemv(L["w_o"], H, Hq * Dh, oq, od, residual=x)
+        nq, nd = _bq(_bnorm(hres, L["ffn_norm"], h["eps"]))
+        gu = _bgemv(L["w_gu"], 2 * F, H, nq, nd)
+        mq, md = _bq(brute.swiglu_decimal(gu[:, :F], gu[:, F:]).astype(np.float32))
+        x = _bgemv(L["w_down"], H, F, mq, md, residual=hres)
+    fq, fd = _bq(_bnorm(x, h["out_norm"], h["eps"]))
+    logits = _bgemv(h["w_lm"], h["vocab"], H, fq, fd)
+    return logits, np.argmax(logits, axis=1)
+
+
+def _small_caches(n, cap, seed):
+    g = synth.rng(seed)
+    return [synth.prefilled_cache(g, SMALL["n_layers"], cap, SMALL["n_kv_heads"], SMALL["head_dim"])
+            for _ in range(n)]
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a.astype(np.float64) - b) / np.linalg.norm(b.astype(np.float64)))
+
+
+import pytest
+
+
+@pytest.mark.parametrize("window", [0, 3])
+def test_step_equals_brute_recomputation(window):
+    """Two layers with distinct random norm gammas and nonzero O and down
+    weights: the oracle's logits, tokens and every written cache row agree with
+    the brute composition.  A swapped attn/ffn norm, the FFN fed from x instead
+    of h, or the down output added to x instead of h each move the logits by
+    orders of magnitude more than the tolerance."""
+    h, m = _small_model(80)
+    m.window = window
+    toks, pos = [3, 41], [5, 9]
+    c_or = _small_caches(2, 12, seed=81)
+    c_br = [(k.copy(), v.copy()) for k, v in c_or]
+    lg, nxt = ostep.decode_step(m, c_or, toks, pos)
+    lb, nb = brute_step(h, c_br, toks, pos, window)
+    assert _rel(lg, lb) <= 1e-5
+    top2 = np.sort(lb, axis=1)[:, -2:]
+    for s in range(2):
+        if top2[s, 1] - top2[s, 0] > 1e-3 * np.abs(lb[s]).max():
+            assert nxt[s] == nb[s]
+    for s in range(2):
+        for c in range(2):
+            a = c_or[s][c].view(np.float16).astype(np.float64)
+            b = c_br[s][c].view(np.float16).astype(np.float64)
+            assert np.abs(a - b).max() <= 2e-3 * np.abs(b).max()
+
+
+def test_single_key_attention_and_zero_ffn_norm_closed_form():
+    """At position 0 the only key is the token's own, so attention returns its
+    fp16 value row exactly, whatever q and k are; with ffn_norm = 0 the
+    feed-forward input quantizes to zero codes and adds exactly +0.  One layer
+    then maps x to x + W_o q8(fp16(v)), and the logits are the LM head of
+    rmsnorm of that: computed here without any attention at all."""
+    h, m = _small_model(82, n_layers=1)
+    L = h["layers"][0]
+    L["ffn_norm"] = np.zeros_like(L["ffn_norm"])
+    m.layers[0]["ffn_norm"] = L["ffn_norm"]
+    H, Hq, Hkv, Dh = h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"]
+    G = Hq // Hkv
+    toks = [7, 30]
+    g = synth.rng(83)
+    caches = [synth.prefilled_cache(g, 1, 4, Hkv, Dh) for _ in range(2)]
+    lg, _ = ostep.decode_step(m, caches, toks, [0, 0])
+    x = h["tok_embd_bits"][toks].view(np.float16).astype(np.float32)
+    aq, ad = _bq(_bnorm(x, L["attn_norm"], h["eps"]))
+    qkv = _bgemv(L["w_qkv"], (Hq + 2 * Hkv) * Dh, H, aq, ad)
+    v = qkv[:, (Hq + Hkv) * Dh:].reshape(2, Hkv, Dh).astype(np.float16).astype(np.float32)
+    o = np.repeat(v, G, axis=1).reshape(2, Hq * Dh)        # head h reads KV head h // G
+    oq, od = _bq(o)
+    hres = _bgemv(L["w_o"], H, Hq * Dh, oq, od, residual=x)
+    fq, fd = _bq(_bnorm(hres, h["out_norm"], h["eps"]))
+    want = _bgemv(h["w_lm"], h["vocab"], H, fq, fd)
+    assert _rel(lg, want) <= 1e-5
+
+
+def test_zero_attention_input_leaves_ffn_on_the_residual():
+    """attn_norm = 0 at position 0: q = k = v = 0, attention returns the zero
+    value row, so h == x exactly and the layer is x + FFN(rmsnorm(x) with
+    ffn_norm).  Swapping the two norms would zero the FFN instead."""
+    h, m = _small_model(84, n_layers=1)
+    L = h["layers"][0]
+    L["attn_norm"] = np.zeros_like(L["attn_norm"])
+    m.layers[0]["attn_norm"] = L["attn_norm"]
+    H, F = h["hidden"], h["ffn"]
+    toks = [11]
+    g = synth.rng(85)
+    caches = [synth.prefilled_cache(g, 1, 4, h["n_kv_heads"], h["head_dim"])]
+    lg, _ = ostep.decode_step(m, caches, toks, [0])
+    assert np.all(caches[0][1][0, 0].view(np.float16) == 0)
+    x = h["tok_embd_bits"][toks].view(np.float16).astype(np.float32)
+    nq, nd = _bq(_bnorm(x, L["ffn_norm"], h["eps"]))
+    gu = _bgemv(L["w_gu"], 2 * F, H, nq, nd)
+    mq, md = _bq(brute.swiglu_decimal(gu[:, :F], gu[:, F:]).astype(np.float32))
+    xo = _bgemv(L["w_down"], H, F, mq, md, residual=x)
+    fq, fd = _bq(_bnorm(xo, h["out_norm"], h["eps"]))
+    want = _bgemv(h["w_lm"], h["vocab"], H, fq, fd)
+    assert _rel(lg, want) <= 1e-5

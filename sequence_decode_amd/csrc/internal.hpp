@@ -26,6 +26,7 @@ constexpr int kAttnHeadDim = 128;
 constexpr int kAttnGroup = 4;       // query heads per KV head handled by one workgroup
 constexpr int kAttnPartialFloats = 132;  // m, l, 2 pad, o[128]
 constexpr int kAttnMaxNew = 4;           // query tokens per sequence in one attention call
+constexpr size_t kAttnScratchBytes = SD_ATTN_SCRATCH_BYTES;  // allocation-free attention partials
 
 // Per-sequence view as passed by value to the attention / append kernels.
 struct SeqArg {
@@ -158,6 +159,9 @@ size_t attn_layout(SeqArgs* seqs, int H_q, int H_kv);
 hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_q, int H_kv,
                        float scale, float* out, float* partials, int8_t* oq, float* od,
                        hipStream_t st);
+// Device address, on the current device, of the attention scratch array
+// (kAttnScratchBytes) used by the allocation-free attention entry point.
+hipError_t attn_scratch(float** ptr);
 
 hipError_t launch_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D,
                              const float* gamma, float eps, int8_t* xq, float* xd, float* y,

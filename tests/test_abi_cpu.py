@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 6
+    assert L.sd_abi_version() == 7
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -114,6 +114,23 @@ def test_attention_rejections(L):
     assert a(FAKE, 4096, v1, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
     v2 = (_lib.SeqView * 2)(_view(2050, 4096), _view(32768, 32768))
     assert L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128) == (9 + 128) * 32 * 132 * 4
+
+
+def test_noalloc_attention_rejections(L):
+    """The allocation-free attention entry point validates like the workspace
+    one, and refuses partials beyond its 16 MiB scratch array before any HIP
+    call (so this runs without a GPU)."""
+    a = L.sd_decode_attn_multiseq_noalloc
+    views5 = (_lib.SeqView * 5)(*[_view(10, 16) for _ in range(5)])
+    assert a(FAKE, 4096, views5, 5, 32, 8, 128, 0.088, FAKE, None) == SD_EINVAL
+    v1 = (_lib.SeqView * 1)(_view(10, 16))
+    assert a(None, 4096, v1, 1, 32, 8, 128, 0.088, FAKE, None) == SD_EINVAL
+    assert a(FAKE, 4096, v1, 1, 32, 8, 64, 0.088, FAKE, None) == SD_EUNSUPPORTED
+    assert a(ODD, 4096, v1, 1, 32, 8, 128, 0.088, FAKE, None) == SD_EALIGN
+    big = (_lib.SeqView * 4)(*[_view(65536, 65536) for _ in range(4)])
+    need = L.sd_decode_attn_workspace_bytes(big, 4, 32, 128)
+    assert need == 4 * 256 * 32 * 132 * 4 > (16 << 20)
+    assert a(FAKE, 4096, big, 4, 32, 8, 128, 0.088, FAKE, None) == SD_EWORKSPACE
 
 
 def test_verify_attention_rejections_and_workspace(L):

@@ -102,6 +102,17 @@ struct RopeArgs {
   SeqArgs seqs;
 };
 
+// Input of a projection given as the q8 blocks of rmsnorm(x [n][ldx], gamma,
+// eps) (the RMSNorm that precedes the QKV, gate|up and output projections of
+// the step), computed by the projection's own workgroups with the arithmetic
+// of launch_rmsnorm_q8: the same codes and scales.
+struct RmsArgs {
+  const float* x;
+  int64_t ldx;
+  const float* gamma;
+  float eps;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
 hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
@@ -131,14 +142,22 @@ hipError_t launch_qgemv(const void* w, int64_t N, int64_t K, const int8_t* xq, c
 // gate|up projection fused with SwiGLU + q8 quantization (see qgemv.hip)
 bool swiglu_fusable(int64_t F, int64_t K, int n_tok);
 hipError_t launch_qgemv_swiglu(const void* w, int64_t F, int64_t K, const int8_t* xq, const float* xd,
-                               int n_tok, int8_t* oq, float* od, hipStream_t st);
+                               int n_tok, int8_t* oq, float* od, hipStream_t st,
+                               const RmsArgs* rms = nullptr);
+// Whether a staged one-chunk projection takes its input as an RMS prologue
+// (K <= 4096, one row): rms != nullptr on the fused launchers replaces xq /
+// xd by the q8 blocks of rmsnorm(rms->x).
+bool rms_fusable(int64_t K, int n_tok);
+hipError_t launch_qgemv_rms(const void* w, int64_t N, int64_t K, const RmsArgs& rms, int n_tok, float* y,
+                            int64_t ldy, hipStream_t st);
 // QKV projection (N = (n_heads + 2 n_kv) * 128 rows) with RoPE of q and k and
 // the fp16 K/V cache write in the same launch: the q rows of y and the cache
 // rows get exactly what launch_rope_kv_step makes of the plain projection's
 // outputs; the k and v rows of y stay unrotated, as there.
 bool qkv_rope_fusable(int64_t N, int64_t K, int n_tok);
 hipError_t launch_qgemv_qkv_rope(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
-                                 int n_tok, float* y, int64_t ldy, const RopeArgs& ra, hipStream_t st);
+                                 int n_tok, float* y, int64_t ldy, const RopeArgs& ra, hipStream_t st,
+                                 const RmsArgs* rms = nullptr);
 
 hipError_t launch_rope_posvec(float* x, int n_tok, int n_heads, int head_dim, int64_t ld_tok,
                               int64_t ld_head, const int32_t* pos, double theta, int n_rot,

@@ -36,6 +36,7 @@
 
 #include "device_math.hpp"
 #include "internal.hpp"
+#include "qgemv_dev.hpp"
 
 namespace sd {
 
@@ -105,25 +106,6 @@ __device__ __forceinline__ void load_pair_rows(uint32_t (&wv)[R][kPairDw], const
   }
 }
 
-// The cell of one pair for R rows and one token: (0 + s_A) + s_B.
-template <int R>
-__device__ __forceinline__ void pair_cells(float (&cell)[R], const uint32_t (&wv)[R][kPairDw],
-                                           const uint32_t (&a)[kPairDw], float dxA, float dxB) {
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int iA = 0, iB = 0;
-#pragma unroll
-    for (int c = 0; c < 9; ++c) iA = __builtin_amdgcn_sdot4(wv[r][c], a[c], iA, false);
-#pragma unroll
-    for (int c = 9; c < 17; ++c) iB = __builtin_amdgcn_sdot4(wv[r][c], a[c], iB, false);
-    const float dwA = f16_bits_to_f32(wv[r][0]);
-    const float dwB = f16_bits_to_f32(wv[r][8] >> 16);
-    const float sA = fmul(fmul(dwA, dxA), (float)iA);
-    const float sB = fmul(fmul(dwB, dxB), (float)iB);
-    cell[r] = fadd(fadd(0.0f, sA), sB);
-  }
-}
-
 __device__ __forceinline__ void read_act(uint32_t (&a)[kPairDw], float& dxA, float& dxB,
                                          const uint32_t* __restrict__ lds_pair) {
   const u32x4a* ap = reinterpret_cast<const u32x4a*>(lds_pair);
@@ -142,12 +124,6 @@ __device__ __forceinline__ void read_act(uint32_t (&a)[kPairDw], float& dxA, flo
   dxB = __uint_as_float(t[18]);
 }
 
-__device__ __forceinline__ void store_out(float v, int n, int t, const float* residual, float* y,
-                                          int64_t ldy) {
-  float o = v;
-  if (residual) o = fadd(residual[(int64_t)t * ldy + n], v);
-  y[(int64_t)t * ldy + n] = o;
-}
 
 // ---------------------------------------------------------------------------
 // 1..8 tokens, K <= 16384 (at most 4 chunks): the streaming kernel.
@@ -171,147 +147,76 @@ __device__ __forceinline__ void store_out(float v, int n, int t, const float* re
 // once, contiguously, before the first weights; each lane then takes its
 // pair's share from there.  Over 3 or 4 chunks (4 waves, two workgroups per
 // CU) each lane loads its pair's activations itself.
-constexpr int kRing = 2;
-constexpr int kTable = 32;
-// rows per streaming item (one row per item measured best: deeper or wider
-// items lowered the bytes in flight per CU)
-constexpr int dma_rows(int) { return 1; }
-// staged activation bytes per chunk and token: 4096 code bytes + 128 fp32 scales
-constexpr int kStageX = 4096;
-constexpr int kStageD = 512;
-// 8 waves with their rings, the staged activations of sp chunks and the
-// output table fit the 160 KiB of LDS (all 8 tokens over 1 or 2 chunks)
-constexpr bool stage_fits(int sp, int nt) {
-  return 8 * kRing * dma_rows(nt) * 64 * kPairBytes + sp * nt * (kStageX + kStageD) <= kGemvLdsMax &&
-         8 * kRing * dma_rows(nt) * 64 * kPairBytes + sp * nt * (kStageX + kStageD) +
-                 kTable * 8 * dma_rows(nt) * nt * 4 <= 160 * 1024;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Waits until at most n DMA instructions of this wave are outstanding.
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<15>(); break;
-  }
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Cache policy of the weight DMAs: non-temporal (nt).  Each weight byte is
-// read once per pass and a model's weights are many times the 256 MB
-// Infinity Cache, so keeping them there buys nothing; with nt the 8B-class
-// sweep streams 4-5% faster at 1-4 tokens (same bytes, same outputs).
-constexpr int kWeightCpol = 2;
-
-// Issues the DMA of one chunk segment (seg_bytes <= 4352) of one row.  A full
-// segment is 4 whole 1 KiB instructions plus one for lanes 0..15; a shorter
-// (last) segment is cut at the lane granularity.  Returns the instructions issued.
-__device__ __forceinline__ int dma_segment(const uint8_t* g, uint8_t* l, int seg_bytes, int lane) {
-  if (seg_bytes == 64 * kPairBytes) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + j * 1024 + lane * 16),
-                                       (lds_ptr)(l + j * 1024), 16, 0, kWeightCpol);
-    if (lane < 16)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + 4096 + lane * 16),
-                                       (lds_ptr)(l + 4096), 16, 0, kWeightCpol);
-    return 5;
-  }
-  const int n = (seg_bytes + 1023) / 1024;
-  for (int j = 0; j < n; ++j)
-    if (j * 1024 + lane * 16 < seg_bytes)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g + j * 1024 + lane * 16),
-                                       (lds_ptr)(l + j * 1024), 16, 0, kWeightCpol);
-  return n;
-}
-
-// The fixed 64-lane tree of wave_sum_fixed for 2..8 token cells at once
-// (transposed butterfly).  At the first level (partners lane ^ 1) a lane keeps
-// half of the tokens and hands the other half to its partner, at the second
-// (lane ^ 2) half of the rest, and with 5..8 tokens at the third (lane 7 - l
-// within 8) the last one.  Every addition combines the same two subtree sums
-// as wave_sum_fixed applied to each token, so each token's total has the same
-// bits, but the tree costs one pass instead of one per token.  Lane l ends
-// with the total of token tree_token(l).  The keep/hand-over choices are
-// parities of lane bits (b0 ^ b2, then b1 ^ b2, then b0 ^ b3), chosen so that
-// each level's partner holds the opposite choice at its own level and the same
-// at every other, and the mirrored partners of the later levels (7 - l, 15 - l)
-// hold the same token.  Tokens past NT are zeros whose sums are never used.
-__device__ __forceinline__ int tree_token(int lane, int nt) {
-  const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
-  if (nt == 2) return b0 ^ b2;
-  if (nt <= 4) return 2 * (b0 ^ b2) + (b1 ^ b2);
-  return 4 * (b0 ^ b2) + 2 * (b1 ^ b2) + (b0 ^ b3);
-}
-
-// lanes whose totals are stored, one per token (tree_token of lanes 0 .. n-1)
-constexpr int tree_writers(int nt) { return nt == 2 ? 2 : (nt <= 4 ? 4 : 8); }
-
-template <int NT>
-__device__ __forceinline__ float wave_sum_fixed_tr(const float (&v)[NT], int lane) {
-  static_assert(NT >= 2 && NT <= 8, "2..8 tokens");
-  const bool lo1 = ((lane ^ (lane >> 2)) & 1) == 0;  // keeps the first half of the tokens
-  float e;
-  if constexpr (NT > 4) {
-    float w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = i < NT ? v[i < NT ? i : 0] : 0.0f;
-    float k[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      k[i] = fadd(lo1 ? w[i] : w[4 + i], dpp_mov<0xB1>(lo1 ? w[4 + i] : w[i]));
-    const bool lo2 = (((lane >> 1) ^ (lane >> 2)) & 1) == 0;  // keeps the first two of its four
-    float m[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      m[i] = fadd(lo2 ? k[i] : k[2 + i], dpp_mov<0x4E>(lo2 ? k[2 + i] : k[i]));
-    const bool lo3 = ((lane ^ (lane >> 3)) & 1) == 0;  // keeps the first of its two
-    e = fadd(lo3 ? m[0] : m[1], dpp_mov<0x141>(lo3 ? m[1] : m[0]));
-    e = fadd(e, dpp_mov<0x140>(e));  // row_mirror
-    return cross_row_sum_fixed(e);
-  } else if constexpr (NT == 2) {
-    const float keep = lo1 ? v[0] : v[1];
-    const float send = lo1 ? v[1] : v[0];
-    e = fadd(keep, dpp_mov<0xB1>(send));
-    e = fadd(e, dpp_mov<0x4E>(e));
-  } else {
-    const float v3 = NT == 4 ? v[NT == 4 ? 3 : 0] : 0.0f;
-    const float k0 = lo1 ? v[0] : v[2], k1 = lo1 ? v[1] : v3;
-    const float s0 = lo1 ? v[2] : v[0], s1 = lo1 ? v3 : v[1];
-    const float a = fadd(k0, dpp_mov<0xB1>(s0));
-    const float b = fadd(k1, dpp_mov<0xB1>(s1));
-    const bool lo2 = (((lane >> 1) ^ (lane >> 2)) & 1) == 0;  // keeps the first of its pair
-    e = fadd(lo2 ? a : b, dpp_mov<0x4E>(lo2 ? b : a));
-  }
-  e = fadd(e, dpp_mov<0x141>(e));  // row_half_mirror
-  e = fadd(e, dpp_mov<0x140>(e));  // row_mirror
-  return cross_row_sum_fixed(e);
-}
 
 // Kernel argument of the RoPE epilogue: the whole RopeArgs (about 620 bytes)
 // only for the ROPE instantiation, an empty struct for every other launch.
 struct NoRope {};
 template <bool ROPE>
 using RopeParam = std::conditional_t<ROPE, RopeArgs, NoRope>;
+
+// RMS prologue: the projection's input is the q8 blocks of
+// rmsnorm(x, gamma, eps), which every workgroup computes itself (K <= 4096).
+struct NoRms {};
+template <bool RMS>
+using RmsParam = std::conditional_t<RMS, RmsArgs, NoRms>;
+
+// q8 blocks of rmsnorm(x, gamma) for NT rows of D <= 4096 values into the
+// staged-activation layout (codes [NT][kStageX], then scales [NT][kStageD]),
+// from the rows held in registers (va: elements j * 1024 + tid, vb: elements
+// j * 1024 + tid + 512, j < 4; gm: gamma at the same elements, [0] for va,
+// [1] for vb).  No memory is read here, so the weight DMAs in flight are not
+// waited for.  Bitwise the outputs of k_rmsnorm_q8<4>: that
+// kernel runs 1024 threads per row, thread v summing the squares of elements
+// j * 1024 + v in j order, then a fixed 64-lane tree per wave, then its 16 wave
+// sums in wave order; here thread tid of 512 plays virtual threads tid and
+// tid + 512 (virtual waves w and w + 8) with the same sums in the same order.
+template <int NT>
+__device__ __forceinline__ void rms_to_stage(const RmsArgs& ra, int64_t D, const float (&va)[NT][4],
+                                             const float (&vb)[NT][4], const float (&gm)[2][4], uint8_t* stage,
+                                             float (*part)[16]) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sa = fadd(sa, fmul(va[t][j], va[t][j]));
+      sb = fadd(sb, fmul(vb[t][j], vb[t][j]));
+    }
+    sa = wave_sum_fixed(sa);
+    sb = wave_sum_fixed(sb);
+    if ((tid & 63) == 0) {
+      part[t][wave] = sa;
+      part[t][wave + 8] = sb;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float total = part[t][0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) total = fadd(total, part[t][w]);
+    const float r = fdiv(1.0f, sqrtf(fadd(fdiv(total, (float)D), ra.eps)));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((int64_t)j * 1024 + 512 * h >= D) break;  // uniform; blocks of 32 stay whole
+        const int64_t i = (int64_t)j * 1024 + tid + 512 * h;
+        const bool valid = i < D;
+        const float v = h ? vb[t][j] : va[t][j];
+        const float o = valid ? fmul(fmul(v, r), gm[h][j]) : 0.0f;
+        const float amax = group_max<32>(valid ? fabsf(o) : 0.0f);
+        const float d = q8_scale(amax);
+        if (valid) {
+          stage[t * kStageX + i] = (uint8_t)(int8_t)q8_code(o, d);
+          if ((tid & 31) == 0) *reinterpret_cast<float*>(stage + NT * kStageX + t * kStageD + (i >> 5) * 4) = d;
+        }
+      }
+    }
+  }
+}
 
 // SWI (gate|up rows, one chunk, staged): instead of y, the kernel emits the
 // SwiGLU of its outputs as q8 blocks (oq, od), each block from one unit of 32
@@ -321,14 +226,15 @@ using RopeParam = std::conditional_t<ROPE, RopeArgs, NoRope>;
 // of pair group g = blockIdx.x + k * gridDim.x, head g / 16: slots 0..3 hold
 // rows 4 (g % 16) + 0..3 of the head and slots 4..7 their rotation partners
 // 64 rows on, so both halves of every RoPE pair meet in the workgroup's table.
-template <int NT, int SP, int R, int NW, bool STAGE, bool SWI = false, bool ROPE = false>
+template <int NT, int SP, int R, int NW, bool STAGE, bool SWI = false, bool ROPE = false, bool RMS = false>
 __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd,
     const float* residual, float* y, int64_t ldy, int S, int8_t* __restrict__ oq,
-    float* __restrict__ od, RopeParam<ROPE> ra) {
+    float* __restrict__ od, RopeParam<ROPE> ra, RmsParam<RMS> rn) {
   static_assert(!SWI || (SP == 1 && R == 1 && NW == 8 && STAGE), "SwiGLU output: one chunk, staged");
   static_assert(!ROPE || (SP == 1 && R == 1 && NW == 8 && STAGE && !SWI), "RoPE epilogue: one chunk, staged");
+  static_assert(!RMS || (SP == 1 && R == 1 && NW == 8 && STAGE && NT <= 4), "RMS prologue: one chunk, staged");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   // chunk sums of the last kTable items, [item % kTable][wave][row * NT + token];
   // written without barriers (one row per item), combined and stored every
@@ -390,7 +296,49 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
         dma_segment(w + (int64_t)(r0 + r) * row_bytes + (int64_t)chunk * SEG, l + r * SEG, seg_bytes, lane);
   };
 
-  if constexpr (STAGE) {
+  // weight items issued before the loop (the RMS prologue keeps both ring
+  // slots in flight while it computes)
+  constexpr int kPre = RMS ? kRing : kRing - 1;
+  if constexpr (RMS) {
+    // this workgroup's own q8 blocks of rmsnorm(x): the rows are loaded (and
+    // waited for) before any weight goes out, so that the weights' DMAs,
+    // issued next, stay in flight while the norm and the quantization run
+    __shared__ float part[NT][16];
+    float va[NT][4], vb[NT][4], gm[2][4];
+    // every load in bounds (indices past the row read its last element) and
+    // unconditional, so they all go out back to back; the values past the
+    // row are zeroed after the wait
+    const int Ki = (int)K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ia = min(j * 1024 + (int)threadIdx.x, Ki - 1), ib = min(j * 1024 + (int)threadIdx.x + 512, Ki - 1);
+      gm[0][j] = rn.gamma[ia];
+      gm[1][j] = rn.gamma[ib];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float* xr = rn.x + (int64_t)t * rn.ldx;
+        va[t][j] = xr[ia];
+        vb[t][j] = xr[ib];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      asm volatile("" ::"v"(gm[0][j]), "v"(gm[1][j]));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" ::"v"(va[t][j]), "v"(vb[t][j]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool oka = j * 1024 + (int)threadIdx.x < Ki, okb = j * 1024 + (int)threadIdx.x + 512 < Ki;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        va[t][j] = oka ? va[t][j] : 0.0f;
+        vb[t][j] = okb ? vb[t][j] : 0.0f;
+      }
+    }
+    for (int d = 0; d < kPre; ++d) issue(d);
+    rms_to_stage<NT>(rn, K, va, vb, gm, stage, part);
+  } else if constexpr (STAGE) {
     // The workgroup's activation copies, as a list of (chunk, token, part)
     // with parts 0..3 the 1 KiB quarters of the codes and parts 4..5 the two
     // 256-byte halves of the scales (4-byte DMAs: scales are only 4-byte
@@ -418,18 +366,25 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     }
   }
 
-  for (int d = 0; d < kRing - 1; ++d) issue(d);
+  if constexpr (!RMS) {
+    for (int d = 0; d < kPre; ++d) issue(d);
+  }
 
   uint32_t act[NT][kPairDw];
   float dxA[NT], dxB[NT];
   if constexpr (STAGE) {
-    // own copies landed (only the weights of the items issued above may be
-    // younger), then everyone's
-    int younger = 0;
+    if constexpr (RMS) {
+      // every wave's quantized blocks are in the stage
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      // own copies landed (only the weights of the items issued above may be
+      // younger), then everyone's
+      int younger = 0;
 #pragma unroll
-    for (int d = 0; d < kRing - 1; ++d) younger += ins_of(d);
-    wait_vmcnt_rt(younger);
-    asm volatile("s_barrier" ::: "memory");
+      for (int d = 0; d < kPre; ++d) younger += ins_of(d);
+      wait_vmcnt_rt(younger);
+      asm volatile("s_barrier" ::: "memory");
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int c = pv ? chunk : 0;
@@ -484,43 +439,9 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   }
 
   // ROPE epilogue for output v of row `row`, token t, whose RoPE partner
-  // (64 rows away in the same head) has output pv: the arithmetic of
-  // k_rope_kv_step (same angles, same rotation, same fp16 rounding).
+  // (64 rows away in the same head) has output pv
   auto rope_out = [&](float v, float pv, int row, int t) {
-   if constexpr (ROPE) {
-    const int hd = row >> 7, d = row & 127, ip = d & 63;
-    const bool lo = d < 64;
-    float r = v;
-    if (hd < ra.n_heads + ra.n_kv) {
-      float c, s;
-      if (ra.tab_mode == 2) {
-        c = ra.cs_tab[2 * (t * 64 + ip)];
-        s = ra.cs_tab[2 * (t * 64 + ip) + 1];
-      } else {
-        rope_angle(ra.pos[t], ip, 128, ra.theta, &c, &s);
-        if (ra.tab_mode == 1 && hd == 0 && lo) {
-          ra.cs_tab[2 * (t * 64 + ip)] = c;
-          ra.cs_tab[2 * (t * 64 + ip) + 1] = s;
-        }
-      }
-      float y0, y1;
-      rope_rotate(lo ? v : pv, lo ? pv : v, c, s, &y0, &y1);
-      r = lo ? y0 : y1;
-    }
-    y[(int64_t)t * ldy + row] = hd < ra.n_heads ? r : v;
-    if (hd >= ra.n_heads) {
-      int sq = 0;
-#pragma unroll
-      for (int i = 1; i < SD_MAX_SEQS; ++i)
-        if (i < ra.seqs.n_seq && t >= ra.seqs.s[i].row0) sq = i;
-      const SeqArg& a = ra.seqs.s[sq];
-      const int64_t crow = seq_row(a, a.ctx_len - a.n_new + (t - a.row0));
-      const bool is_k = hd < ra.n_heads + ra.n_kv;
-      const int g = hd - ra.n_heads - (is_k ? 0 : ra.n_kv);
-      uint16_t* dst = (is_k ? a.k_w : a.v_w) + crow * a.ld_tok + (int64_t)g * a.ld_head + d;
-      *dst = f32_to_f16_bits(r);
-    }
-   }
+    if constexpr (ROPE) rope_epilogue(ra, v, pv, row, t, y, ldy);
   };
 
   // Combines and stores the outputs of items [kb, kb + cnt): each row gets its
@@ -547,7 +468,7 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
 
   int kb = 0;
   for (int k = 0; k < iters; ++k) {
-    issue(k + kRing - 1);
+    if (k + kRing - 1 >= kPre) issue(k + kRing - 1);
     // wait for item k: the only VMEM operations younger than its DMAs are the
     // DMAs of the items issued after it (and, with SWI, the block stores below;
     // no other global store happens in the loop)
@@ -614,12 +535,7 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
           const int kb8 = k - 7;
           const float g = table[(kb8 + (i >> 3)) % kTable][i & 7][t];
           const float up = table[(kb8 + 4 + (i >> 3)) % kTable][i & 7][t];
-          const float silu = fdiv(g, fadd(1.0f, expf(-g)));
-          const float m = fmul(silu, up);
-          const float amax = group_max<32>(fabsf(m));
-          const float d = q8_scale(amax);
-          oq[(int64_t)t * F + 32 * u + i] = (int8_t)q8_code(m, d);
-          if (i == 0) od[(int64_t)t * units + u] = d;
+          swiglu_epilogue(g, up, t, i, u, F, units, oq, od);
         }
       }
     } else if (k - kb == kTable - 1) {
@@ -976,19 +892,22 @@ hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, 
   return hipGetLastError();
 }
 
-template <int NT, int SP, int NW, bool STAGE, bool SWI = false, bool ROPE = false>
+template <int NT, int SP, int NW, bool STAGE, bool SWI = false, bool ROPE = false, bool RMS = false>
 hipError_t launch_dma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                       const float* xd, const float* residual, float* y, int64_t ldy, hipStream_t st,
-                      int8_t* oq = nullptr, float* od = nullptr, const RopeArgs* ra = nullptr) {
+                      int8_t* oq = nullptr, float* od = nullptr, const RopeArgs* ra = nullptr,
+                      const RmsArgs* rms = nullptr) {
   constexpr int R = dma_rows(NT);
   // rings and staged activations take up to 140 KiB
-  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>>(); e != hipSuccess)
+  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE, RMS>>(); e != hipSuccess)
     return e;
   RopeParam<ROPE> rp{};
   if constexpr (ROPE) rp = *ra;
-  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
+  RmsParam<RMS> rn{};
+  if constexpr (RMS) rn = *rms;
+  hipLaunchKernelGGL((k_qgemv_q8_0_dma<NT, SP, R, NW, STAGE, SWI, ROPE, RMS>), dim3(pl.grid), dim3(64 * NW), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
-                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od, rp);
+                     xq, K, xd, residual, y, ldy, pl.chunks, oq, od, rp, rn);
   return hipGetLastError();
 }
 
@@ -1130,15 +1049,25 @@ bool swiglu_fusable(int64_t F, int64_t K, int n_tok) {
   return pl.use_reg && pl.stage && pl.sp == 1;
 }
 
+// The RMS prologue pays only for one row: every workgroup normalizes and
+// quantizes every row itself, and with two or more rows that work outweighs
+// the launch it saves (decode at 2 / 3 / 4 sequences: 820 / 973 / 1000 tok/s
+// with it against 834 / 1052 / 1099 without; one sequence: 461 against 437).
+bool rms_fusable(int64_t K, int n_tok) { return K <= 4096 && n_tok == 1; }
+
 hipError_t launch_qgemv_swiglu(const void* w, int64_t F, int64_t K, const int8_t* xq, const float* xd,
-                               int n_tok, int8_t* oq, float* od, hipStream_t st) {
+                               int n_tok, int8_t* oq, float* od, hipStream_t st, const RmsArgs* rms) {
   if (!swiglu_fusable(F, K, n_tok)) return hipErrorInvalidValue;
+  if (rms && !rms_fusable(K, n_tok)) return hipErrorInvalidValue;
   GemvPlan pl;
   plan_qgemv(2 * F, K, n_tok, SD_GEMV_NARROW, &pl);
   // one unit (32 gate rows and their 32 up rows, 8 items per wave) at a time
   const int64_t units = F / 32;
   const int64_t per = (units + 255) / 256;
   pl.grid = (int)((units + per - 1) / per);
+  if (rms)
+    return launch_dma<1, 1, 8, true, true, false, true>(pl, w, 2 * F, K, nullptr, nullptr, nullptr, nullptr, 0, st,
+                                                         oq, od, nullptr, rms);
   switch (n_tok) {
 #define SD_CASE(n) \
   case n: return launch_dma<n, 1, 8, true, true>(pl, w, 2 * F, K, xq, xd, nullptr, nullptr, 0, st, oq, od);
@@ -1160,14 +1089,19 @@ bool qkv_rope_fusable(int64_t N, int64_t K, int n_tok) {
 }
 
 hipError_t launch_qgemv_qkv_rope(const void* w, int64_t N, int64_t K, const int8_t* xq, const float* xd,
-                                 int n_tok, float* y, int64_t ldy, const RopeArgs& ra, hipStream_t st) {
+                                 int n_tok, float* y, int64_t ldy, const RopeArgs& ra, hipStream_t st,
+                                 const RmsArgs* rms) {
   if (!qkv_rope_fusable(N, K, n_tok)) return hipErrorInvalidValue;
+  if (rms && !rms_fusable(K, n_tok)) return hipErrorInvalidValue;
   GemvPlan pl;
   plan_qgemv(N, K, n_tok, SD_GEMV_NARROW, &pl);
   // one pair group (8 rows) per item, as many items per workgroup as the plain launch
   const int64_t groups = N / 8;
   const int64_t per = (groups + 255) / 256;
   pl.grid = (int)((groups + per - 1) / per);
+  if (rms)
+    return launch_dma<1, 1, 8, true, false, true, true>(pl, w, N, K, nullptr, nullptr, nullptr, y, ldy, st, nullptr,
+                                                         nullptr, &ra, rms);
   switch (n_tok) {
 #define SD_CASE(n) \
   case n: return launch_dma<n, 1, 8, true, false, true>(pl, w, N, K, xq, xd, nullptr, y, ldy, st, nullptr, nullptr, &ra);
@@ -1175,6 +1109,18 @@ hipError_t launch_qgemv_qkv_rope(const void* w, int64_t N, int64_t K, const int8
 #undef SD_CASE
     default: return hipErrorInvalidValue;
   }
+}
+
+// y = W q8(rmsnorm(x)) with the norm computed by every workgroup of the
+// projection (the output head of the step): the staged one-chunk streaming
+// kernel, K <= 4096, one row; else hipErrorInvalidValue.
+hipError_t launch_qgemv_rms(const void* w, int64_t N, int64_t K, const RmsArgs& rms, int n_tok, float* y,
+                            int64_t ldy, hipStream_t st) {
+  GemvPlan pl;
+  if (!rms_fusable(K, n_tok) || !plan_qgemv(N, K, n_tok, SD_GEMV_NARROW, &pl)) return hipErrorInvalidValue;
+  if (!pl.use_reg || !pl.stage || pl.sp != 1) return hipErrorInvalidValue;
+  return launch_dma<1, 1, 8, true, false, false, true>(pl, w, N, K, nullptr, nullptr, nullptr, y, ldy, st, nullptr,
+                                                        nullptr, nullptr, &rms);
 }
 
 }  // namespace sd

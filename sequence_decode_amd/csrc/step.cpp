@@ -180,6 +180,15 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
   // kernel allows it (fp16 caches, whole 128-dim heads rotated, 1..8 rows)
   bool qkv_rope = D == 128 && (m->n_rot == 0 || m->n_rot == D) && qkv_rope_fusable(QKV, H, n);
   for (int s = 0; s < n_seq; ++s) qkv_rope = qkv_rope && !sa.s[s].q8;
+  // the RMSNorm before the QKV, gate|up and output projections computed by
+  // those projections' own workgroups (one row, hidden <= 4096): one launch
+  // instead of two, the same codes and scales
+  const bool rms_in = rms_fusable(H, n);
+  GemvPlan qkv_plan, head_plan;
+  const bool qkv_rms_plain = rms_in && plan_qgemv(QKV, H, n, SD_GEMV_NARROW, &qkv_plan) && qkv_plan.use_reg &&
+                             qkv_plan.stage && qkv_plan.sp == 1;
+  const bool head_rms = rms_in && plan_qgemv(m->vocab, H, n, SD_GEMV_NARROW, &head_plan) && head_plan.use_reg &&
+                        head_plan.stage && head_plan.sp == 1;
   SD_TRY(launch_embed(m->tok_embd, m->vocab, H, io->tokens, n, x, st));
   for (int l = 0; l < m->n_layers; ++l) {
     const sd_layer_weights& L = m->layers[l];
@@ -198,32 +207,49 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
         sa.s[s].v_w = q.v_cache + off;
       }
     }
-    SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
+    const RmsArgs attn_rms{x, H, L.attn_norm, m->rms_eps};
+    if (!rms_in) SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
     if (qkv_rope) {
       // RoPE and the fp16 K/V write in the projection's epilogue (one launch)
       RopeArgs ra{io->positions, m->rope_theta, rope_tab, l == 0 ? 1 : 2, Hq, Hkv, sa};
-      SD_TRY(launch_qgemv_qkv_rope(L.w_qkv, QKV, H, aq, ad, n, qkv, QKV, ra, st));
+      SD_TRY(launch_qgemv_qkv_rope(L.w_qkv, QKV, H, aq, ad, n, qkv, QKV, ra, st, rms_in ? &attn_rms : nullptr));
     } else {
-      SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
+      if (qkv_rms_plain) {
+        SD_TRY(launch_qgemv_rms(L.w_qkv, QKV, H, attn_rms, n, qkv, QKV, st));
+      } else {
+        if (rms_in) SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.attn_norm, m->rms_eps, aq, ad, nullptr, st));
+        SD_TRY(launch_qgemv(L.w_qkv, QKV, H, aq, ad, n, nullptr, qkv, QKV, st));
+      }
       SD_TRY(launch_rope_kv_step(qkv, QKV, n, Hq, Hkv, D, m->n_rot ? m->n_rot : D, io->positions,
                                  m->rope_theta, sa, rope_tab, l == 0 ? 1 : 2, st));
     }
     SD_TRY(launch_attn(qkv, QKV, sa, Hq, Hkv, scale, attn_o, part, aq, ad, st));
     SD_TRY(launch_qgemv(L.w_o, H, HqD, aq, ad, n, x, x, H, st));
-    SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));
-    if (fuse_swiglu) {
+    const RmsArgs ffn_rms{x, H, L.ffn_norm, m->rms_eps};
+    if (fuse_swiglu && rms_in) {
+      // RMSNorm, gate|up and SwiGLU in one launch
+      SD_TRY(launch_qgemv_swiglu(L.w_gate_up, F, H, nullptr, nullptr, n, fq, fd, st, &ffn_rms));
+      SD_TRY(launch_qgemv(L.w_down, H, F, fq, fd, n, x, x, H, st));
+    } else if (fuse_swiglu) {
       // gate|up and SwiGLU in one launch; its q8 output goes to the (here
       // unused) gate|up region, since the launch still reads aq / ad
+      SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));
       SD_TRY(launch_qgemv_swiglu(L.w_gate_up, F, H, aq, ad, n, fq, fd, st));
       SD_TRY(launch_qgemv(L.w_down, H, F, fq, fd, n, x, x, H, st));
     } else {
+      SD_TRY(launch_rmsnorm_q8(x, H, n, H, L.ffn_norm, m->rms_eps, aq, ad, nullptr, st));
       SD_TRY(launch_qgemv(L.w_gate_up, 2 * (int64_t)F, H, aq, ad, n, nullptr, gu, 2 * (int64_t)F, st));
       SD_TRY(launch_swiglu_q8(gu, 2 * (int64_t)F, n, F, aq, ad, nullptr, st));
       SD_TRY(launch_qgemv(L.w_down, H, F, aq, ad, n, x, x, H, st));
     }
   }
-  SD_TRY(launch_rmsnorm_q8(x, H, n, H, m->out_norm, m->rms_eps, aq, ad, nullptr, st));
-  SD_TRY(launch_qgemv(m->w_lm_head, m->vocab, H, aq, ad, n, nullptr, io->logits, m->vocab, st));
+  if (head_rms) {
+    SD_TRY(launch_qgemv_rms(m->w_lm_head, m->vocab, H, RmsArgs{x, H, m->out_norm, m->rms_eps}, n, io->logits,
+                            m->vocab, st));
+  } else {
+    SD_TRY(launch_rmsnorm_q8(x, H, n, H, m->out_norm, m->rms_eps, aq, ad, nullptr, st));
+    SD_TRY(launch_qgemv(m->w_lm_head, m->vocab, H, aq, ad, n, nullptr, io->logits, m->vocab, st));
+  }
   SD_TRY(launch_argmax(io->logits, m->vocab, n, m->vocab, io->next_tokens, ws + W.arg, st));
 #undef SD_TRY
   return SD_OK;

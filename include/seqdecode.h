@@ -49,7 +49,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 7
+#define SD_ABI_VERSION 8
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -393,6 +393,17 @@ size_t sd_argmax_workspace_bytes(int n_tok, int64_t V);
  */
 int sd_argmax_rows(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
                    void* ws, size_t ws_bytes, sd_stream_t stream);
+
+/* ------------------------------------------------------------ measurement
+ * sd_hbm_stream_read -- reads every byte of buf once (16-byte non-temporal
+ * loads, the cache policy of the GEMV's weight stream) and writes nothing
+ * but, in a case no real buffer hits, a word of sink.  Not part of the decode
+ * step: the plain streaming read that the GEMV and attention kernels'
+ * bandwidth is compared with, timed by the caller.
+ *   buf   16-byte aligned device buffer of bytes bytes (bytes % 16 == 0, >= 16).
+ *   sink  64 uint32 of device memory (contents unspecified afterwards).
+ */
+int sd_hbm_stream_read(const void* buf, size_t bytes, uint32_t* sink, sd_stream_t stream);
 
 /* ------------------------------------------------------- the decode step */
 

@@ -27,6 +27,7 @@ SIGNATURES = {
     "sd_swiglu_q8": ([P, i64, i32, i64, P, P, P, P], i32),
     "sd_qgemv_q8_0_swiglu_q8": ([P, i64, i64, P, P, i32, P, P, P], i32),
     "sd_embed_f16": ([P, i64, i64, P, i32, P, P], i32),
+    "sd_hbm_stream_read": ([P, sz, P, P], i32),
     "sd_argmax_workspace_bytes": ([i32, i64], sz),
     "sd_argmax_rows": ([P, i64, i32, i64, P, P, sz, P], i32),
     "sd_decode_step_workspace_bytes": ([P, i32, i32], sz),

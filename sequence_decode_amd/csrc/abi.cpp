@@ -302,6 +302,12 @@ int sd_embed_f16(const uint16_t* table, int64_t V, int64_t H, const int32_t* tok
   return from_hip(launch_embed(table, V, H, tokens, n_tok, x, hs(stream)));
 }
 
+int sd_hbm_stream_read(const void* buf, size_t bytes, uint32_t* sink, sd_stream_t stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return SD_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return SD_EALIGN;
+  return from_hip(launch_stream_read(buf, bytes, sink, hs(stream)));
+}
+
 size_t sd_argmax_workspace_bytes(int n_tok, int64_t V) {
   if (n_tok < 1 || n_tok > 65535 || V < 1 || V > INT32_MAX - 1) return 0;
   return argmax_ws_bytes(n_tok, V);

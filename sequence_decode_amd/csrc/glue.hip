@@ -243,4 +243,46 @@ hipError_t launch_argmax(const float* logits, int64_t ld, int n_tok, int64_t V, 
   return hipGetLastError();
 }
 
+namespace {
+
+// ---------------------------------------------------------------------------
+// Plain streaming read: every 16-byte word of the buffer loaded once
+// (non-temporal, as the GEMV streams its weights), folded by XOR into a
+// register that is stored only if it equals a value no real buffer gives, so
+// the loads cannot be dropped.  Eight words in flight per thread; workgroups
+// take contiguous 64 KiB tiles in grid-stride order.  The achievable-bandwidth
+// reference for the kernels above; not part of the decode step.
+constexpr int kReadTile = 65536;
+
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4a* __restrict__ buf, int64_t words,
+                                                     uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const int64_t tile_words = kReadTile / 16;
+  for (int64_t t0 = (int64_t)blockIdx.x * tile_words; t0 < words; t0 += (int64_t)gridDim.x * tile_words) {
+    const int64_t end = t0 + tile_words < words ? t0 + tile_words : words;
+    for (int64_t i = t0 + threadIdx.x; i < end; i += 8 * 256) {
+      u32x4a v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t k = i + (int64_t)u * 256;
+        v[u] = k < end ? __builtin_nontemporal_load(buf + k) : u32x4a{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  }
+  if (acc == 0x9E3779B9u && threadIdx.x == 0) sink[blockIdx.x & 63] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const int64_t words = (int64_t)(bytes / 16);
+  const int64_t tiles = (int64_t)((bytes + kReadTile - 1) / kReadTile);
+  const int64_t grid = tiles < 2048 ? (tiles > 0 ? tiles : 1) : 2048;  // at most 8 workgroups per CU
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, st, static_cast<const u32x4a*>(buf),
+                     words, sink);
+  return hipGetLastError();
+}
+
 }  // namespace sd

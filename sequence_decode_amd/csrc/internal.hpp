@@ -189,6 +189,9 @@ hipError_t launch_swiglu_q8(const float* gu, int64_t ldgu, int n_tok, int64_t F,
                             float* xd, float* y, hipStream_t st);
 hipError_t launch_embed(const uint16_t* table, int64_t V, int64_t H, const int32_t* tokens,
                         int n_tok, float* x, hipStream_t st);
+// Plain streaming read of bytes (a multiple of 16) from a 16-byte aligned
+// buffer: the achievable-bandwidth reference; sink gets 64 words at most.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 size_t argmax_ws_bytes(int n_tok, int64_t V);
 hipError_t launch_argmax(const float* logits, int64_t ld, int n_tok, int64_t V, int32_t* out,
                          void* ws, hipStream_t st);

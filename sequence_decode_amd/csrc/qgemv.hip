@@ -296,9 +296,12 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
         dma_segment(w + (int64_t)(r0 + r) * row_bytes + (int64_t)chunk * SEG, l + r * SEG, seg_bytes, lane);
   };
 
-  // weight items issued before the loop (the RMS prologue keeps both ring
-  // slots in flight while it computes)
-  constexpr int kPre = RMS ? kRing : kRing - 1;
+  // weight items issued before the loop: both ring slots where the start
+  // waits on something else anyway (the RMS prologue's arithmetic, the
+  // per-wave activation loads), one where the staged copies are all it waits
+  // for (a second item in flight there measured slower: QKV 7.3 -> 8.1 us,
+  // O 5.8 -> 7.1 us at 4 tokens)
+  constexpr int kPre = (RMS || !STAGE) ? kRing : kRing - 1;
   if constexpr (RMS) {
     // this workgroup's own q8 blocks of rmsnorm(x): the rows are loaded (and
     // waited for) before any weight goes out, so that the weights' DMAs,
@@ -366,12 +369,48 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     }
   }
 
+  uint32_t act[NT][kPairDw];
+  float dxA[NT], dxB[NT];
+  if constexpr (!STAGE) {
+    // this lane's pair of activations for every token, loaded before any
+    // weight goes out (a load behind the weight DMAs would wait for them);
+    // unconditional (lanes past the row read pair 0 and zero it), so that the
+    // loads of all tokens go out back to back
+    const int64_t pp = pv ? (int64_t)p : 0;
+    u32x4a raw[NT][4];
+    float rA[NT], rB[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4a* src = reinterpret_cast<const u32x4a*>(xq + (int64_t)t * K + 64 * pp);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) raw[t][v] = src[v];
+      rA[t] = xd[(int64_t)t * nb + 2 * pp];
+      rB[t] = xd[(int64_t)t * nb + 2 * pp + 1];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t a[16];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        a[4 * v + 0] = pv ? raw[t][v].x : 0u;
+        a[4 * v + 1] = pv ? raw[t][v].y : 0u;
+        a[4 * v + 2] = pv ? raw[t][v].z : 0u;
+        a[4 * v + 3] = pv ? raw[t][v].w : 0u;
+      }
+      act[t][0] = a[0] << 16;
+#pragma unroll
+      for (int c = 1; c < 8; ++c) act[t][c] = (a[c - 1] >> 16) | (a[c] << 16);
+      act[t][8] = a[7] >> 16;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) act[t][9 + c] = a[8 + c];
+      dxA[t] = pv ? rA[t] : 0.0f;
+      dxB[t] = pv ? rB[t] : 0.0f;
+    }
+  }
   if constexpr (!RMS) {
     for (int d = 0; d < kPre; ++d) issue(d);
   }
 
-  uint32_t act[NT][kPairDw];
-  float dxA[NT], dxB[NT];
   if constexpr (STAGE) {
     if constexpr (RMS) {
       // every wave's quantized blocks are in the stage
@@ -407,34 +446,6 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
       act[t][8] = a[7] >> 16;
 #pragma unroll
       for (int c2 = 0; c2 < 8; ++c2) act[t][9 + c2] = a[8 + c2];
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (pv) {
-        const u32x4a* src = reinterpret_cast<const u32x4a*>(xq + (int64_t)t * K + 64 * (int64_t)p);
-        uint32_t a[16];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          u32x4a q = src[v];
-          a[4 * v + 0] = q.x;
-          a[4 * v + 1] = q.y;
-          a[4 * v + 2] = q.z;
-          a[4 * v + 3] = q.w;
-        }
-        act[t][0] = a[0] << 16;
-#pragma unroll
-        for (int c = 1; c < 8; ++c) act[t][c] = (a[c - 1] >> 16) | (a[c] << 16);
-        act[t][8] = a[7] >> 16;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) act[t][9 + c] = a[8 + c];
-        dxA[t] = xd[(int64_t)t * nb + 2 * p];
-        dxB[t] = xd[(int64_t)t * nb + 2 * p + 1];
-      } else {
-#pragma unroll
-        for (int c = 0; c < kPairDw; ++c) act[t][c] = 0u;
-        dxA[t] = dxB[t] = 0.0f;
-      }
     }
   }
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 7
+    assert L.sd_abi_version() == 8
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -80,6 +80,15 @@ def test_gemv_swiglu_rejections(L):
     assert f(FAKE, 64, 4096, FAKE, FAKE, 9, FAKE, FAKE, None) == SD_EUNSUPPORTED   # > 8 tokens
     assert f(ODD, 64, 256, FAKE, FAKE, 1, FAKE, FAKE, None) == SD_EALIGN
     assert f(FAKE, 64, 256, ODD, FAKE, 1, FAKE, FAKE, None) == SD_EALIGN
+
+
+def test_stream_read_rejections(L):
+    r = L.sd_hbm_stream_read
+    assert r(None, 64, FAKE, None) == SD_EINVAL
+    assert r(FAKE, 0, FAKE, None) == SD_EINVAL
+    assert r(FAKE, 40, FAKE, None) == SD_EINVAL
+    assert r(FAKE, 64, None, None) == SD_EINVAL
+    assert r(ctypes.c_void_p(0x10008), 64, FAKE, None) == SD_EALIGN
 
 
 def test_quantize_rejections(L):

@@ -125,3 +125,21 @@ def test_embed_and_argmax(sd):
     got = host(sd.argmax_rows(dev(logits)))
     assert np.array_equal(got, oracle.argmax_rows(logits))
     assert got[1] == 5 and got[2] == 0 and got[3] == 151935
+
+
+def test_stream_read_runs_and_writes_nothing(sd):
+    """The streaming-read reference kernel reads a buffer (no output beyond the
+    sink word it writes only for one magic fold value) and leaves the buffer
+    untouched."""
+    import torch
+    say("stream read")
+    buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda")   # 1 MiB, fold != magic
+    before = buf.clone()
+    sink = torch.full((64,), 7, dtype=torch.int32, device="cuda")
+    lib = sd._lib.load()
+    import ctypes
+    rc = lib.sd_hbm_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4,
+                                ctypes.c_void_p(sink.data_ptr()), None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before) and torch.all(sink == 7)

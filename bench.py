@@ -683,6 +683,84 @@ def oracle_attention_and_step(torch, budget_steps=4):
     return out
 
 
+def trace_summary(trace_db, fetch_db=None, write_db=None, n_tok=4):
+    """Summary (markdown) of rocprofv3 results databases of `bench.py
+    --sweep-only --calibrate-copy`: per-kernel statistics of the trace, and
+    for the launches the roofline pass times (per shape, the 128 timed ones of
+    its 160, in launch order: QKV, O, gate|up on the staged one-chunk kernel,
+    down on the four-chunk one) their average trace duration and, from the
+    counter runs, their HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB) scaled by
+    what the same counters read for the 1 GiB calibration copy."""
+    import hashlib
+    import sqlite3
+    import statistics
+
+    def dispatches(db, pmc=None):
+        con = sqlite3.connect(db)
+        if pmc is None:
+            q = ("select k.display_name, d.start, d.end from rocpd_kernel_dispatch d join "
+                 "rocpd_info_kernel_symbol k on d.kernel_id = k.id order by d.start")
+            return [(n, (e - s_) / 1e3) for n, s_, e in con.execute(q)]
+        q = "select name, counter_value from pmc_events where counter_name = ? order by dispatch_id"
+        return list(con.execute(q, (pmc,)))
+
+    def short(name):
+        name = name.replace("void ", "", 1)
+        name = name.replace("sd::(anonymous namespace)::", "")
+        i = name.find("(")
+        return name[:i] if i > 0 else name
+
+    staged = f"k_qgemv_q8_0_dma<{n_tok}, 1, 1, 8, true, false, false, false>"
+    four = f"k_qgemv_q8_0_dma<{n_tok}, 4, 1, 4, false, false, false, false>"
+
+    def roofline_launches(rows):
+        a = [v for n, v in rows if short(n) == staged][-480:]
+        b = [v for n, v in rows if short(n) == four][-160:]
+        if len(a) < 480 or len(b) < 160:
+            raise RuntimeError("the database does not hold the roofline pass")
+        return {"qkv": a[32:160], "o": a[192:320], "gate_up": a[352:480], "down": b[32:160]}
+
+    tr = dispatches(trace_db)
+    per = {}
+    for n, us in tr:
+        per.setdefault(short(n), []).append(us)
+    lines = ["| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))[:24]:
+        lines.append(f"| {k[:110]} | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{sum(v) / 1e3:.2f} |")
+    roof = roofline_launches(tr)
+    shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
+    out = {"kernel_stats": "\n".join(lines), "per_shape": {}}
+    tot_us, tot_b = 0.0, 0
+    for k, v in roof.items():
+        N, K = shapes[k]
+        b = gemv_bytes(N, K, n_tok)
+        out["per_shape"][k] = {"trace_avg_us": round(statistics.mean(v), 3), "GB_s": round(b / statistics.mean(v) / 1e3, 1)}
+        tot_us += sum(v)
+        tot_b += b * len(v)
+    out["trace_avg_us_per_launch"] = round(tot_us / 512, 3)
+    out["trace_launches"] = 512
+    out["achieved_GB_s"] = round(tot_b / tot_us / 1e3, 1)
+    out["gemv_us_per_sweep"] = round(sum(statistics.mean(v) for v in roof.values()) * N_LAYERS, 1)
+    if fetch_db and write_db:
+        f = dispatches(fetch_db, "FETCH_SIZE")
+        w = dispatches(write_db, "WRITE_SIZE")
+        fcal = [v for n, v in f if "copyBuffer" in n]
+        wcal = [v for n, v in w if "copyBuffer" in n]
+        ff = (1 << 30) / (fcal[-1] * 1024)
+        wf = (1 << 30) / (wcal[-1] * 1024)
+        rf, rw = roofline_launches(f), roofline_launches(w)
+        fetched = sum(sum(v) for v in rf.values()) * 1024 * ff / 512
+        written = sum(sum(v) for v in rw.values()) * 1024 * wf / 512
+        out["fetch_factor"], out["write_factor"] = round(ff, 4), round(wf, 4)
+        out["traffic_bytes_per_launch"] = int(round(fetched + written))
+        out["algorithmic_bytes_per_launch"] = int(round(tot_b / 512))
+        out["traffic_over_algorithmic"] = round((fetched + written) / (tot_b / 512), 4)
+    src = os.path.join(ROOT, "sequence_decode_amd", "csrc", "qgemv.hip")
+    out["kernel_source_sha256"] = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -704,7 +782,13 @@ def main():
                     help="only the projection sweeps and the per-shape event pass (for a kernel trace)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for byte counters)")
+    ap.add_argument("--trace-summary", nargs="+", metavar="DB",
+                    help="summarize rocprofv3 results databases of a --sweep-only run: the kernel-trace "
+                         "database, then optionally the FETCH_SIZE and WRITE_SIZE ones (no GPU used)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(json.dumps(trace_summary(*args.trace_summary[:3], n_tok=args.n_tok), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode step here is built and measured on a "
               "single MI355X; run it with --gpus 1", file=sys.stderr)

@@ -49,7 +49,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 8
+#define SD_ABI_VERSION 9
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -61,10 +61,16 @@ int sd_abi_version(void);
  * max 4); "feat(qwen4exp): exact 4-slot concurrent serving", "What" (more than
  * four is refused). */
 #define SD_MAX_SEQS 4
-/* Keys per attention chunk.  Fixed, so a sequence's split depends on its own
- * length only. */
+/* Attention chunks (the units of the split over keys), fixed in absolute
+ * positions so that a token's split depends on its own position only:
+ * positions below SD_ATTN_SMALL_SPAN in chunks of SD_ATTN_SMALL_CHUNK keys
+ * (a short context still spreads over the whole GPU), later positions in
+ * chunks of SD_ATTN_CHUNK keys. */
 #define SD_ATTN_CHUNK 256
-/* Longest context one attention call takes (2048 chunks). */
+#define SD_ATTN_SMALL_CHUNK 64
+#define SD_ATTN_SMALL_SPAN 2048
+/* Most keys one attention token attends to (the span from its lowest key to
+ * its own position). */
 #define SD_MAX_CTX (2048 * SD_ATTN_CHUNK)
 
 /* ------------------------------------------------------------------ q8 data
@@ -257,8 +263,9 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  * walkthrough / CUDA kernels": multi-sequence decode attention).
  * For sequence s and query head h (KV head g = h / (H_q/H_kv)):
  *   out[s][h] = sum_j softmax_j(scale * q[s][h] . k_j) v_j,  j < ctx_len_s.
- * fp32 throughout (online softmax over fixed SD_ATTN_CHUNK-key chunks, merged
- * in chunk order), so a sequence's bits do not depend on the others.
+ * fp32 throughout (a softmax partial per chunk of the fixed position grid of
+ * SD_ATTN_SMALL_CHUNK / SD_ATTN_CHUNK keys, merged with fixed reduction
+ * shapes), so a sequence's bits do not depend on the others.
  *   q    [n_seq][H_q][D] fp32 at sequence stride ld_q (elements), 16-byte aligned.
  *   out  [n_seq][H_q][D] fp32 contiguous, 16-byte aligned.
  *   ws   workspace of at least sd_decode_attn_workspace_bytes(), 16-byte aligned.
@@ -290,7 +297,7 @@ int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* view
  * those of sd_decode_attn_multiseq, plus SD_EWORKSPACE when
  * sd_decode_attn_workspace_bytes() for these views exceeds
  * SD_ATTN_SCRATCH_BYTES (checked before any HIP call; e.g. 32 query heads fit
- * 992 chunks of SD_ATTN_CHUNK keys summed over the sequences).  Every call on
+ * 992 chunk partials per head summed over the sequences and their tokens).  Every call on
  * one GPU shares that GPU's array and leaves its partials there: calls that
  * overlap on one GPU (on different streams, or from several host threads
  * without ordering) race and give undefined results.  The first call on a

@@ -16,13 +16,15 @@ __all__ = [
     "decode_attn_multiseq_noalloc", "ATTN_SCRATCH_BYTES",
     "decode_attn_verify", "ATTN_MAX_NEW",
     "rmsnorm_q8", "swiglu_q8", "qgemv_q8_0_swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
-    "ATTN_CHUNK", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "kv_append_q8_0",
+    "ATTN_CHUNK", "ATTN_SMALL_CHUNK", "ATTN_SMALL_SPAN", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "kv_append_q8_0",
     "KV_F16", "KV_Q8_0",
 ]
 
 MAX_TOKENS = 16
 MAX_SEQS = 4
 ATTN_CHUNK = 256
+ATTN_SMALL_CHUNK = 64
+ATTN_SMALL_SPAN = 2048
 ATTN_MAX_NEW = 4
 ATTN_SCRATCH_BYTES = 16 << 20
 GEMV_AUTO, GEMV_NARROW, GEMV_MFMA = 0, 1, 2

@@ -79,9 +79,10 @@ int check_views(const sd_seqview* views, int n_seq, int D, bool attn,
       return SD_EINVAL;
     }
     if (attn) {
-      const int lo0 = v.window ? std::max(0, v.ctx_len - T - v.window + 1) : 0;
-      if ((v.ctx_len - 1) / SD_ATTN_CHUNK - lo0 / SD_ATTN_CHUNK + 1 > SD_MAX_CTX / SD_ATTN_CHUNK)
-        return SD_EUNSUPPORTED;
+      // every token's keys span at most SD_MAX_CTX positions (the newest
+      // token's span is the longest)
+      const int span = v.window ? std::min(v.ctx_len, v.window) : v.ctx_len;
+      if (span > SD_MAX_CTX) return SD_EUNSUPPORTED;
     }
     if (v.ld_head < D || v.ld_tok < D) return SD_EINVAL;
     if (v.kv_type == SD_KV_F16) {

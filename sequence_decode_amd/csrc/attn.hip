@@ -6,10 +6,14 @@
 // in one launch for all sequences ("2. Single-GPU decode batches don't
 // scale").  The layout here is CDNA4's own:
 //
-// * Work unit = (sequence, KV head, chunk of SD_ATTN_CHUNK keys).  The chunk
-//   size is fixed, so how a sequence is split depends on its own length only;
-//   the grid is the sum of all sequences' units, which fills 256 CUs even for
-//   four sequences (a sequence-per-workgroup split would give 32 units).
+// * Work unit = (sequence, KV head, chunk).  Chunks sit on a grid fixed in
+//   absolute positions: 64 keys below position 2048, 256 keys beyond, so how
+//   a token's keys are split depends on its position alone.  The grid is the
+//   sum of all sequences' units.  One CU streams only about 1/256 of the
+//   chip's HBM rate, so a short context must spread over many CUs: 2050 keys
+//   make 33 chunks x 8 KV heads = 264 workgroups of 32 KB each (with 256-key
+//   chunks: 72 of 128 KB, on 72 CUs); long contexts keep 256-key chunks, whose
+//   partials cost 3% of the cache bytes instead of 12%.
 // * A workgroup loads each key and value row of its chunk once for the four
 //   query heads that share the KV head; every load is issued before any
 //   arithmetic.  Scores and the weighted value sum both come from MFMA (fp16
@@ -22,8 +26,8 @@
 //   concurrent serving implementation with speculation"): token i at position
 //   p_i sees keys 0..p_i.  The four heads of a group times up to four tokens are
 //   the 16 columns of the MFMA tiles, and each column keeps its own key limit
-//   and its own chunk count ceil((p_i + 1) / SD_ATTN_CHUNK), so token i gets
-//   bitwise what a one-token call over p_i + 1 keys gives.
+//   and its own chunks (those of positions 0..p_i), so token i gets bitwise
+//   what a one-token call over p_i + 1 keys gives.
 // * Caches: plain (position j in row j), ring (row j % capacity, with a
 //   sliding window), or paged (a per-sequence block table into a shared pool,
 //   "feat(qwen36): complete concurrent serving implementation with
@@ -43,7 +47,6 @@ namespace sd {
 
 namespace {
 
-constexpr int C = kAttnChunk;
 constexpr int HD = kAttnHeadDim;
 constexpr int PF = kAttnPartialFloats;
 
@@ -126,8 +129,8 @@ __device__ __forceinline__ h8 codes_to_h8(uint32_t w0, uint32_t w1) {
   return h8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
 }
 
-// One workgroup = (sequence, KV head g, chunk of C keys); wave w owns keys
-// 64w .. 64w+63 of the chunk.  Both contractions run on v_mfma_f32_16x16x32_f16
+// One workgroup = (sequence, KV head g, chunk); wave w owns keys 64w .. 64w+63
+// of the chunk (a chunk of at most 64 keys is one wave's).  Both contractions run on v_mfma_f32_16x16x32_f16
 // with the four query heads of the group as the first 4 of 16 columns:
 //  * scores S^T = K q^T: A = 16 keys x 32 dims of K (fp16 as stored), B = q^T as
 //    the exact fp16 pair hi + lo of the fp32 query.  Tile t = (key block b =
@@ -160,11 +163,28 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int s = find_seq(seqs, blockIdx.x);
   const SeqArg& A = seqs.s[s];
   const int local = blockIdx.x - A.unit_begin;
-  const int g = local / A.n_chunks;
-  const int ci = local - g * A.n_chunks;  // chunk of this unit, counted from c0
-  const int c = A.c0 + ci;                // absolute chunk: positions c*C .. c*C + C-1
-  const int j0 = c * C;
-  const int nk = min(C, A.ctx_len - j0);  // keys of the chunk below ctx_len
+  const int g = local / A.units;
+  const int u = local - g * A.units;  // unit of this workgroup within KV head g
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The chunk of this wave.  Units 0 .. n_su-1 hold the chunks of the 64-key
+  // grid, A.pk of them per unit (4: one per wave; 1: wave 0's alone), the units
+  // after them one chunk each.  A chunk with at most 64 keys below ctx_len is
+  // one wave's ("small"): that wave keeps its softmax partial to itself (no
+  // barrier, no cross-wave sums) and the waves without a chunk leave at once.
+  // Which unit or wave computes a chunk changes no bits of its partial.
+  const int n_su = (A.ns + A.pk - 1) / A.pk;
+  const bool packed = u < n_su && A.pk == 4;
+  const int ci = u < n_su ? u * A.pk + (packed ? wave : 0) : A.ns + (u - n_su);  // counted from c0
+  const int c = A.c0 + ci;                // absolute chunk: positions j0 .. j0 + csz - 1
+  const int j0 = attn_chunk_begin(c);
+  const int csz = attn_chunk_size(c);
+  const int nk = min(csz, A.ctx_len - j0);  // keys of the chunk below ctx_len
+  const bool small = packed || nk <= kWaveKeys;
+  if (packed ? ci >= A.ns : small && wave != 0) return;
+  // a small chunk's wave alone in its workgroup takes the next wave's V region
+  // too and loads all its V rows at once
+  const bool alone = small && !packed;
   const int jlo = max(0, A.lo0 - j0);     // keys of the chunk below any query's window
   // ring caches: row of chunk key jl (jlo <= jl < nk) runs on from that of jlo
   // and wraps once at the ring's end (the keys in use span at most the ring)
@@ -173,12 +193,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     return r >= A.ring_cap ? r - A.ring_cap : r;
   };
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int col = lane & 15;  // MFMA row (A loads) / column (B, D)
   const int kg = lane >> 4;   // MFMA k-group
-  const int wk = wave * kWaveKeys;
+  const int wk = small ? 0 : wave * kWaveKeys;  // first key of the wave within the chunk
   // MFMA column col = 4 * (burst token) + (head in the group); token tk sits at
   // position p = ctx_len - T + tk and sees the keys from max(0, p - window + 1)
   // (or 0) up to p
@@ -187,7 +205,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int hh = col & (kAttnGroup - 1);
   const bool colv = tk < T;
   const int p_col = A.ctx_len - T + tk;
-  const int nk_col = colv ? min(C, p_col + 1 - j0) : 0;
+  const int nk_col = colv ? min(csz, p_col + 1 - j0) : 0;
   const int jlo_col = A.window ? max(0, p_col - A.window + 1) - j0 : 0;
 
   // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
@@ -195,13 +213,12 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const bool lin = A.ring_cap == 0;
   // plain and paged caches: the wave's 64 positions j0 + wk + x are the 64
   // consecutive rows jrow + wk + x (a block holds a multiple of 64 positions and
-  // chunks start at multiples of C); jlast is the row of the chunk's last key.
+  // chunks start at multiples of 64); jlast is the row of the chunk's last key.
   // A wave wholly past the end loads no K and reads V from jlast only.
   int64_t jrow = j0, jlast = j0 + nk - 1;
   if (A.btab) {
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     jlast = seq_row(A, j0 + nk - 1);
-    jrow = wv * kWaveKeys < nk ? seq_row(A, j0 + wv * kWaveKeys) - wv * kWaveKeys : jlast;
+    jrow = wk < nk ? seq_row(A, j0 + wk) - wk : jlast;
   }
   // cache row of chunk key jl, clamped into the keys in use (V rows, scales)
   auto vrow = [&](int jl) -> int64_t {
@@ -295,7 +312,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   }
   // fp16: the wave's V rows go to LDS in two halves of 32 rows (8 KiB), the
   // second after the first has been read
-  auto dma_v = [&](int h) {
+  auto dma_v = [&](int h, uint8_t* dst) {
     const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
     const int jv = wk + (lane >> 4);
     if (__builtin_expect(lin, 1)) {
@@ -308,7 +325,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
         const int r = 4 * i + (lane >> 4);
         const int piece = (lane & 15) ^ (2 * vswz(r));
         const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, kVCpol);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(dst + ii * 1024), 16, 0, kVCpol);
       }
     } else {
       const int prow0 = (j0 + jlo) % A.ring_cap;
@@ -319,11 +336,14 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
         const int piece = (lane & 15) ^ (2 * vswz(r));
         const int jl = min(max(jv + 4 * i, jlo), nk - 1);
         const uint8_t* row = reinterpret_cast<const uint8_t*>(vbase + (int64_t)krow(prow0, jl) * A.ld_tok);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(vw + ii * 1024), 16, 0, kVCpol);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(dst + ii * 1024), 16, 0, kVCpol);
       }
     }
   };
-  if constexpr (!Q8) dma_v(0);
+  if constexpr (!Q8) {
+    dma_v(0, vw);
+    if (alone) dma_v(1, vw + kVB);
+  }
   if constexpr (Q8) {
     // every load is in flight before the first use of a loaded value: the pins
     // keep the compiler from moving arithmetic (and its waits) between the issues
@@ -391,6 +411,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     }
   }
   // ---- the chunk maximum per column, shared by the four waves
+  float M;
   {
     float mw = -INFINITY;
 #pragma unroll
@@ -398,10 +419,14 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
       for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
     mw = cross_row_max(mw);
-    if (lane < 16) s_m[wave][lane] = mw;
+    if (small) {
+      M = mw;
+    } else {
+      if (lane < 16) s_m[wave][lane] = mw;
+      __syncthreads();
+      M = fmaxf(fmaxf(s_m[0][col], s_m[1][col]), fmaxf(s_m[2][col], s_m[3][col]));
+    }
   }
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0][col], s_m[1][col]), fmaxf(s_m[2][col], s_m[3][col]));
   // ---- weights, their sum, and the P^T operands (block b: slot j = tile 2b + j/4, slot j%4)
   h8 phi[2], plo[2];
   float pw[4][4];
@@ -421,7 +446,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       }
     }
   lw = cross_row_sum_fixed(lw);
-  if (lane < 16) s_l[wave][lane] = lw;
+  if (!small && lane < 16) s_l[wave][lane] = lw;
 
   // ---- weighted values: this wave's V rows have landed in LDS
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -434,15 +459,16 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      if (b == 1) {
+      if (b == 1 && !alone) {
         // every read of the first half has returned before its rows are replaced
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        dma_v(1);
+        dma_v(1, vw);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
+      const int hb = b == 1 && alone ? kVB : 0;  // where the second half sits
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int a0 = rbase + ((dt ^ vg) << 5);
+        const int a0 = hb + rbase + ((dt ^ vg) << 5);
         const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0));
         const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -522,10 +548,30 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[dt][r] = fmul(o[dt][r], down);
   }
+  // D slot r of lane (col, kg) = dim 16dt + 4kg + r of column col
+  if (small) {
+    // a small chunk: the wave's partial is the chunk's, for each column whose
+    // token reaches the chunk.  0 + o is what the four-wave sum below gives when
+    // the other waves hold no key of the column (as in a verify call whose
+    // later tokens make the same chunk a four-wave one), so the bits agree.
+    const int p2 = A.ctx_len - T + tk;
+    if (colv && j0 <= p2 && !(A.window && j0 + csz <= p2 - A.window + 1)) {
+      const int h = g * kAttnGroup + hh;
+      float* dst = part + ((int64_t)A.partial_begin + ((int64_t)tk * H_q + h) * A.n_chunks + ci) * PF;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 4 + 16 * dt + 4 * kg) =
+            f32x4{fadd(0.0f, o[dt][0]), fadd(0.0f, o[dt][1]), fadd(0.0f, o[dt][2]), fadd(0.0f, o[dt][3])};
+      if (kg == 0) {
+        dst[0] = M;
+        dst[1] = lw;
+      }
+    }
+    return;
+  }
   // every lane of the wave is done reading the wave's V region before it takes
-  // the partial (LDS reads of one wave complete in order)
-  // D slot r of lane (col, kg) = dim 16dt + 4kg + r of column col; the wave's
-  // own V region (now read) takes its partial O[column][dim]
+  // the partial (LDS reads of one wave complete in order); the wave's own V
+  // region (now read) takes its partial O[column][dim]
   float* so = reinterpret_cast<float*>(vw);
   if (colv)
 #pragma unroll
@@ -542,7 +588,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     const int t2 = cc >> 2;
     const int p2 = A.ctx_len - T + t2;
     if (j0 > p2) continue;  // chunk past this token's position
-    if (A.window && j0 + C <= p2 - A.window + 1) continue;  // chunk before its window
+    if (A.window && j0 + csz <= p2 - A.window + 1) continue;  // chunk before its window
     float O = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -567,7 +613,56 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 // that are then added by a fixed tree.  Every shape depends only on the
 // sequence's chunk count.  Optionally also emits the q8 blocks of the output
 // row (the quantized input of the output projection).
-constexpr int kMaxChunks = SD_MAX_CTX / SD_ATTN_CHUNK;
+constexpr int kMaxChunks = kAttnMaxChunks;
+constexpr int kFastLoads = 20;  // value loads per thread on the one-pass path: up to 160 chunks
+
+// The combine's one-pass merge for nc <= 8 * NL chunks: every load is issued
+// up front, (m, l) of chunk tid and the values of chunks j, j + 8, ..., j + 8(NL-1)
+// (thread (j, dims d4..d4+3)), so the merge waits for memory once.  Loads past
+// the last chunk read chunk nc - 1 and are never used, so the sums are those
+// of the general path term for term, whatever NL.  Leaves the eight group sums
+// in s_o and returns L.
+template <int NL>
+__device__ __forceinline__ float merge_one_pass(const float* __restrict__ base, int nc, int tid,
+                                                float* s_w, float* s_red, float* s_o) {
+  const int j = tid >> 5;
+  const int d4 = (tid & 31) * 4;
+  const float* mlp = base + (int64_t)min(tid, nc - 1) * PF;
+  const float m_c = mlp[0], l_c = mlp[1];
+  f32x4 a[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    a[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(j + 8 * i, nc - 1) * PF + 4 + d4);
+  float mx = group_max<64>(tid < nc ? m_c : -INFINITY);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  float lp = 0.0f;
+  if (tid < nc) {
+    const float w = expf(fsub(m_c, M));
+    s_w[tid] = w;
+    lp = fadd(lp, fmul(l_c, w));
+  }
+  lp = wave_sum_fixed(lp);
+  if ((tid & 63) == 0) s_red[tid >> 6] = lp;
+  __syncthreads();
+  const float L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (j + 8 * i < nc) {
+      const float w = s_w[j + 8 * i];
+      acc.x = fadd(acc.x, fmul(a[i].x, w));
+      acc.y = fadd(acc.y, fmul(a[i].y, w));
+      acc.z = fadd(acc.z, fmul(a[i].z, w));
+      acc.w = fadd(acc.w, fmul(a[i].w, w));
+    }
+  }
+  *reinterpret_cast<f32x4*>(s_o + j * HD + d4) = acc;
+  __syncthreads();
+  return L;
+}
 
 __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
                                                       const float* __restrict__ part,
@@ -586,52 +681,22 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
   const int t = row - A.row0;
   const int p = A.ctx_len - A.n_new + t;
   const int lo = A.window ? max(0, p - A.window + 1) : 0;
-  const int nc = p / C - lo / C + 1;  // this token's chunks: those of positions lo..p
-  const float* base =
-      part + ((int64_t)A.partial_begin + ((int64_t)t * H_q + h) * A.n_chunks + (lo / C - A.c0)) * PF;
+  const int nc = attn_chunks(lo, p);  // this token's chunks: those of positions lo..p
+  const float* base = part + ((int64_t)A.partial_begin + ((int64_t)t * H_q + h) * A.n_chunks +
+                              (attn_chunk_of(lo) - A.c0)) * PF;
 
   float L;
   const int j = tid >> 5;         // chunk group of the value sums
   const int d4 = (tid & 31) * 4;  // dims d4 .. d4+3
-  if (nc <= 8 * 16) {
-    // Up to 128 chunks (32768 keys): every load is issued up front, (m, l) of
-    // chunk tid and the values of chunks j, j + 8, ..., so the merge waits for
-    // memory once.  Loads past the last chunk read chunk nc - 1 and are never
-    // used; the sums below are those of the general path, term for term.
-    const float* mlp = base + (int64_t)min(tid, nc - 1) * PF;
-    const float m_c = mlp[0], l_c = mlp[1];
-    f32x4 a[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      a[i] = *reinterpret_cast<const f32x4*>(base + (int64_t)min(j + 8 * i, nc - 1) * PF + 4 + d4);
-    float mx = group_max<64>(tid < nc ? m_c : -INFINITY);
-    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
-    float lp = 0.0f;
-    if (tid < nc) {
-      const float w = expf(fsub(m_c, M));
-      s_w[tid] = w;
-      lp = fadd(lp, fmul(l_c, w));
-    }
-    lp = wave_sum_fixed(lp);
-    if ((tid & 63) == 0) s_red[tid >> 6] = lp;
-    __syncthreads();
-    L = fadd(fadd(s_red[0], s_red[1]), fadd(s_red[2], s_red[3]));
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (j + 8 * i < nc) {
-        const float w = s_w[j + 8 * i];
-        acc.x = fadd(acc.x, fmul(a[i].x, w));
-        acc.y = fadd(acc.y, fmul(a[i].y, w));
-        acc.z = fadd(acc.z, fmul(a[i].z, w));
-        acc.w = fadd(acc.w, fmul(a[i].w, w));
-      }
-    }
-    *reinterpret_cast<f32x4*>(s_o + j * HD + d4) = acc;
-    __syncthreads();
+  if (nc <= 8 * kFastLoads) {
+    // up to 160 chunks (34816 keys from position 0): one pass, with as many
+    // value loads per thread as the token's chunk count needs
+    if (nc <= 40)
+      L = merge_one_pass<5>(base, nc, tid, s_w, s_red, s_o);
+    else if (nc <= 80)
+      L = merge_one_pass<10>(base, nc, tid, s_w, s_red, s_o);
+    else
+      L = merge_one_pass<kFastLoads>(base, nc, tid, s_w, s_red, s_o);
   } else {
     // maximum of the chunk maxima (exact, order-free)
     float mx = -INFINITY;
@@ -703,20 +768,32 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
 }  // namespace
 
 size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
-  int units = 0, parts = 0, rows = 0;
+  int units = 0, parts = 0, rows = 0, small_units = 0;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.lo0 = x.window ? (x.ctx_len - x.n_new - x.window + 1 > 0 ? x.ctx_len - x.n_new - x.window + 1 : 0) : 0;
-    x.c0 = x.lo0 / C;
-    x.n_chunks = (x.ctx_len - 1) / C - x.c0 + 1;
+    x.c0 = attn_chunk_of(x.lo0);
+    x.n_chunks = attn_chunks(x.lo0, x.ctx_len - 1);
+    const int c_end = x.c0 + x.n_chunks;  // chunks c0 .. c_end - 1
+    x.ns = (c_end < kAttnSmallChunks ? c_end : kAttnSmallChunks) - x.c0;
+    if (x.ns < 0) x.ns = 0;
+    small_units += x.ns * H_kv;
+  }
+  // One 64-key chunk per workgroup spreads a short context over the CUs; when
+  // the call has more of them than a few per CU, four per workgroup (one per
+  // wave) keep each CU's loads in flight with fewer workgroups.
+  const int pk = small_units > kAttnSpreadUnits ? 4 : 1;
+  for (int s = 0; s < a->n_seq; ++s) {
+    SeqArg& x = a->s[s];
+    x.pk = pk;
+    x.units = (x.ns + pk - 1) / pk + (x.n_chunks - x.ns);
     x.unit_begin = units;
     x.partial_begin = parts;
     x.row0 = rows;
-    units += x.n_chunks * (H_q / kAttnGroup);
+    units += x.units * H_kv;
     parts += x.n_chunks * H_q * x.n_new;
     rows += x.n_new;
   }
-  (void)H_kv;
   return (size_t)parts * PF;
 }
 
@@ -724,7 +801,7 @@ hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_
                        float scale, float* out, float* partials, int8_t* oq, float* od,
                        hipStream_t st) {
   int units = 0;
-  for (int s = 0; s < seqs.n_seq; ++s) units += seqs.s[s].n_chunks * H_kv;
+  for (int s = 0; s < seqs.n_seq; ++s) units += seqs.s[s].units * H_kv;
   if (seqs.s[0].q8)
     hipLaunchKernelGGL(k_attn_chunk<true>, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale,
                        partials);

@@ -22,11 +22,37 @@ constexpr int kActDw = 20;          // dwords per pair in the LDS activation lay
 constexpr int kGemvThreads = 256;   // four wave64 per workgroup
 constexpr int kGemvLdsMax = 144 * 1024;
 constexpr int kAttnChunk = SD_ATTN_CHUNK;
+constexpr int kAttnSmallChunk = SD_ATTN_SMALL_CHUNK;
+constexpr int kAttnSmallSpan = SD_ATTN_SMALL_SPAN;
+constexpr int kAttnSmallChunks = kAttnSmallSpan / kAttnSmallChunk;
+static_assert(kAttnSmallSpan % kAttnChunk == 0 && kAttnChunk % kAttnSmallChunk == 0, "chunk grid");
 constexpr int kAttnHeadDim = 128;
 constexpr int kAttnGroup = 4;       // query heads per KV head handled by one workgroup
 constexpr int kAttnPartialFloats = 132;  // m, l, 2 pad, o[128]
 constexpr int kAttnMaxNew = 4;           // query tokens per sequence in one attention call
 constexpr size_t kAttnScratchBytes = SD_ATTN_SCRATCH_BYTES;  // allocation-free attention partials
+
+// Attention chunk grid, fixed in absolute positions: chunk c < kAttnSmallChunks
+// holds positions 64c .. 64c+63, later chunks hold 256 positions each from
+// kAttnSmallSpan on.  A key's chunk depends on its position alone.
+__host__ __device__ constexpr int attn_chunk_of(int j) {
+  return j < kAttnSmallSpan ? j / kAttnSmallChunk : kAttnSmallChunks + (j - kAttnSmallSpan) / kAttnChunk;
+}
+__host__ __device__ constexpr int attn_chunk_begin(int c) {
+  return c < kAttnSmallChunks ? c * kAttnSmallChunk : kAttnSmallSpan + (c - kAttnSmallChunks) * kAttnChunk;
+}
+__host__ __device__ constexpr int attn_chunk_size(int c) {
+  return c < kAttnSmallChunks ? kAttnSmallChunk : kAttnChunk;
+}
+// Chunks that keys lo..hi touch.
+__host__ __device__ constexpr int attn_chunks(int lo, int hi) { return attn_chunk_of(hi) - attn_chunk_of(lo) + 1; }
+// Most chunks any span of at most SD_MAX_CTX keys touches: the span from 0 has
+// the most (chunks are densest at low positions), plus one for a span that
+// starts inside a chunk.
+constexpr int kAttnMaxChunks = attn_chunks(0, SD_MAX_CTX - 1) + 1;
+// Above this many (64-key chunk, KV head) units in a call, four 64-key chunks
+// share a workgroup.
+constexpr int kAttnSpreadUnits = 512;
 
 // Per-sequence view as passed by value to the attention / append kernels.
 struct SeqArg {
@@ -37,7 +63,10 @@ struct SeqArg {
   int64_t ld_tok;
   int64_t ld_head;
   int32_t ctx_len;
-  int32_t n_chunks;
+  int32_t n_chunks;       // chunks c0 .. c0 + n_chunks - 1 (partials per token and head)
+  int32_t ns;             // of them on the 64-key grid (the first ns)
+  int32_t pk;             // 64-key chunks per workgroup: 1 or 4
+  int32_t units;          // workgroups per KV head
   int32_t unit_begin;     // first workgroup index of this sequence
   int32_t partial_begin;  // first partial slot of this sequence (per token and head: n_chunks slots)
   int32_t n_new;          // query tokens of the sequence (the newest n_new positions), 1..4
@@ -45,7 +74,7 @@ struct SeqArg {
   int32_t window;         // attention window in positions, 0 = whole context
   int32_t ring_cap;       // ring of ring_cap rows (position j in row j % ring_cap), 0 = plain
   int32_t lo0;            // lowest position any query token of the call attends to
-  int32_t c0;             // chunk (absolute, lo0 / SD_ATTN_CHUNK) of the first work unit
+  int32_t c0;             // chunk (absolute, attn_chunk_of(lo0)) of the first work unit
   const int32_t* btab;    // paged cache: block table (device), else null
   int32_t bshift;         // log2 of the block size (paged)
   int32_t n_blocks;       // blocks in the pool (paged)

@@ -13,6 +13,8 @@
 // Python, so the host keeps ahead of the GPU.
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 
 using namespace sd;
@@ -46,7 +48,9 @@ StepLayout layout(const sd_model* m, int n, int max_ctx) {
   size_t maxk = (size_t)m->hidden;
   if ((size_t)m->ffn > maxk) maxk = m->ffn;
   if ((size_t)m->n_heads * m->head_dim > maxk) maxk = (size_t)m->n_heads * m->head_dim;
-  const size_t chunks = (size_t)(max_ctx + kAttnChunk - 1) / kAttnChunk;
+  // a sequence's chunks are at most those of keys 0 .. max_ctx - 1 (chunks are
+  // densest at low positions)
+  const size_t chunks = (size_t)attn_chunks(0, max_ctx - 1);
   StepLayout L;
   size_t off = 0;
   L.x = off;      off = align_up(off + (size_t)n * m->hidden * 4, 256);
@@ -110,14 +114,13 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
       return SD_EINVAL;
     }
     {
+      // every token's keys span at most SD_MAX_CTX positions; the sequence's
+      // chunks (from lo0's to the last token's) are at most those of max_ctx
+      // keys from position 0
       const int lo0 = m->window ? (q.pos - m->window + 1 > 0 ? q.pos - m->window + 1 : 0) : 0;
-      if ((q.pos + T - 1) / SD_ATTN_CHUNK - lo0 / SD_ATTN_CHUNK + 1 > SD_MAX_CTX / SD_ATTN_CHUNK)
-        return SD_EUNSUPPORTED;
-    }
-    {
-      // attention chunks of this sequence are at most those of max_ctx keys
-      const int lo0 = m->window ? (q.pos - m->window + 1 > 0 ? q.pos - m->window + 1 : 0) : 0;
-      const int keys = q.pos + T - (lo0 / SD_ATTN_CHUNK) * SD_ATTN_CHUNK;
+      const int span = m->window ? std::min(q.pos + T, m->window) : q.pos + T;
+      if (span > SD_MAX_CTX) return SD_EUNSUPPORTED;
+      const int keys = q.pos + T - attn_chunk_begin(attn_chunk_of(lo0));
       if (keys > max_ctx) max_ctx = keys;
     }
     n += T;

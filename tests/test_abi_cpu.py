@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 8
+    assert L.sd_abi_version() == 9
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -122,7 +122,8 @@ def test_attention_rejections(L):
     assert need == 1 * 32 * 132 * 4      # one chunk per head for ctx 10
     assert a(FAKE, 4096, v1, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
     v2 = (_lib.SeqView * 2)(_view(2050, 4096), _view(32768, 32768))
-    assert L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128) == (9 + 128) * 32 * 132 * 4
+    # chunks: 64 keys below position 2048, 256 beyond -> 32 + 1 and 32 + 120
+    assert L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128) == (33 + 152) * 32 * 132 * 4
 
 
 def test_noalloc_attention_rejections(L):
@@ -138,7 +139,7 @@ def test_noalloc_attention_rejections(L):
     assert a(ODD, 4096, v1, 1, 32, 8, 128, 0.088, FAKE, None) == SD_EALIGN
     big = (_lib.SeqView * 4)(*[_view(65536, 65536) for _ in range(4)])
     need = L.sd_decode_attn_workspace_bytes(big, 4, 32, 128)
-    assert need == 4 * 256 * 32 * 132 * 4 > (16 << 20)
+    assert need == 4 * (32 + 248) * 32 * 132 * 4 > (16 << 20)
     assert a(FAKE, 4096, big, 4, 32, 8, 128, 0.088, FAKE, None) == SD_EWORKSPACE
 
 
@@ -147,7 +148,7 @@ def test_verify_attention_rejections_and_workspace(L):
     v2 = (_lib.SeqView * 2)(_view(258, 300), _view(3, 16))
     nn = (ctypes.c_int32 * 2)(4, 3)
     need = L.sd_decode_attn_verify_workspace_bytes(v2, nn, 2, 32, 128)
-    assert need == (2 * 4 + 1 * 3) * 32 * 132 * 4  # chunks x tokens x heads partials
+    assert need == (5 * 4 + 1 * 3) * 32 * 132 * 4  # chunks x tokens x heads partials
     assert L.sd_decode_attn_verify_workspace_bytes(v2, None, 2, 32, 128) == \
         L.sd_decode_attn_workspace_bytes(v2, 2, 32, 128)
     for bad in ((0, 1), (5, 1), (4, 4)):   # 0 tokens, more than 4, more than ctx_len
@@ -165,7 +166,7 @@ def test_window_and_ring_rejections(L):
     ok = view(5000, 300, 256, 1)          # ring: 256 positions in use fit 300 rows
     assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, 0, None) == SD_EWORKSPACE
     need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
-    assert need == 2 * 32 * 132 * 4       # positions 4744..4999 touch chunks 18 and 19
+    assert need == 2 * 32 * 132 * 4       # positions 4744..4999 touch chunks 42 and 43
     for bad in (view(5000, 300, 0, 1),    # a ring needs a window
                 view(5000, 200, 256, 1),  # the window does not fit the ring
                 view(10, 16, -1, 0),      # negative window
@@ -189,7 +190,7 @@ def test_paged_rejections(L):
     for bs in (64, 128, 256):
         ok = view(5000, 1024, bs)         # a paged context may exceed the pool (shared blocks)
         need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
-        assert need == 20 * 32 * 132 * 4
+        assert need == (32 + 12) * 32 * 132 * 4
         assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
     for bad in (view(100, 1024, 32),      # blocks of 64, 128 or 256 rows only
                 view(100, 1024, 100),
@@ -212,7 +213,7 @@ def test_q8_0_view_rejections(L):
     one = lambda v: (_lib.SeqView * 1)(v)
     ok = one(view())
     need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
-    assert need == 32 * 132 * 4
+    assert need == 2 * 32 * 132 * 4       # 100 keys: two 64-key chunks
     assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
     for bad, rc in ((view(kq=ctypes.c_void_p(0)), SD_EINVAL),     # missing codes
                     (view(kd=ctypes.c_void_p(0)), SD_EINVAL),     # missing scales

@@ -42,7 +42,9 @@ def _check_parity(o, ref):
 
 
 @pytest.mark.parametrize("lens", [[1], [5], [255, 256, 257], [511, 512, 513, 1],
-                                  [2050, 2051], [300, 17, 4000, 9]])
+                                  [2050, 2051], [300, 17, 4000, 9],
+                                  [63, 64, 65, 129],          # 64-key chunk edges
+                                  [2047, 2048, 2049, 2305]])  # the 64 -> 256-key grid edge
 def test_attention_parity_small(sd, lens):
     say(f"attention parity lens={lens}")
     kv = [_seq(1000 + i + L, L + 3) for i, L in enumerate(lens)]
@@ -142,7 +144,7 @@ def test_workspace_reuse_across_shapes(sd):
 
 
 def test_attention_maximum_context(sd):
-    """The largest supported span, SD_MAX_CTX = 524288 keys (2048 chunks), in
+    """The largest supported span, SD_MAX_CTX = 524288 keys (2072 chunks), in
     one sequence beside a short one: sampled heads against the oracle, and the
     long sequence alone gives the same bits."""
     import torch

@@ -48,7 +48,8 @@ def _check_parity(o, ref):
 
 @pytest.mark.parametrize("lens,news", [([1, 2, 63, 64], [1, 1, 1, 1]),
                                        ([65, 255, 256, 257], [1, 4, 2, 3]),
-                                       ([700, 1, 513, 2050], [4, 1, 3, 2])])
+                                       ([700, 1, 513, 2050], [4, 1, 3, 2]),
+                                       ([2047, 2048, 2049, 2051], [1, 4, 2, 4])])
 def test_q8_attention_parity_and_prefix(sd, lens, news):
     say(f"q8 attn {lens} {news}")
     caches = [_kv(5000 + i + sum(lens), L) for i, L in enumerate(lens)]

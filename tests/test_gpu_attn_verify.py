@@ -49,6 +49,10 @@ CASES = [
     ([258, 3], [4, 3]),                    # burst straddles the 256-key chunk boundary; burst = context
     ([2050, 3072, 16384, 300], [4, 2, 3, 1]),
     ([1, 513, 256, 257], [1, 4, 4, 2]),
+    ([2049, 2051, 66, 2300], [4, 4, 3, 2]),  # bursts across the 64 -> 256-key grid edge at 2048
+    # a 256-key chunk with 66 keys below ctx_len (four waves) whose earlier
+    # tokens see at most 64 of them (one wave in their one-token calls)
+    ([2114, 2370, 130], [4, 4, 2]),
 ]
 
 

@@ -63,6 +63,29 @@ def test_window_parity_plain_and_ring(sd, window):
             r += 1
 
 
+@pytest.mark.parametrize("window", [60, 100, 2047])
+def test_window_across_the_grid_edge(sd, window):
+    """Windows that start among the 64-key chunks below position 2048 and end
+    among the 256-key ones: oracle parity, ring == plain, burst token == its
+    one-token call."""
+    say(f"window {window} across the chunk grid edge")
+    lens, news = [2100, 2049, 2400, 70], [4, 2, 3, 1]
+    kvs = [_kv(3300 + i, L) for i, L in enumerate(lens)]
+    q = synth.queries(synth.rng(3400 + window), sum(news), H_Q, D)
+    o = _run(sd, q, kvs, lens, news, window, False)
+    ref = oracle.attn_verify(q, kvs, lens, news, SCALE, window=window)
+    _check_parity(o, ref)
+    caps = [min(L, window + T - 1) + 5 for L, T in zip(lens, news)]
+    rings = [_ring_of(k, v, L, cap) for (k, v), L, cap in zip(kvs, lens, caps)]
+    assert np.array_equal(bits(_run(sd, q, rings, lens, news, window, True)), bits(o))
+    r = 0
+    for s, (L, T) in enumerate(zip(lens, news)):
+        for i in range(T):
+            one = _run(sd, q[r:r + 1], [kvs[s]], [L - T + i + 1], [1], window, False)
+            assert np.array_equal(bits(one[0]), bits(o[r])), (s, i)
+            r += 1
+
+
 def test_ring_wrapping_inside_a_chunk_and_small_ring(sd):
     """A ring smaller than a chunk (window 40, 43 rows), positions far past the
     ring size, so the rows of one chunk wrap."""

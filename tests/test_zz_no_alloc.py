@@ -48,8 +48,8 @@ def test_noalloc_equals_workspace_entry_point_two_calls(sd):
 
 
 def test_noalloc_refuses_partials_beyond_the_scratch_array(sd):
-    """Four sequences of 65536 keys need 4 * 256 chunks * 32 heads * 528 B =
-    17.3 MB of partials, beyond the 16 MiB array: SD_EWORKSPACE, no launch."""
+    """Four sequences of 65536 keys need 4 * 280 chunks * 32 heads * 528 B =
+    18.9 MB of partials, beyond the 16 MiB array: SD_EWORKSPACE, no launch."""
     import torch
     # real 65536-row caches, so that every access would stay in bounds even if
     # the call were (wrongly) launched

@@ -768,7 +768,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
 }  // namespace
 
 size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
-  int units = 0, parts = 0, rows = 0, small_units = 0;
+  int units = 0, parts = 0, rows = 0;
+  int64_t small_keys = 0, large_keys = 0;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.lo0 = x.window ? (x.ctx_len - x.n_new - x.window + 1 > 0 ? x.ctx_len - x.n_new - x.window + 1 : 0) : 0;
@@ -777,12 +778,15 @@ size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
     const int c_end = x.c0 + x.n_chunks;  // chunks c0 .. c_end - 1
     x.ns = (c_end < kAttnSmallChunks ? c_end : kAttnSmallChunks) - x.c0;
     if (x.ns < 0) x.ns = 0;
-    small_units += x.ns * H_kv;
+    small_keys += (int64_t)x.ns * kAttnSmallChunk;
+    large_keys += x.ctx_len > kAttnSmallSpan ? x.ctx_len - kAttnSmallSpan : 0;
   }
-  // One 64-key chunk per workgroup spreads a short context over the CUs; when
-  // the call has more of them than a few per CU, four per workgroup (one per
-  // wave) keep each CU's loads in flight with fewer workgroups.
-  const int pk = small_units > kAttnSpreadUnits ? 4 : 1;
+  // One 64-key chunk per workgroup spreads short contexts over the CUs; when
+  // most of the call's keys sit in 256-key chunks, four 64-key chunks per
+  // workgroup (one per wave) do better (measured: four 2050-key sequences
+  // 16.0 against 17.6 us with one per workgroup; one 32768-key sequence 32.8
+  // against 34.9 us and the four ragged contexts 49.2 against 52.4 us with four).
+  const int pk = large_keys > small_keys ? 4 : 1;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.pk = pk;

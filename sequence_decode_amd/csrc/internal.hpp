@@ -50,9 +50,6 @@ __host__ __device__ constexpr int attn_chunks(int lo, int hi) { return attn_chun
 // the most (chunks are densest at low positions), plus one for a span that
 // starts inside a chunk.
 constexpr int kAttnMaxChunks = attn_chunks(0, SD_MAX_CTX - 1) + 1;
-// Above this many (64-key chunk, KV head) units in a call, four 64-key chunks
-// share a workgroup.
-constexpr int kAttnSpreadUnits = 512;
 
 // Per-sequence view as passed by value to the attention / append kernels.
 struct SeqArg {

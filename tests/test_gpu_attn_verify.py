@@ -53,6 +53,9 @@ CASES = [
     # a 256-key chunk with 66 keys below ctx_len (four waves) whose earlier
     # tokens see at most 64 of them (one wave in their one-token calls)
     ([2114, 2370, 130], [4, 4, 2]),
+    # the newest token at 4096 has 41 chunks, the one before it 40: the merge
+    # loads them in different numbers of rounds, with the same sums
+    ([4097, 4095], [4, 2]),
 ]
 
 

@@ -50,11 +50,13 @@ namespace {
 constexpr int HD = kAttnHeadDim;
 constexpr int PF = kAttnPartialFloats;
 
-__device__ __forceinline__ int find_seq(const SeqArgs& a, int u) {
+// Sequence of workgroup b: 256-key units first (every sequence's, from
+// large_begin), then the 64-key ones (from small_begin).
+__device__ __forceinline__ int find_seq(const SeqArgs& a, int b, bool large) {
   int s = 0;
 #pragma unroll
   for (int i = 1; i < SD_MAX_SEQS; ++i)
-    if (i < a.n_seq && u >= a.s[i].unit_begin) s = i;
+    if (i < a.n_seq && b >= (large ? a.s[i].large_begin : a.s[i].small_begin)) s = i;
   return s;
 }
 
@@ -160,11 +162,23 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[Q8 ? 4 * 64 * 4 : 1];  // per wave and key: K, V scales
   __shared__ float s_m[4][16], s_l[4][16];  // per wave and MFMA column (token, head)
 
-  const int s = find_seq(seqs, blockIdx.x);
+  // The grid holds every sequence's 256-key units first (the long-running
+  // ones start first), then its 64-key units; within each, KV head by KV head.
+  const bool large = (int)blockIdx.x < seqs.large_total;
+  const int s = find_seq(seqs, blockIdx.x, large);
   const SeqArg& A = seqs.s[s];
-  const int local = blockIdx.x - A.unit_begin;
-  const int g = local / A.units;
-  const int u = local - g * A.units;  // unit of this workgroup within KV head g
+  const int n_su = (A.ns + A.pk - 1) / A.pk;  // 64-key units per KV head
+  const int n_lu = A.n_chunks - A.ns;         // 256-key units per KV head
+  int g, u;  // KV head, and unit within it (64-key units first)
+  if (large) {
+    const int local = blockIdx.x - A.large_begin;
+    g = local / n_lu;
+    u = n_su + (local - g * n_lu);
+  } else {
+    const int local = blockIdx.x - A.small_begin;
+    g = local / n_su;
+    u = local - g * n_su;
+  }
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // The chunk of this wave.  Units 0 .. n_su-1 hold the chunks of the 64-key
@@ -173,7 +187,6 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   // one wave's ("small"): that wave keeps its softmax partial to itself (no
   // barrier, no cross-wave sums) and the waves without a chunk leave at once.
   // Which unit or wave computes a chunk changes no bits of its partial.
-  const int n_su = (A.ns + A.pk - 1) / A.pk;
   const bool packed = u < n_su && A.pk == 4;
   const int ci = u < n_su ? u * A.pk + (packed ? wave : 0) : A.ns + (u - n_su);  // counted from c0
   const int c = A.c0 + ci;                // absolute chunk: positions j0 .. j0 + csz - 1
@@ -768,7 +781,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
 }  // namespace
 
 size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
-  int units = 0, parts = 0, rows = 0;
+  int parts = 0, rows = 0;
   int64_t small_keys = 0, large_keys = 0;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
@@ -781,31 +794,43 @@ size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
     small_keys += (int64_t)x.ns * kAttnSmallChunk;
     large_keys += x.ctx_len > kAttnSmallSpan ? x.ctx_len - kAttnSmallSpan : 0;
   }
-  // One 64-key chunk per workgroup spreads short contexts over the CUs; when
-  // most of the call's keys sit in 256-key chunks, four 64-key chunks per
-  // workgroup (one per wave) do better (measured: four 2050-key sequences
-  // 16.0 against 17.6 us with one per workgroup; one 32768-key sequence 32.8
-  // against 34.9 us and the four ragged contexts 49.2 against 52.4 us with four).
-  const int pk = large_keys > small_keys ? 4 : 1;
+  // One 64-key chunk per workgroup spreads a short context over the CUs (one
+  // 2050-key sequence: 264 workgroups, 9.4 us against 12.4 us with four per
+  // workgroup).  Once the call has more such chunks than the chip has CUs, or
+  // most of its keys sit in 256-key chunks, four per workgroup (one per wave)
+  // do better (graph-timed, us, one vs four per workgroup: {2050, 3072} 14.9
+  // vs 13.8; four 2050s 16.5 vs 15.0; one 32768-key sequence 34.7 vs 32.6).
+  const int pk = small_keys / kAttnSmallChunk * H_kv > kAttnSpreadUnits || large_keys > small_keys ? 4 : 1;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.pk = pk;
-    x.units = (x.ns + pk - 1) / pk + (x.n_chunks - x.ns);
-    x.unit_begin = units;
     x.partial_begin = parts;
     x.row0 = rows;
-    units += x.units * H_kv;
     parts += x.n_chunks * H_q * x.n_new;
     rows += x.n_new;
   }
+  // workgroups: every sequence's 256-key units, then every sequence's 64-key units
+  int units = 0;
+  for (int s = 0; s < a->n_seq; ++s) {
+    SeqArg& x = a->s[s];
+    x.large_begin = units;
+    units += (x.n_chunks - x.ns) * H_kv;
+  }
+  a->large_total = units;
+  for (int s = 0; s < a->n_seq; ++s) {
+    SeqArg& x = a->s[s];
+    x.small_begin = units;
+    units += (x.ns + pk - 1) / pk * H_kv;
+  }
+  a->units_total = units;
   return (size_t)parts * PF;
 }
 
 hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_q, int H_kv,
                        float scale, float* out, float* partials, int8_t* oq, float* od,
                        hipStream_t st) {
-  int units = 0;
-  for (int s = 0; s < seqs.n_seq; ++s) units += seqs.s[s].units * H_kv;
+  const int units = seqs.units_total;
+  (void)H_kv;
   if (seqs.s[0].q8)
     hipLaunchKernelGGL(k_attn_chunk<true>, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale,
                        partials);

@@ -50,6 +50,8 @@ __host__ __device__ constexpr int attn_chunks(int lo, int hi) { return attn_chun
 // the most (chunks are densest at low positions), plus one for a span that
 // starts inside a chunk.
 constexpr int kAttnMaxChunks = attn_chunks(0, SD_MAX_CTX - 1) + 1;
+// Up to this many (64-key chunk, KV head) units in a call, one per workgroup.
+constexpr int kAttnSpreadUnits = 320;
 
 // Per-sequence view as passed by value to the attention / append kernels.
 struct SeqArg {
@@ -63,8 +65,8 @@ struct SeqArg {
   int32_t n_chunks;       // chunks c0 .. c0 + n_chunks - 1 (partials per token and head)
   int32_t ns;             // of them on the 64-key grid (the first ns)
   int32_t pk;             // 64-key chunks per workgroup: 1 or 4
-  int32_t units;          // workgroups per KV head
-  int32_t unit_begin;     // first workgroup index of this sequence
+  int32_t large_begin;    // first workgroup of its 256-key units
+  int32_t small_begin;    // first workgroup of its 64-key units
   int32_t partial_begin;  // first partial slot of this sequence (per token and head: n_chunks slots)
   int32_t n_new;          // query tokens of the sequence (the newest n_new positions), 1..4
   int32_t row0;           // q / out row of its first query token
@@ -95,6 +97,8 @@ __device__ inline int64_t seq_row(const SeqArg& a, int64_t j) {
 struct SeqArgs {
   SeqArg s[SD_MAX_SEQS];
   int32_t n_seq;
+  int32_t large_total;  // workgroups holding 256-key units (they come first)
+  int32_t units_total;  // all workgroups of the chunk kernel
 };
 
 // Angle pos * theta^(-2i/n_rot) of RoPE pair i, its cosine and sine in fp64,

@@ -761,6 +761,139 @@ def trace_summary(trace_db, fetch_db=None, write_db=None, n_tok=4):
     return out
 
 
+def _rocpd_dispatches(db, pmc=None):
+    """(kernel display name, duration us) of every dispatch of a rocprofv3
+    results database in start order, or (name, counter value) per dispatch of
+    a counter run."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    if pmc is None:
+        q = ("select k.display_name, d.start, d.end from rocpd_kernel_dispatch d join "
+             "rocpd_info_kernel_symbol k on d.kernel_id = k.id order by d.start")
+        return [(n, (e - s_) / 1e3) for n, s_, e in con.execute(q)]
+    q = "select name, counter_value from pmc_events where counter_name = ? order by dispatch_id"
+    return list(con.execute(q, (pmc,)))
+
+
+def _short_kernel(name):
+    name = name.replace("void ", "", 1).replace("sd::(anonymous namespace)::", "")
+    i = name.find("(")
+    return name[:i] if i > 0 else name
+
+
+def _kernel_stats(rows, top=24):
+    import statistics
+    per = {}
+    for n, us in rows:
+        per.setdefault(_short_kernel(n), []).append(us)
+    lines = ["| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        lines.append(f"| {k[:110]} | {len(v)} | {statistics.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{sum(v) / 1e3:.2f} |")
+    return "\n".join(lines)
+
+
+ATTN_CASES = {"n1_2050": [2050], "n4_2050": [2050] * 4, "n4_ragged": [2050, 3072, 16384, 32768],
+              "n1_32768": [32768]}
+
+
+def attn_trace_summary(trace_db, fetch_db=None, write_db=None, reps=20):
+    """Summary (markdown) of rocprofv3 results databases of `bench.py
+    --attention-only` (and, for the counter runs, `--attention-only
+    --calibrate-copy`): per case of the attention pass (its order: each context
+    set with fp16, q8_0 and paged fp16 caches), the average trace duration of
+    the chunk kernel and of the merge kernel over the timed calls (the last
+    `reps` graph replays of every cache set; each case makes 2 warm-up rounds,
+    one untimed replay and `reps` timed ones), and from the counter runs the
+    HBM bytes per chunk-kernel dispatch: FETCH_SIZE and WRITE_SIZE (KiB) scaled
+    by what the same counters read for the 1 GiB calibration copy."""
+    import hashlib
+    import statistics
+
+    def split(rows):
+        chunk = [v for n, v in rows if _short_kernel(n).startswith("k_attn_chunk")]
+        comb = [v for n, v in rows if _short_kernel(n).startswith("k_attn_combine")]
+        out, i = {}, 0
+        for cname, lens in ATTN_CASES.items():
+            for kind in ("f16", "q8_0", "f16_paged64"):
+                sets = attn_sets(lens, kind)
+                n = (3 + reps) * sets
+                out[f"{cname}_{kind}"] = (chunk[i + 3 * sets:i + n], comb[i + 3 * sets:i + n])
+                i += n
+        if i != len(chunk) or i != len(comb):
+            raise RuntimeError(f"the database does not hold exactly one attention pass ({len(chunk)} "
+                               f"chunk and {len(comb)} merge dispatches, expected {i})")
+        return out
+
+    tr = _rocpd_dispatches(trace_db)
+    cases = split(tr)
+    have_pmc = fetch_db and write_db
+    if have_pmc:
+        f = _rocpd_dispatches(fetch_db, "FETCH_SIZE")
+        w = _rocpd_dispatches(write_db, "WRITE_SIZE")
+        ff = (1 << 30) / ([v for n, v in f if "copyBuffer" in n][-1] * 1024)
+        wf = (1 << 30) / ([v for n, v in w if "copyBuffer" in n][-1] * 1024)
+        fc, wc = split(f), split(w)
+    lines = ["| case | chunk kernel avg us | merge avg us | cache bytes | fetched B (calibrated) | ratio | written B |",
+             "|---|---|---|---|---|---|---|"]
+    for key, (ch, cb) in cases.items():
+        cname, kind = key.split("_", 2)[0] + "_" + key.split("_", 2)[1], key.split("_", 2)[2]
+        lens = ATTN_CASES[cname]
+        cache = sum(lens) * (2176 if kind == "q8_0" else 4096)
+        row = f"| {key} | {statistics.mean(ch):.2f} | {statistics.mean(cb):.2f} | {cache:,} |"
+        if have_pmc:
+            fb = statistics.mean(fc[key][0]) * 1024 * ff
+            wb = statistics.mean(wc[key][0]) * 1024 * wf
+            row += f" {fb:,.0f} | {fb / cache:.3f} | {wb:,.0f} |"
+        else:
+            row += " | | |"
+        lines.append(row)
+    src = os.path.join(ROOT, "sequence_decode_amd", "csrc", "attn.hip")
+    out = {"per_case": "\n".join(lines), "kernel_stats": _kernel_stats(tr, 8),
+           "kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest()}
+    if have_pmc:
+        out["fetch_factor"], out["write_factor"] = round(ff, 4), round(wf, 4)
+    return out
+
+
+def step_trace_summary(trace_db, n_steps=10):
+    """Summary (markdown) of a rocprofv3 results database of `bench.py
+    --step-only N`: the library's kernels of the last `n_steps` steps (a step
+    ends with its argmax), per kernel and per step, with the step's span and
+    its kernel-busy time."""
+    import statistics
+    rows = []
+    import sqlite3
+    con = sqlite3.connect(trace_db)
+    q = ("select k.display_name, d.start, d.end, d.grid_size_x from rocpd_kernel_dispatch d join "
+         "rocpd_info_kernel_symbol k on d.kernel_id = k.id order by d.start")
+    for n, s_, e, g in con.execute(q):
+        if "sd::" in n:
+            rows.append((_short_kernel(n), s_, e, g))
+    ends, prev = [], None
+    for i, r in enumerate(rows):
+        if r[0].startswith("k_argmax"):
+            if prev is not None and i == prev + 1:
+                ends[-1] = i
+            else:
+                ends.append(i)
+            prev = i
+    ends = ends[-(n_steps + 1):]
+    acc, spans, busy = {}, [], []
+    for a, b in zip(ends[:-1], ends[1:]):
+        seg = rows[a + 1:b + 1]
+        spans.append((seg[-1][2] - rows[a][2]) / 1e3)
+        busy.append(sum(e - s_ for _, s_, e, _ in seg) / 1e3)
+        for n, s_, e, g in seg:
+            acc.setdefault((n, g), []).append((e - s_) / 1e3)
+    k = len(spans)
+    lines = [f"{k} steps: span {statistics.mean(spans):.1f} us per step, kernel-busy {statistics.mean(busy):.1f} us",
+             "", "| kernel | grid | per step | avg us | us per step |", "|---|---|---|---|---|"]
+    for (n, g), v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {n[:100]} | {g} | {len(v) / k:.1f} | {statistics.mean(v):.2f} | {sum(v) / k:.1f} |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -782,10 +915,22 @@ def main():
                     help="only the projection sweeps and the per-shape event pass (for a kernel trace)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for byte counters)")
+    ap.add_argument("--attn-trace-summary", nargs="+", metavar="DB",
+                    help="print the per-case summary of rocprofv3 databases of --attention-only: "
+                         "trace [FETCH_SIZE WRITE_SIZE]")
+    ap.add_argument("--step-trace-summary", metavar="DB",
+                    help="print the per-step kernel breakdown of a rocprofv3 database of --step-only N")
     ap.add_argument("--trace-summary", nargs="+", metavar="DB",
                     help="summarize rocprofv3 results databases of a --sweep-only run: the kernel-trace "
                          "database, then optionally the FETCH_SIZE and WRITE_SIZE ones (no GPU used)")
     args = ap.parse_args()
+    if args.attn_trace_summary:
+        r = attn_trace_summary(*args.attn_trace_summary[:3])
+        print(r["per_case"] + "\n\n" + r["kernel_stats"] + "\n\nkernel_source_sha256: " + r["kernel_source_sha256"])
+        return
+    if args.step_trace_summary:
+        print(step_trace_summary(args.step_trace_summary))
+        return
     if args.trace_summary:
         print(json.dumps(trace_summary(*args.trace_summary[:3], n_tok=args.n_tok), indent=1))
         return

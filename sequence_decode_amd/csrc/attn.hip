@@ -39,6 +39,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "device_math.hpp"
 #include "internal.hpp"
@@ -198,425 +199,434 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   // a small chunk's wave alone in its workgroup takes the next wave's V region
   // too and loads all its V rows at once
   const bool alone = small && !packed;
-  const int jlo = max(0, A.lo0 - j0);     // keys of the chunk below any query's window
-  // ring caches: row of chunk key jl (jlo <= jl < nk) runs on from that of jlo
-  // and wraps once at the ring's end (the keys in use span at most the ring)
-  auto krow = [&](int prow0, int jl) {
-    const int r = prow0 + (jl - jlo);
-    return r >= A.ring_cap ? r - A.ring_cap : r;
-  };
+  // The rest is compiled twice: for small chunks and for four-wave ones, so
+  // neither path carries the other's branches.
+  auto body = [&](auto small_c) {
+    constexpr bool SMALL = decltype(small_c)::value;
+    const int jlo = max(0, A.lo0 - j0);     // keys of the chunk below any query's window
+    // ring caches: row of chunk key jl (jlo <= jl < nk) runs on from that of jlo
+    // and wraps once at the ring's end (the keys in use span at most the ring)
+    auto krow = [&](int prow0, int jl) {
+      const int r = prow0 + (jl - jlo);
+      return r >= A.ring_cap ? r - A.ring_cap : r;
+    };
 
-  const int lane = tid & 63;
-  const int col = lane & 15;  // MFMA row (A loads) / column (B, D)
-  const int kg = lane >> 4;   // MFMA k-group
-  const int wk = small ? 0 : wave * kWaveKeys;  // first key of the wave within the chunk
-  // MFMA column col = 4 * (burst token) + (head in the group); token tk sits at
-  // position p = ctx_len - T + tk and sees the keys from max(0, p - window + 1)
-  // (or 0) up to p
-  const int T = A.n_new;
-  const int tk = col >> 2;
-  const int hh = col & (kAttnGroup - 1);
-  const bool colv = tk < T;
-  const int p_col = A.ctx_len - T + tk;
-  const int nk_col = colv ? min(csz, p_col + 1 - j0) : 0;
-  const int jlo_col = A.window ? max(0, p_col - A.window + 1) - j0 : 0;
+    const int lane = tid & 63;
+    const int col = lane & 15;  // MFMA row (A loads) / column (B, D)
+    const int kg = lane >> 4;   // MFMA k-group
+    const int wk = SMALL ? 0 : wave * kWaveKeys;  // first key of the wave within the chunk
+    // MFMA column col = 4 * (burst token) + (head in the group); token tk sits at
+    // position p = ctx_len - T + tk and sees the keys from max(0, p - window + 1)
+    // (or 0) up to p
+    const int T = A.n_new;
+    const int tk = col >> 2;
+    const int hh = col & (kAttnGroup - 1);
+    const bool colv = tk < T;
+    const int p_col = A.ctx_len - T + tk;
+    const int nk_col = colv ? min(csz, p_col + 1 - j0) : 0;
+    const int jlo_col = A.window ? max(0, p_col - A.window + 1) - j0 : 0;
 
-  // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
-  const int jk = wk + 8 * (col >> 2) + (col & 3);
-  const bool lin = A.ring_cap == 0;
-  // plain and paged caches: the wave's 64 positions j0 + wk + x are the 64
-  // consecutive rows jrow + wk + x (a block holds a multiple of 64 positions and
-  // chunks start at multiples of 64); jlast is the row of the chunk's last key.
-  // A wave wholly past the end loads no K and reads V from jlast only.
-  int64_t jrow = j0, jlast = j0 + nk - 1;
-  if (A.btab) {
-    jlast = seq_row(A, j0 + nk - 1);
-    jrow = wk < nk ? seq_row(A, j0 + wk) - wk : jlast;
-  }
-  // cache row of chunk key jl, clamped into the keys in use (V rows, scales)
-  auto vrow = [&](int jl) -> int64_t {
-    if (__builtin_expect(lin, 1)) return jl < nk ? jrow + jl : jlast;
-    return krow((j0 + jlo) % A.ring_cap, min(max(jl, jlo), nk - 1));
-  };
-  uint8_t* vw = s_v + wave * kVB;
-  if constexpr (Q8) {
-    // ---- V code rows of this wave -> LDS by DMA, issued first (the scores
-    // wait for every load of the wave): instruction i fills rows
-    // 8i .. 8i+7; lane l writes row 8i + l/8 at 16-byte position l%8, which
-    // holds the row's segment (l%8) ^ vswz8(row)
-    const int8_t* vbase = A.vq + (int64_t)g * A.ld_head;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * i + (lane >> 3);
-      const int seg = (lane & 7) ^ vswz8(r);
-      const int8_t* row = vbase + vrow(wk + r) * A.ld_tok;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * seg), (lds_ptr)(vw + i * 1024), 16, 0, kVCpol);
+    // ---- K (score A operands): tile t, row col -> key wk + 32b + 8(col/4) + 4half + col%4
+    const int jk = wk + 8 * (col >> 2) + (col & 3);
+    const bool lin = A.ring_cap == 0;
+    // plain and paged caches: the wave's 64 positions j0 + wk + x are the 64
+    // consecutive rows jrow + wk + x (a block holds a multiple of 64 positions and
+    // chunks start at multiples of 64); jlast is the row of the chunk's last key.
+    // A wave wholly past the end loads no K and reads V from jlast only.
+    int64_t jrow = j0, jlast = j0 + nk - 1;
+    if (A.btab) {
+      jlast = seq_row(A, j0 + nk - 1);
+      jrow = wk < nk ? seq_row(A, j0 + wk) - wk : jlast;
     }
-  }
-  u32x4a ka[4][4];   // fp16 caches: 8 dims per (tile, block)
-  u32x2a kc[4][4];   // q8_0 caches: 8 codes per (tile, block)
-  if constexpr (!Q8) {
-    const uint16_t* kb = A.k + (int64_t)g * A.ld_head + 8 * kg;
-    if (__builtin_expect(lin, 1)) {
-      // plain / paged cache: keys past the end read the last key, keys below a
-      // window are real rows (both masked below)
+    // cache row of chunk key jl, clamped into the keys in use (V rows, scales)
+    auto vrow = [&](int jl) -> int64_t {
+      if (__builtin_expect(lin, 1)) return jl < nk ? jrow + jl : jlast;
+      return krow((j0 + jlo) % A.ring_cap, min(max(jl, jlo), nk - 1));
+    };
+    uint8_t* vw = s_v + wave * kVB;
+    if constexpr (Q8) {
+      // ---- V code rows of this wave -> LDS by DMA, issued first (the scores
+      // wait for every load of the wave): instruction i fills rows
+      // 8i .. 8i+7; lane l writes row 8i + l/8 at 16-byte position l%8, which
+      // holds the row's segment (l%8) ^ vswz8(row)
+      const int8_t* vbase = A.vq + (int64_t)g * A.ld_head;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
-        const uint16_t* kr = kb + (jl < nk ? jrow + jl : jlast) * A.ld_tok;
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const int seg = (lane & 7) ^ vswz8(r);
+        const int8_t* row = vbase + vrow(wk + r) * A.ld_tok;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * seg), (lds_ptr)(vw + i * 1024), 16, 0, kVCpol);
+      }
+    }
+    u32x4a ka[4][4];   // fp16 caches: 8 dims per (tile, block)
+    u32x2a kc[4][4];   // q8_0 caches: 8 codes per (tile, block)
+    if constexpr (!Q8) {
+      const uint16_t* kb = A.k + (int64_t)g * A.ld_head + 8 * kg;
+      if (__builtin_expect(lin, 1)) {
+        // plain / paged cache: keys past the end read the last key, keys below a
+        // window are real rows (both masked below)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+        for (int t = 0; t < 4; ++t) {
+          const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+          const uint16_t* kr = kb + (jl < nk ? jrow + jl : jlast) * A.ld_tok;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+        }
+      } else {
+        // ring: keys outside jlo .. nk-1 read the nearest key in use (their scores
+        // are replaced by -inf below)
+        const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+          const uint16_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+        }
       }
     } else {
-      // ring: keys outside jlo .. nk-1 read the nearest key in use (their scores
-      // are replaced by -inf below)
-      const int prow0 = (j0 + jlo) % A.ring_cap;
+      const int8_t* kb = A.kq + (int64_t)g * A.ld_head + 8 * kg;
+      if (__builtin_expect(lin, 1)) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
-        const uint16_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+        for (int t = 0; t < 4; ++t) {
+          const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+          const int8_t* kr = kb + (jl < nk ? jrow + jl : jlast) * A.ld_tok;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+          for (int kk = 0; kk < 4; ++kk) kc[t][kk] = *reinterpret_cast<const u32x2a*>(kr + 32 * kk);
+        }
+      } else {
+        const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+          const int8_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) kc[t][kk] = *reinterpret_cast<const u32x2a*>(kr + 32 * kk);
+        }
       }
     }
-  } else {
-    const int8_t* kb = A.kq + (int64_t)g * A.ld_head + 8 * kg;
-    if (__builtin_expect(lin, 1)) {
+    // ---- q8_0 scales: lane (col, kg) fetches the K and V scales of key
+    // 8kg + col%8 + 32(col/8) of the wave (the 16 lanes of a group cover the 16
+    // keys whose scores and weights the group holds); they go to LDS below
+    u32x2a ksc = {0u, 0u}, vsc = {0u, 0u};
+    if constexpr (Q8) {
+      const int kw = 8 * kg + (col & 7) + 32 * (col >> 3);
+      const int64_t so = vrow(wk + kw) * (A.ld_tok >> 5) + (int64_t)g * (A.ld_head >> 5);
+      ksc = *reinterpret_cast<const u32x2a*>(A.kd + so);
+      vsc = *reinterpret_cast<const u32x2a*>(A.vd + so);
+    }
+    // ---- q (score B operands): column col = (token tk, head g*4 + hh), dims 32kk + 8kg ..
+    // (a column past the sequence's tokens reads its last token: all its keys are
+    // masked and its partial is not stored)
+    f32x4 qv[4][2];
+    {
+      const f32x4* qp = reinterpret_cast<const f32x4*>(
+          q + (int64_t)(A.row0 + min(tk, T - 1)) * ld_q + (int64_t)(g * kAttnGroup + hh) * HD + 8 * kg);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
-        const int8_t* kr = kb + (jl < nk ? jrow + jl : jlast) * A.ld_tok;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kc[t][kk] = *reinterpret_cast<const u32x2a*>(kr + 32 * kk);
-      }
-    } else {
-      const int prow0 = (j0 + jlo) % A.ring_cap;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
-        const int8_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kc[t][kk] = *reinterpret_cast<const u32x2a*>(kr + 32 * kk);
+      for (int kk = 0; kk < 4; ++kk) {
+        qv[kk][0] = qp[8 * kk];
+        qv[kk][1] = qp[8 * kk + 1];
       }
     }
-  }
-  // ---- q8_0 scales: lane (col, kg) fetches the K and V scales of key
-  // 8kg + col%8 + 32(col/8) of the wave (the 16 lanes of a group cover the 16
-  // keys whose scores and weights the group holds); they go to LDS below
-  u32x2a ksc = {0u, 0u}, vsc = {0u, 0u};
-  if constexpr (Q8) {
-    const int kw = 8 * kg + (col & 7) + 32 * (col >> 3);
-    const int64_t so = vrow(wk + kw) * (A.ld_tok >> 5) + (int64_t)g * (A.ld_head >> 5);
-    ksc = *reinterpret_cast<const u32x2a*>(A.kd + so);
-    vsc = *reinterpret_cast<const u32x2a*>(A.vd + so);
-  }
-  // ---- q (score B operands): column col = (token tk, head g*4 + hh), dims 32kk + 8kg ..
-  // (a column past the sequence's tokens reads its last token: all its keys are
-  // masked and its partial is not stored)
-  f32x4 qv[4][2];
-  {
-    const f32x4* qp = reinterpret_cast<const f32x4*>(
-        q + (int64_t)(A.row0 + min(tk, T - 1)) * ld_q + (int64_t)(g * kAttnGroup + hh) * HD + 8 * kg);
+    // fp16: the wave's V rows go to LDS in two halves of 32 rows (8 KiB), the
+    // second after the first has been read
+    auto dma_v = [&](int h, uint8_t* dst) {
+      const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
+      const int jv = wk + (lane >> 4);
+      if (__builtin_expect(lin, 1)) {
+        const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (jrow + jv) * A.ld_tok);
+        const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + jlast * A.ld_tok);
+        const int64_t step4 = 4 * A.ld_tok * 2;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = 8 * h + ii;
+          const int r = 4 * i + (lane >> 4);
+          const int piece = (lane & 15) ^ (2 * vswz(r));
+          const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(dst + ii * 1024), 16, 0, kVCpol);
+        }
+      } else {
+        const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = 8 * h + ii;
+          const int r = 4 * i + (lane >> 4);
+          const int piece = (lane & 15) ^ (2 * vswz(r));
+          const int jl = min(max(jv + 4 * i, jlo), nk - 1);
+          const uint8_t* row = reinterpret_cast<const uint8_t*>(vbase + (int64_t)krow(prow0, jl) * A.ld_tok);
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(dst + ii * 1024), 16, 0, kVCpol);
+        }
+      }
+    };
+    if constexpr (!Q8) {
+      dma_v(0, vw);
+      if (SMALL && alone) dma_v(1, vw + kVB);
+    }
+    if constexpr (Q8) {
+      // every load is in flight before the first use of a loaded value: the pins
+      // keep the compiler from moving arithmetic (and its waits) between the issues
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qv[kk][0]), "+v"(qv[kk][1]));
+      // the scales, 16 bytes per key (K then V), in the wave's own region; only
+      // this wave reads them back, after its own write
+      uint32_t* sw = s_sc + wave * 256;
+      const int kw = 8 * kg + (col & 7) + 32 * (col >> 3);
+      *reinterpret_cast<u32x4a*>(sw + 4 * kw) = u32x4a{ksc.x, ksc.y, vsc.x, vsc.y};
+    }
+
+    // ---- scores
+    h8 bhi[4], blo[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      qv[kk][0] = qp[8 * kk];
-      qv[kk][1] = qp[8 * kk + 1];
-    }
-  }
-  // fp16: the wave's V rows go to LDS in two halves of 32 rows (8 KiB), the
-  // second after the first has been read
-  auto dma_v = [&](int h, uint8_t* dst) {
-    const uint16_t* vbase = A.v + (int64_t)g * A.ld_head;
-    const int jv = wk + (lane >> 4);
-    if (__builtin_expect(lin, 1)) {
-      const uint8_t* v0 = reinterpret_cast<const uint8_t*>(vbase + (jrow + jv) * A.ld_tok);
-      const uint8_t* vlast = reinterpret_cast<const uint8_t*>(vbase + jlast * A.ld_tok);
-      const int64_t step4 = 4 * A.ld_tok * 2;
+      const float x[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
+                          qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int i = 8 * h + ii;
-        const int r = 4 * i + (lane >> 4);
-        const int piece = (lane & 15) ^ (2 * vswz(r));
-        const uint8_t* row = jv + 4 * i < nk ? v0 + i * step4 : vlast;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(dst + ii * 1024), 16, 0, kVCpol);
-      }
-    } else {
-      const int prow0 = (j0 + jlo) % A.ring_cap;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int i = 8 * h + ii;
-        const int r = 4 * i + (lane >> 4);
-        const int piece = (lane & 15) ^ (2 * vswz(r));
-        const int jl = min(max(jv + 4 * i, jlo), nk - 1);
-        const uint8_t* row = reinterpret_cast<const uint8_t*>(vbase + (int64_t)krow(prow0, jl) * A.ld_tok);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + 16 * piece), (lds_ptr)(dst + ii * 1024), 16, 0, kVCpol);
+      for (int j = 0; j < 8; ++j) {
+        _Float16 hi, lo;
+        split_f16(x[j], hi, lo);
+        bhi[kk][j] = hi;
+        blo[kk][j] = lo;
       }
     }
-  };
-  if constexpr (!Q8) {
-    dma_v(0, vw);
-    if (alone) dma_v(1, vw + kVB);
-  }
-  if constexpr (Q8) {
-    // every load is in flight before the first use of a loaded value: the pins
-    // keep the compiler from moving arithmetic (and its waits) between the issues
+    float z[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qv[kk][0]), "+v"(qv[kk][1]));
-    // the scales, 16 bytes per key (K then V), in the wave's own region; only
-    // this wave reads them back, after its own write
-    uint32_t* sw = s_sc + wave * 256;
-    const int kw = 8 * kg + (col & 7) + 32 * (col >> 3);
-    *reinterpret_cast<u32x4a*>(sw + 4 * kw) = u32x4a{ksc.x, ksc.y, vsc.x, vsc.y};
-  }
-
-  // ---- scores
-  h8 bhi[4], blo[4];
+    for (int t = 0; t < 4; ++t) {
+      f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (!Q8) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const float x[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
-                        qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
+        for (int kk = 0; kk < 4; ++kk) {
+          const h8 av = __builtin_bit_cast(h8, ka[t][kk]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], acc, 0, 0, 0);
+        }
+      } else {
+        // block kk's partial score, times the key's block-kk scale, in block order
+        const uint32_t* sw = s_sc + wave * 256;
+        f32x4v dk[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      _Float16 hi, lo;
-      split_f16(x[j], hi, lo);
-      bhi[kk][j] = hi;
-      blo[kk][j] = lo;
-    }
-  }
-  float z[4][4];
+        for (int kk = 0; kk < 4; ++kk) {
+          const h8 av = codes_to_h8(kc[t][kk].x, kc[t][kk].y);
+          dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], dk[kk], 0, 0, 0);
+        }
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (!Q8) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 av = __builtin_bit_cast(h8, ka[t][kk]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], acc, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          const int kw = 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
+          // (the four fp16 scales as one h4: taking halves of the two dwords
+          // separately made this compiler fold both dwords into the first)
+          const h4 sk = __builtin_bit_cast(h4, *reinterpret_cast<const u32x2a*>(sw + 4 * kw));
+          float a = __builtin_fmaf(dk[0][r], (float)sk[0], 0.0f);
+          a = __builtin_fmaf(dk[1][r], (float)sk[1], a);
+          a = __builtin_fmaf(dk[2][r], (float)sk[2], a);
+          acc[r] = __builtin_fmaf(dk[3][r], (float)sk[3], a);
+        }
       }
-    } else {
-      // block kk's partial score, times the key's block-kk scale, in block order
-      const uint32_t* sw = s_sc + wave * 256;
-      f32x4v dk[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 av = codes_to_h8(kc[t][kk].x, kc[t][kk].y);
-        dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], dk[kk], 0, 0, 0);
-      }
+      // D slot r of this lane = row 4kg + r = key wk + 32(t/2) + 8kg + 4(t%2) + r, head col
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kw = 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
-        // (the four fp16 scales as one h4: taking halves of the two dwords
-        // separately made this compiler fold both dwords into the first)
-        const h4 sk = __builtin_bit_cast(h4, *reinterpret_cast<const u32x2a*>(sw + 4 * kw));
-        float a = __builtin_fmaf(dk[0][r], (float)sk[0], 0.0f);
-        a = __builtin_fmaf(dk[1][r], (float)sk[1], a);
-        a = __builtin_fmaf(dk[2][r], (float)sk[2], a);
-        acc[r] = __builtin_fmaf(dk[3][r], (float)sk[3], a);
+        const int jl = wk + 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
+        z[t][r] = (jl < nk_col && jl >= jlo_col) ? fmul(acc[r], scale) : -INFINITY;
       }
     }
-    // D slot r of this lane = row 4kg + r = key wk + 32(t/2) + 8kg + 4(t%2) + r, head col
+    // ---- the chunk maximum per column, shared by the four waves
+    float M;
+    {
+      float mw = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int jl = wk + 32 * (t >> 1) + 8 * kg + 4 * (t & 1) + r;
-      z[t][r] = (jl < nk_col && jl >= jlo_col) ? fmul(acc[r], scale) : -INFINITY;
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
+      mw = cross_row_max(mw);
+      if constexpr (SMALL) {
+        M = mw;
+      } else {
+        if (lane < 16) s_m[wave][lane] = mw;
+        __syncthreads();
+        M = fmaxf(fmaxf(s_m[0][col], s_m[1][col]), fmaxf(s_m[2][col], s_m[3][col]));
+      }
     }
-  }
-  // ---- the chunk maximum per column, shared by the four waves
-  float M;
-  {
-    float mw = -INFINITY;
+    // ---- weights, their sum, and the P^T operands (block b: slot j = tile 2b + j/4, slot j%4)
+    h8 phi[2], plo[2];
+    float pw[4][4];
+    float lw = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mw = fmaxf(mw, z[t][r]);
-    mw = cross_row_max(mw);
-    if (small) {
-      M = mw;
-    } else {
-      if (lane < 16) s_m[wave][lane] = mw;
-      __syncthreads();
-      M = fmaxf(fmaxf(s_m[0][col], s_m[1][col]), fmaxf(s_m[2][col], s_m[3][col]));
-    }
-  }
-  // ---- weights, their sum, and the P^T operands (block b: slot j = tile 2b + j/4, slot j%4)
-  h8 phi[2], plo[2];
-  float pw[4][4];
-  float lw = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pz = z[t][r] == -INFINITY ? 0.0f : exp_w(fsub(z[t][r], M));
-      lw = fadd(lw, pz);
-      pw[t][r] = pz;
-      if constexpr (!Q8) {
-        _Float16 hi, lo;
-        split_f16(pz, hi, lo);
-        phi[t >> 1][4 * (t & 1) + r] = hi;
-        plo[t >> 1][4 * (t & 1) + r] = lo;
+      for (int r = 0; r < 4; ++r) {
+        const float pz = z[t][r] == -INFINITY ? 0.0f : exp_w(fsub(z[t][r], M));
+        lw = fadd(lw, pz);
+        pw[t][r] = pz;
+        if constexpr (!Q8) {
+          _Float16 hi, lo;
+          split_f16(pz, hi, lo);
+          phi[t >> 1][4 * (t & 1) + r] = hi;
+          plo[t >> 1][4 * (t & 1) + r] = lo;
+        }
       }
-    }
-  lw = cross_row_sum_fixed(lw);
-  if (!small && lane < 16) s_l[wave][lane] = lw;
+    lw = cross_row_sum_fixed(lw);
+    if (!SMALL && lane < 16) s_l[wave][lane] = lw;
 
-  // ---- weighted values: this wave's V rows have landed in LDS
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  f32x4v o[8];
-  if constexpr (!Q8) {
-    // lane (col, kg) reads row 32b + 8kg + 4h + col/4, dims 16dt + 4(col%4) .. +3
-    const int vg = vswz(8 * kg + (col >> 2));
-    const int rbase = (8 * kg + (col >> 2)) * kRowBytes + 8 * (col & 3);
+    // ---- weighted values: this wave's V rows have landed in LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    f32x4v o[8];
+    if constexpr (!Q8) {
+      // lane (col, kg) reads row 32b + 8kg + 4h + col/4, dims 16dt + 4(col%4) .. +3
+      const int vg = vswz(8 * kg + (col >> 2));
+      const int rbase = (8 * kg + (col >> 2)) * kRowBytes + 8 * (col & 3);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (b == 1 && !alone) {
-        // every read of the first half has returned before its rows are replaced
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        dma_v(1, vw);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      for (int b = 0; b < 2; ++b) {
+        if (b == 1 && !(SMALL && alone)) {
+          // every read of the first half has returned before its rows are replaced
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          dma_v(1, vw);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const int hb = SMALL && alone && b == 1 ? kVB : 0;  // where the second half sits
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int a0 = hb + rbase + ((dt ^ vg) << 5);
+          const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0));
+          const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + 4 * kRowBytes));
+          const h8 av = __builtin_bit_cast(h8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[b], o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);
+        }
       }
-      const int hb = b == 1 && alone ? kVB : 0;  // where the second half sits
+    } else {
+      // lane (col, kg) of step b reads code row 32b + 8kg + col/2, bytes 16dt +
+      // 8(col%2) .. +7: the transposed read hands lane (m, kg) the codes of keys
+      // 32b + 8kg + 0..7 at dim 16dt + m
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int a0 = hb + rbase + ((dt ^ vg) << 5);
-        const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0));
-        const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4_ptr)((__attribute__((address_space(3))) uint8_t*)vw + a0 + 4 * kRowBytes));
-        const h8 av = __builtin_bit_cast(h8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[b], o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[b], o[dt], 0, 0, 0);
-      }
-    }
-  } else {
-    // lane (col, kg) of step b reads code row 32b + 8kg + col/2, bytes 16dt +
-    // 8(col%2) .. +7: the transposed read hands lane (m, kg) the codes of keys
-    // 32b + 8kg + 0..7 at dim 16dt + m
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t* sw = s_sc + wave * 256;
-    const int sg = (col >> 1) ^ (kg & 1);  // vswz8 of the rows this lane reads
-    u32x2a sv[2][8];  // V scales of keys 32b + 8kg + j
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sv[b][j] = *reinterpret_cast<const u32x2a*>(sw + 4 * (32 * b + 8 * kg + j) + 2);
-    // The weights p * d are about d times smaller than p, so their fp16 hi + lo
-    // pair would lose bits to fp16's subnormal range.  Each column scales them
-    // by 2^k, k = 29 - (fp16 exponent of the largest |d| among the keys it
-    // weights in this wave), so p * d * 2^k < 2^15, and scales its partial back
-    // by 2^-k (both exact).  k depends only on keys the column attends to.
-    float up, down;
-    {
-      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-      u16x2 mb = {0, 0};
+      for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+      const uint32_t* sw = s_sc + wave * 256;
+      const int sg = (col >> 1) ^ (kg & 1);  // vswz8 of the rows this lane reads
+      u32x2a sv[2][8];  // V scales of keys 32b + 8kg + j
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u16x2 x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, sv[b][j].x & 0x7fff7fffu),
-                                                    __builtin_bit_cast(u16x2, sv[b][j].y & 0x7fff7fffu));
-          if (pw[2 * b + (j >> 2)][j & 3] > 0.0f) mb = __builtin_elementwise_max(mb, x);
-        }
-      const float mf = cross_row_max((float)(mb.x > mb.y ? mb.x : mb.y));
-      const int kx = 29 - ((int)mf >> 10);
-      up = __builtin_bit_cast(float, (uint32_t)(kx + 127) << 23);
-      down = __builtin_bit_cast(float, (uint32_t)(127 - kx) << 23);
-    }
+        for (int j = 0; j < 8; ++j) sv[b][j] = *reinterpret_cast<const u32x2a*>(sw + 4 * (32 * b + 8 * kg + j) + 2);
+      // The weights p * d are about d times smaller than p, so their fp16 hi + lo
+      // pair would lose bits to fp16's subnormal range.  Each column scales them
+      // by 2^k, k = 29 - (fp16 exponent of the largest |d| among the keys it
+      // weights in this wave), so p * d * 2^k < 2^15, and scales its partial back
+      // by 2^-k (both exact).  k depends only on keys the column attends to.
+      float up, down;
+      {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 mb = {0, 0};
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pw[t][r] = fmul(pw[t][r], up);
+          for (int j = 0; j < 8; ++j) {
+            const u16x2 x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, sv[b][j].x & 0x7fff7fffu),
+                                                      __builtin_bit_cast(u16x2, sv[b][j].y & 0x7fff7fffu));
+            if (pw[2 * b + (j >> 2)][j & 3] > 0.0f) mb = __builtin_elementwise_max(mb, x);
+          }
+        const float mf = cross_row_max((float)(mb.x > mb.y ? mb.x : mb.y));
+        const int kx = 29 - ((int)mf >> 10);
+        up = __builtin_bit_cast(float, (uint32_t)(kx + 127) << 23);
+        down = __builtin_bit_cast(float, (uint32_t)(127 - kx) << 23);
+      }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int rb = (32 * b + 8 * kg + (col >> 1)) * kRowBytes8 + 8 * (col & 1);
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        h8 whi, wlo;
+        for (int r = 0; r < 4; ++r) pw[t][r] = fmul(pw[t][r], up);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const h4 sp = __builtin_bit_cast(h4, sv[b][j]);
-          const float w = __builtin_fmaf(pw[2 * b + (j >> 2)][j & 3], (float)sp[bb], 0.0f);
-          _Float16 hi, lo;
-          split_f16(w, hi, lo);
-          whi[j] = hi;
-          wlo[j] = lo;
-        }
+      for (int b = 0; b < 2; ++b) {
+        const int rb = (32 * b + 8 * kg + (col >> 1)) * kRowBytes8 + 8 * (col & 1);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int dt = 2 * bb + e;
-          const i32x2 cv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2_ptr)((__attribute__((address_space(3))) uint8_t*)vw + rb + 16 * (dt ^ sg)));
-          const h8 av = codes_to_h8((uint32_t)cv.x, (uint32_t)cv.y);
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, whi, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wlo, o[dt], 0, 0, 0);
+        for (int bb = 0; bb < 4; ++bb) {
+          h8 whi, wlo;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const h4 sp = __builtin_bit_cast(h4, sv[b][j]);
+            const float w = __builtin_fmaf(pw[2 * b + (j >> 2)][j & 3], (float)sp[bb], 0.0f);
+            _Float16 hi, lo;
+            split_f16(w, hi, lo);
+            whi[j] = hi;
+            wlo[j] = lo;
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int dt = 2 * bb + e;
+            const i32x2 cv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2_ptr)((__attribute__((address_space(3))) uint8_t*)vw + rb + 16 * (dt ^ sg)));
+            const h8 av = codes_to_h8((uint32_t)cv.x, (uint32_t)cv.y);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, whi, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wlo, o[dt], 0, 0, 0);
+          }
         }
       }
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[dt][r] = fmul(o[dt][r], down);
-  }
-  // D slot r of lane (col, kg) = dim 16dt + 4kg + r of column col
-  if (small) {
-    // a small chunk: the wave's partial is the chunk's, for each column whose
-    // token reaches the chunk.  0 + o is what the four-wave sum below gives when
-    // the other waves hold no key of the column (as in a verify call whose
-    // later tokens make the same chunk a four-wave one), so the bits agree.
-    const int p2 = A.ctx_len - T + tk;
-    if (colv && j0 <= p2 && !(A.window && j0 + csz <= p2 - A.window + 1)) {
-      const int h = g * kAttnGroup + hh;
-      float* dst = part + ((int64_t)A.partial_begin + ((int64_t)tk * H_q + h) * A.n_chunks + ci) * PF;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(dst + 4 + 16 * dt + 4 * kg) =
-            f32x4{fadd(0.0f, o[dt][0]), fadd(0.0f, o[dt][1]), fadd(0.0f, o[dt][2]), fadd(0.0f, o[dt][3])};
-      if (kg == 0) {
-        dst[0] = M;
-        dst[1] = lw;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[dt][r] = fmul(o[dt][r], down);
+    }
+    // D slot r of lane (col, kg) = dim 16dt + 4kg + r of column col
+    if constexpr (SMALL) {
+      // a small chunk: the wave's partial is the chunk's, for each column whose
+      // token reaches the chunk.  0 + o is what the four-wave sum below gives when
+      // the other waves hold no key of the column (as in a verify call whose
+      // later tokens make the same chunk a four-wave one), so the bits agree.
+      const int p2 = A.ctx_len - T + tk;
+      if (colv && j0 <= p2 && !(A.window && j0 + csz <= p2 - A.window + 1)) {
+        const int h = g * kAttnGroup + hh;
+        float* dst = part + ((int64_t)A.partial_begin + ((int64_t)tk * H_q + h) * A.n_chunks + ci) * PF;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4*>(dst + 4 + 16 * dt + 4 * kg) =
+              f32x4{fadd(0.0f, o[dt][0]), fadd(0.0f, o[dt][1]), fadd(0.0f, o[dt][2]), fadd(0.0f, o[dt][3])};
+        if (kg == 0) {
+          dst[0] = M;
+          dst[1] = lw;
+        }
+      }
+      return;
+    }
+    // every lane of the wave is done reading the wave's V region before it takes
+    // the partial (LDS reads of one wave complete in order); the wave's own V
+    // region (now read) takes its partial O[column][dim]
+    float* so = reinterpret_cast<float*>(vw);
+    if (colv)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(so + col * HD + 16 * dt + 4 * kg) =
+            f32x4{o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
+    __syncthreads();
+
+    // ---- sum of the four wave partials, in wave order, for each column whose
+    // token reaches this chunk
+    for (int idx = tid; idx < T * kAttnGroup * HD; idx += 256) {
+      const int cc = idx / HD;
+      const int d = idx - cc * HD;
+      const int t2 = cc >> 2;
+      const int p2 = A.ctx_len - T + t2;
+      if (j0 > p2) continue;  // chunk past this token's position
+      if (A.window && j0 + csz <= p2 - A.window + 1) continue;  // chunk before its window
+      float O = 0.0f, L = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        O = fadd(O, reinterpret_cast<const float*>(s_v + w * kVB)[idx]);
+        L = fadd(L, s_l[w][cc]);
+      }
+      const float Mh = fmaxf(fmaxf(s_m[0][cc], s_m[1][cc]), fmaxf(s_m[2][cc], s_m[3][cc]));
+      const int h = g * kAttnGroup + (cc & (kAttnGroup - 1));
+      float* dst = part + ((int64_t)A.partial_begin + ((int64_t)t2 * H_q + h) * A.n_chunks + ci) * PF;
+      dst[4 + d] = O;
+      if (d == 0) {
+        dst[0] = Mh;
+        dst[1] = L;
       }
     }
-    return;
-  }
-  // every lane of the wave is done reading the wave's V region before it takes
-  // the partial (LDS reads of one wave complete in order); the wave's own V
-  // region (now read) takes its partial O[column][dim]
-  float* so = reinterpret_cast<float*>(vw);
-  if (colv)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<f32x4*>(so + col * HD + 16 * dt + 4 * kg) =
-          f32x4{o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
-  __syncthreads();
-
-  // ---- sum of the four wave partials, in wave order, for each column whose
-  // token reaches this chunk
-  for (int idx = tid; idx < T * kAttnGroup * HD; idx += 256) {
-    const int cc = idx / HD;
-    const int d = idx - cc * HD;
-    const int t2 = cc >> 2;
-    const int p2 = A.ctx_len - T + t2;
-    if (j0 > p2) continue;  // chunk past this token's position
-    if (A.window && j0 + csz <= p2 - A.window + 1) continue;  // chunk before its window
-    float O = 0.0f, L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      O = fadd(O, reinterpret_cast<const float*>(s_v + w * kVB)[idx]);
-      L = fadd(L, s_l[w][cc]);
-    }
-    const float Mh = fmaxf(fmaxf(s_m[0][cc], s_m[1][cc]), fmaxf(s_m[2][cc], s_m[3][cc]));
-    const int h = g * kAttnGroup + (cc & (kAttnGroup - 1));
-    float* dst = part + ((int64_t)A.partial_begin + ((int64_t)t2 * H_q + h) * A.n_chunks + ci) * PF;
-    dst[4 + d] = O;
-    if (d == 0) {
-      dst[0] = Mh;
-      dst[1] = L;
-    }
-  }
+  };
+  if (small)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 // Grid (query rows * H_q), 256 threads.  Merges the chunk partials of one
@@ -708,6 +718,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
       L = merge_one_pass<5>(base, nc, tid, s_w, s_red, s_o);
     else if (nc <= 80)
       L = merge_one_pass<10>(base, nc, tid, s_w, s_red, s_o);
+    else if (nc <= 128)
+      L = merge_one_pass<16>(base, nc, tid, s_w, s_red, s_o);
     else
       L = merge_one_pass<kFastLoads>(base, nc, tid, s_w, s_red, s_o);
   } else {

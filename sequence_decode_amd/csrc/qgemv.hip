@@ -240,6 +240,15 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   // written without barriers (one row per item), combined and stored every
   // kTable items
   __shared__ float table[kTable][NW][R * NT];
+  // The one-chunk kernel (plain and SwiGLU) deals its workgroup's items to
+  // the waves as they ask (an LDS counter) when the outputs of all of them fit
+  // dtab; the waves of a workgroup otherwise finish up to 2 us apart
+  // (measured, 8 waves of gate|up at 4 tokens), and every item's arithmetic is
+  // the same whichever wave takes it.
+  constexpr bool kDynOk = STAGE && SP == 1 && R == 1 && NW == 8 && !ROPE;
+  constexpr int kDynMax = kDynFloats / NT;  // items dtab holds
+  __shared__ float dtab[kDynOk ? kDynMax : 1][NT];
+  __shared__ int s_next;
   constexpr int SLOTS = NW / SP;
   constexpr int SEG = 64 * kPairBytes;  // bytes of a full chunk segment
   const int lane = threadIdx.x & 63;
@@ -259,6 +268,9 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   // item k of slot sl covers rows (blockIdx.x + k * gridDim.x) * SLOTS * R + sl * R + [0, R);
   // with SWI, unit u = blockIdx.x + (k / 8) * gridDim.x, and local row
   // lr = 8 (k % 8) + sl is gate row 32u + lr (lr < 32) or up row F + 32u + lr - 32
+  // items 0 .. kPre * NW - 1 go out below, kPre per wave, before the first
+  // barrier (of the staging or of the RMS prologue)
+  if (kDynOk && threadIdx.x == 0) s_next = (RMS || !STAGE ? kRing : kRing - 1) * NW;
   const int stride = (int)gridDim.x * SLOTS * R;
   const int row0 = (int)blockIdx.x * SLOTS * R;
   const int F = N / 2;
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
 #pragma unroll
       for (int d = 0; d < kPre; ++d) younger += ins_of(d);
       wait_vmcnt_rt(younger);
-      asm volatile("s_barrier" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -477,24 +489,8 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
     __syncthreads();
   };
 
-  int kb = 0;
-  for (int k = 0; k < iters; ++k) {
-    if (k + kRing - 1 >= kPre) issue(k + kRing - 1);
-    // wait for item k: the only VMEM operations younger than its DMAs are the
-    // DMAs of the items issued after it (and, with SWI, the block stores below;
-    // no other global store happens in the loop)
-    int younger = 0;
-#pragma unroll
-    for (int d = 1; d < kRing; ++d) younger += ins_of(k + d);
-    if constexpr (SWI) {
-      // the previous unit's block stores (a code and a scale store in each
-      // wave that holds a (token, dim) of it) came after this item's DMAs
-      if (k > 0 && (k & 7) == 0 && wave * 64 < NT * 32) younger += 2;
-    }
-    wait_vmcnt_rt(younger);
-    const int r0 = row_of(k);
-    const uint8_t* st = ring + (k % kRing) * (R * SEG);
-    float v[R][NT];
+  // the cells of the R rows at st (rows r0 ..) for every token
+  auto item_cells = [&](const uint8_t* st, int r0, float (&v)[R][NT]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (pv && r0 + r < N) {
@@ -513,12 +509,16 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
         for (int t = 0; t < NT; ++t) v[r][t] = 0.0f;
       }
     }
+  };
+  // the fixed lane tree over the cells; put(r, t, total) runs on one lane per
+  // (row, token)
+  auto item_sums = [&](float (&v)[R][NT], auto&& put) {
     if constexpr (NT >= 2 && NT <= 8) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float tot = wave_sum_fixed_tr<NT>(v[r], lane);
         const int tt = tree_token(lane, NT);
-        if (lane < tree_writers(NT) && tt < NT) table[k % kTable][wave][r * NT + tt] = tot;
+        if (lane < tree_writers(NT) && tt < NT) put(r, tt, tot);
       }
     } else {
 #pragma unroll
@@ -529,8 +529,86 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int t = 0; t < NT; ++t) table[k % kTable][wave][r * NT + t] = v[r][t];
+          for (int t = 0; t < NT; ++t) put(r, t, v[r][t]);
     }
+  };
+
+  if constexpr (kDynOk) {
+    // item i of the workgroup = item i / NW of slot i % NW: the row of the
+    // static order.  Wave w starts with items w (and w + NW with two issued
+    // ahead), which went out above.
+    const int total = NW * iters;
+    if (total <= kDynMax) {
+      auto row_item = [&](int i) { return row_at(i / NW, i % NW); };
+      // (the LDS add is written out: as a builtin the compiler makes it wait
+      // for every DMA in flight first, since they write LDS too)
+      const uint32_t next_addr = (uint32_t)(uintptr_t)(lds_ptr)&s_next;
+      auto grab = [&]() {
+        int v = 0;
+        if (lane == 0)
+          asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(next_addr), "v"(1) : "memory");
+        return __builtin_amdgcn_readfirstlane(v);
+      };
+      int cur = wave, cs = 0;  // item this wave computes next, and its ring slot
+      int nxt = wave + NW;     // the one after it, if already issued
+      bool ahead = kPre == 2;
+      while (cur < total) {
+        if (!ahead) {
+          nxt = grab();
+          if (nxt < total && row_item(nxt) < N)
+            dma_segment(w + (int64_t)row_item(nxt) * row_bytes, ring + (cs ^ 1) * SEG, seg_bytes, lane);
+        }
+        ahead = false;
+        wait_vmcnt_rt(nxt < total && row_item(nxt) < N ? n_ins : 0);
+        const int row = row_item(cur);
+        if (row < N) {
+          float v[R][NT];
+          item_cells(ring + cs * SEG, row, v);
+          item_sums(v, [&](int, int t, float tot) { dtab[cur][t] = tot; });
+        }
+        cur = nxt;
+        cs ^= 1;
+      }
+      __syncthreads();
+      if constexpr (SWI) {
+        // unit ui of the workgroup: items 64 ui .. 64 ui + 63 are its gate
+        // rows 0..31 and up rows 0..31; one 32-lane group per (unit, token)
+        for (int e = threadIdx.x; e < (iters / 8) * NT * 32; e += 64 * NW) {
+          const int ui = e / (NT * 32);
+          const int t = (e >> 5) % NT;
+          const int i = e & 31;
+          swiglu_epilogue(dtab[64 * ui + i][t], dtab[64 * ui + 32 + i][t], t, i,
+                          (int)blockIdx.x + ui * (int)gridDim.x, F, units, oq, od);
+        }
+      } else {
+        for (int i = threadIdx.x; i < total * NT; i += 64 * NW) {
+          const int row = row_item(i / NT);
+          if (row < N) store_out(dtab[i / NT][i % NT], row, i % NT, residual, y, ldy);
+        }
+      }
+      return;
+    }
+  }
+
+  int kb = 0;
+  for (int k = 0; k < iters; ++k) {
+    if (k + kRing - 1 >= kPre) issue(k + kRing - 1);
+    // wait for item k: the only VMEM operations younger than its DMAs are the
+    // DMAs of the items issued after it (and, with SWI, the block stores below;
+    // no other global store happens in the loop)
+    int younger = 0;
+#pragma unroll
+    for (int d = 1; d < kRing; ++d) younger += ins_of(k + d);
+    if constexpr (SWI) {
+      // the previous unit's block stores (a code and a scale store in each
+      // wave that holds a (token, dim) of it) came after this item's DMAs
+      if (k > 0 && (k & 7) == 0 && wave * 64 < NT * 32) younger += 2;
+    }
+    wait_vmcnt_rt(younger);
+    const int r0 = row_of(k);
+    float v[R][NT];
+    item_cells(ring + (k % kRing) * (R * SEG), r0, v);
+    item_sums(v, [&](int r, int t, float tot) { table[k % kTable][wave][r * NT + t] = tot; });
     if constexpr (SWI) {
       if ((k & 7) == 7) {
         // the unit's 64 rows are in the table: m = silu(g) * u for 32 dims and

@@ -38,6 +38,10 @@ __device__ __forceinline__ void store_out(float v, int n, int t, const float* re
 
 constexpr int kRing = 2;
 constexpr int kTable = 32;
+// outputs (items x tokens) of a workgroup that the one-chunk kernel keeps until
+// the end when it deals the items to its waves on demand; 4 KiB of static LDS,
+// which with the output table leaves the 144 KiB of dynamic LDS room
+constexpr int kDynFloats = 1024;
 // rows per streaming item (one row per item measured best: deeper or wider
 // items lowered the bytes in flight per CU)
 constexpr int dma_rows(int) { return 1; }

@@ -137,32 +137,52 @@ def time_graph(torch, fn, steps, warmup):
     return dt / steps
 
 
+# launches of each shape's 32 matrices before the timed ones in the roofline
+# pass: one eager round, one graph replay
+ROOF_WARM_ROUNDS = 2
+# timed replays per shape
+ROOF_REPS = 4
+
+
 def roofline_pass(torch, sweep, n_tok, reps):
-    """Average duration of the GEMV kernel per shape: HIP events on the launch
-    stream around `reps` rounds of the shape's 32 matrices launched back to back
-    (nothing else in between), so each average is one kernel's duration plus
-    the dispatch gap to the next launch of the same kernel."""
+    """Average duration of the GEMV kernel per shape: the shape's 32 matrices
+    launched back to back as one HIP graph (as the sweep runs them), replayed
+    `reps` times between HIP events on the graph's stream (nothing else in
+    between), so each average is one kernel's duration plus the dispatch gap to
+    the next launch of the same kernel."""
     import ctypes
     lib = sweep.sd._lib.load()
-    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = ctypes.c_void_p
     per = {}
     tot_bytes, tot_ms, launches = 0, 0.0, 0
+    s = torch.cuda.Stream()
     for name, N, K in SHAPES:
         xq, xd, y = sweep.xq[K], sweep.xd[K], sweep.y[name]
         def run():
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             for L in sweep.w:
-                lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()), P(xd.data_ptr()),
-                                        n_tok, None, P(y.data_ptr()), N, st)
+                rc = lib.sd_qgemv_q8_0_batch(P(L[name].data_ptr()), N, K, P(xq.data_ptr()), P(xd.data_ptr()),
+                                             n_tok, None, P(y.data_ptr()), N, st)
+                if rc:
+                    raise sweep.sd.SdError("sd_qgemv_q8_0_batch", rc)
         run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            run()
+            g.capture_end()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            run()
-        e1.record()
+        with torch.cuda.stream(s):
+            g.replay()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
         torch.cuda.synchronize()
+        del g
         ms = e0.elapsed_time(e1)
         n = reps * len(sweep.w)
         b = gemv_bytes(N, K, n_tok) * n
@@ -713,12 +733,16 @@ def trace_summary(trace_db, fetch_db=None, write_db=None, n_tok=4):
     staged = f"k_qgemv_q8_0_dma<{n_tok}, 1, 1, 8, true, false, false, false>"
     four = f"k_qgemv_q8_0_dma<{n_tok}, 4, 1, 4, false, false, false, false>"
 
+    per_shape_n = (ROOF_WARM_ROUNDS + ROOF_REPS) * N_LAYERS  # dispatches per shape in the pass
+    skip = ROOF_WARM_ROUNDS * N_LAYERS
+
     def roofline_launches(rows):
-        a = [v for n, v in rows if short(n) == staged][-480:]
-        b = [v for n, v in rows if short(n) == four][-160:]
-        if len(a) < 480 or len(b) < 160:
+        a = [v for n, v in rows if short(n) == staged][-3 * per_shape_n:]
+        b = [v for n, v in rows if short(n) == four][-per_shape_n:]
+        if len(a) < 3 * per_shape_n or len(b) < per_shape_n:
             raise RuntimeError("the database does not hold the roofline pass")
-        return {"qkv": a[32:160], "o": a[192:320], "gate_up": a[352:480], "down": b[32:160]}
+        return {"qkv": a[skip:per_shape_n], "o": a[per_shape_n + skip:2 * per_shape_n],
+                "gate_up": a[2 * per_shape_n + skip:], "down": b[skip:]}
 
     tr = dispatches(trace_db)
     per = {}
@@ -738,10 +762,24 @@ def trace_summary(trace_db, fetch_db=None, write_db=None, n_tok=4):
         out["per_shape"][k] = {"trace_avg_us": round(statistics.mean(v), 3), "GB_s": round(b / statistics.mean(v) / 1e3, 1)}
         tot_us += sum(v)
         tot_b += b * len(v)
-    out["trace_avg_us_per_launch"] = round(tot_us / 512, 3)
-    out["trace_launches"] = 512
+    n_roof = 4 * ROOF_REPS * N_LAYERS
+    out["trace_avg_us_per_launch"] = round(tot_us / n_roof, 3)
+    out["trace_launches"] = n_roof
     out["achieved_GB_s"] = round(tot_b / tot_us / 1e3, 1)
     out["gemv_us_per_sweep"] = round(sum(statistics.mean(v) for v in roof.values()) * N_LAYERS, 1)
+    # the same kernels in the graph-replayed n_tok sweeps of the run (every
+    # launch before the roofline pass, in layer order QKV, O, gate|up, down):
+    # what a sweep's wall time holds
+    sw = [(short(n), v) for n, v in tr if short(n) in (staged, four)][:-4 * per_shape_n]
+    if sw and len(sw) % (4 * N_LAYERS) == 0 and all(
+            nm == (four if i % 4 == 3 else staged) for i, (nm, _) in enumerate(sw)):
+        by = {k: [v for i, (_, v) in enumerate(sw) if i % 4 == j] for j, k in enumerate(shapes)}
+        out["graph_sweeps"] = {
+            "sweeps": len(sw) // (4 * N_LAYERS),
+            "per_shape_avg_us": {k: round(statistics.mean(v), 3) for k, v in by.items()},
+            "gemv_us_per_sweep": round(sum(statistics.mean(v) for v in by.values()) * N_LAYERS, 1),
+            "GB_s": round(sum(gemv_bytes(*shapes[k], n_tok) for k in shapes) * N_LAYERS /
+                          (sum(statistics.mean(v) for v in by.values()) * N_LAYERS) / 1e3, 1)}
     if fetch_db and write_db:
         f = dispatches(fetch_db, "FETCH_SIZE")
         w = dispatches(write_db, "WRITE_SIZE")
@@ -750,12 +788,12 @@ def trace_summary(trace_db, fetch_db=None, write_db=None, n_tok=4):
         ff = (1 << 30) / (fcal[-1] * 1024)
         wf = (1 << 30) / (wcal[-1] * 1024)
         rf, rw = roofline_launches(f), roofline_launches(w)
-        fetched = sum(sum(v) for v in rf.values()) * 1024 * ff / 512
-        written = sum(sum(v) for v in rw.values()) * 1024 * wf / 512
+        fetched = sum(sum(v) for v in rf.values()) * 1024 * ff / n_roof
+        written = sum(sum(v) for v in rw.values()) * 1024 * wf / n_roof
         out["fetch_factor"], out["write_factor"] = round(ff, 4), round(wf, 4)
         out["traffic_bytes_per_launch"] = int(round(fetched + written))
-        out["algorithmic_bytes_per_launch"] = int(round(tot_b / 512))
-        out["traffic_over_algorithmic"] = round((fetched + written) / (tot_b / 512), 4)
+        out["algorithmic_bytes_per_launch"] = int(round(tot_b / n_roof))
+        out["traffic_over_algorithmic"] = round((fetched + written) / (tot_b / n_roof), 4)
     src = os.path.join(ROOT, "sequence_decode_amd", "csrc", "qgemv.hip")
     out["kernel_source_sha256"] = hashlib.sha256(open(src, "rb").read()).hexdigest()
     return out
@@ -987,7 +1025,7 @@ def main():
     dt, runs = sweep_median(torch, sweep, n, args.steps, args.warmup)
     value = sweep.bytes_per_step(n) / dt / 1e9
 
-    tb, tms, launches, per_shape = roofline_pass(torch, sweep, n, reps=4)
+    tb, tms, launches, per_shape = roofline_pass(torch, sweep, n, reps=ROOF_REPS)
     achieved = tb / (tms / 1e3) / 1e9
     log(f"GEMV kernel (event-timed, {launches} launches): {achieved:.1f} GB/s; {per_shape}")
     floor = launch_floor_us(torch)

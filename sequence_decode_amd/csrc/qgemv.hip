@@ -268,9 +268,15 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
   // item k of slot sl covers rows (blockIdx.x + k * gridDim.x) * SLOTS * R + sl * R + [0, R);
   // with SWI, unit u = blockIdx.x + (k / 8) * gridDim.x, and local row
   // lr = 8 (k % 8) + sl is gate row 32u + lr (lr < 32) or up row F + 32u + lr - 32
+  // weight items issued before the loop: both ring slots where the start
+  // waits on something else anyway (the RMS prologue's arithmetic, the
+  // per-wave activation loads), one where the staged copies are all it waits
+  // for (a second item in flight there measured slower: QKV 7.3 -> 8.1 us,
+  // O 5.8 -> 7.1 us at 4 tokens)
+  constexpr int kPre = (RMS || !STAGE) ? kRing : kRing - 1;
   // items 0 .. kPre * NW - 1 go out below, kPre per wave, before the first
   // barrier (of the staging or of the RMS prologue)
-  if (kDynOk && threadIdx.x == 0) s_next = (RMS || !STAGE ? kRing : kRing - 1) * NW;
+  if (kDynOk && threadIdx.x == 0) s_next = kPre * NW;
   const int stride = (int)gridDim.x * SLOTS * R;
   const int row0 = (int)blockIdx.x * SLOTS * R;
   const int F = N / 2;
@@ -308,12 +314,6 @@ __global__ __launch_bounds__(64 * NW) void k_qgemv_q8_0_dma(
         dma_segment(w + (int64_t)(r0 + r) * row_bytes + (int64_t)chunk * SEG, l + r * SEG, seg_bytes, lane);
   };
 
-  // weight items issued before the loop: both ring slots where the start
-  // waits on something else anyway (the RMS prologue's arithmetic, the
-  // per-wave activation loads), one where the staged copies are all it waits
-  // for (a second item in flight there measured slower: QKV 7.3 -> 8.1 us,
-  // O 5.8 -> 7.1 us at 4 tokens)
-  constexpr int kPre = (RMS || !STAGE) ? kRing : kRing - 1;
   if constexpr (RMS) {
     // this workgroup's own q8 blocks of rmsnorm(x): the rows are loaded (and
     // waited for) before any weight goes out, so that the weights' DMAs,

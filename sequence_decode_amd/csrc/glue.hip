@@ -41,10 +41,13 @@ __global__ __launch_bounds__(256) void k_quantize_q8(const float* __restrict__ x
   quantize_lane(v, valid, xq + t * K + b * 32 + lane32, xd + t * nb + b, lane32);
 }
 
-// One workgroup of 1024 threads per token row, the row held in registers
-// (EPT values per thread, element j*1024 + tid).  The sum of squares runs per
-// thread in j order, then over the 64 lanes of a wave (fixed tree), then over
-// the 16 waves in wave order.
+// Workgroups of 1024 threads, EPT per token row (blockIdx.y = j): each holds
+// the whole row in registers (EPT values per thread, element j*1024 + tid) for
+// the sum of squares, which runs per thread in j order, then over the 64 lanes
+// of a wave (fixed tree), then over the 16 waves in wave order; workgroup j
+// then normalizes and quantizes elements j*1024 .. j*1024 + 1023 only.  Every
+// workgroup of a row forms the same sum, so splitting the quantization (the
+// costly part: a division per element) over EPT compute units changes no bits.
 template <int EPT>
 __global__ __launch_bounds__(1024) void k_rmsnorm_q8(const float* __restrict__ x, int64_t ldx,
                                                      int64_t D, const float* __restrict__ gamma,
@@ -52,15 +55,16 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_q8(const float* __restrict__ x
                                                      float* __restrict__ xd, float* y) {
   __shared__ float part[16];
   const int t = blockIdx.x;
+  const int js = blockIdx.y;  // the slice this workgroup quantizes
   const int tid = threadIdx.x;
   const float* xr = x + (int64_t)t * ldx;
-  constexpr bool kGammaEarly = EPT <= 16;  // registers for gamma too (no spills up to 16)
-  float v[EPT], gm[kGammaEarly ? EPT : 1];
+  const int64_t is = (int64_t)js * 1024 + tid;
+  const float gs = is < D ? gamma[is] : 0.0f;
+  float v[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int64_t i = (int64_t)j * 1024 + tid;
     v[j] = i < D ? xr[i] : 0.0f;
-    if (kGammaEarly) gm[kGammaEarly ? j : 0] = i < D ? gamma[i] : 0.0f;
   }
   float ss = 0.0f;
 #pragma unroll
@@ -73,16 +77,15 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_q8(const float* __restrict__ x
   for (int w = 1; w < 16; ++w) total = fadd(total, part[w]);
   const float r = fdiv(1.0f, sqrtf(fadd(fdiv(total, (float)D), eps)));
   const int64_t nb = D / 32;
+  if ((int64_t)js * 1024 >= D) return;  // uniform: D is a multiple of 32, blocks stay whole
+  float vs = v[0];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int64_t i = (int64_t)j * 1024 + tid;
-    if ((int64_t)j * 1024 >= D) break;  // uniform: D is a multiple of 32, blocks stay whole
-    const bool valid = i < D;
-    const float gj = kGammaEarly ? gm[kGammaEarly ? j : 0] : (valid ? gamma[i] : 0.0f);
-    const float o = valid ? fmul(fmul(v[j], r), gj) : 0.0f;
-    if (valid && y) y[(int64_t)t * D + i] = o;
-    quantize_lane(o, valid, xq + (int64_t)t * D + i, xd + (int64_t)t * nb + (i >> 5), tid & 31);
-  }
+  for (int j = 1; j < EPT; ++j)
+    if (j == js) vs = v[j];
+  const bool valid = is < D;
+  const float o = valid ? fmul(fmul(vs, r), gs) : 0.0f;
+  if (valid && y) y[(int64_t)t * D + is] = o;
+  quantize_lane(o, valid, xq + (int64_t)t * D + is, xd + (int64_t)t * nb + (is >> 5), tid & 31);
 }
 
 __global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu, int64_t ldgu,
@@ -201,13 +204,13 @@ hipError_t launch_quantize_q8(const float* x, int64_t ldx, int n_tok, int64_t K,
 hipError_t launch_rmsnorm_q8(const float* x, int64_t ldx, int n_tok, int64_t D, const float* gamma,
                              float eps, int8_t* xq, float* xd, float* y, hipStream_t st) {
   if (D <= 4096)
-    hipLaunchKernelGGL(k_rmsnorm_q8<4>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+    hipLaunchKernelGGL(k_rmsnorm_q8<4>, dim3(n_tok, 4), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
   else if (D <= 8192)
-    hipLaunchKernelGGL(k_rmsnorm_q8<8>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+    hipLaunchKernelGGL(k_rmsnorm_q8<8>, dim3(n_tok, 8), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
   else if (D <= 16384)
-    hipLaunchKernelGGL(k_rmsnorm_q8<16>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+    hipLaunchKernelGGL(k_rmsnorm_q8<16>, dim3(n_tok, 16), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
   else
-    hipLaunchKernelGGL(k_rmsnorm_q8<32>, dim3(n_tok), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
+    hipLaunchKernelGGL(k_rmsnorm_q8<32>, dim3(n_tok, 32), dim3(1024), 0, st, x, ldx, D, gamma, eps, xq, xd, y);
   return hipGetLastError();
 }
 

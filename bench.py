@@ -903,11 +903,11 @@ def step_trace_summary(trace_db, n_steps=10):
     rows = []
     import sqlite3
     con = sqlite3.connect(trace_db)
-    q = ("select k.display_name, d.start, d.end, d.grid_size_x from rocpd_kernel_dispatch d join "
-         "rocpd_info_kernel_symbol k on d.kernel_id = k.id order by d.start")
-    for n, s_, e, g in con.execute(q):
+    q = ("select k.display_name, d.start, d.end, d.grid_size_x, d.grid_size_y from rocpd_kernel_dispatch d "
+         "join rocpd_info_kernel_symbol k on d.kernel_id = k.id order by d.start")
+    for n, s_, e, gx, gy in con.execute(q):
         if "sd::" in n:
-            rows.append((_short_kernel(n), s_, e, g))
+            rows.append((_short_kernel(n), s_, e, f"{gx}" if gy == 1 else f"{gx}x{gy}"))
     ends, prev = [], None
     for i, r in enumerate(rows):
         if r[0].startswith("k_argmax"):
@@ -926,7 +926,7 @@ def step_trace_summary(trace_db, n_steps=10):
             acc.setdefault((n, g), []).append((e - s_) / 1e3)
     k = len(spans)
     lines = [f"{k} steps: span {statistics.mean(spans):.1f} us per step, kernel-busy {statistics.mean(busy):.1f} us",
-             "", "| kernel | grid | per step | avg us | us per step |", "|---|---|---|---|---|"]
+             "", "| kernel | grid (threads, x or x by y) | per step | avg us | us per step |", "|---|---|---|---|---|"]
     for (n, g), v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {n[:100]} | {g} | {len(v) / k:.1f} | {statistics.mean(v):.2f} | {sum(v) / k:.1f} |")
     return "\n".join(lines)

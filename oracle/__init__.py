@@ -36,6 +36,8 @@ def lib():
         L.oracle_f16_decode.argtypes = [P, i64, P]
         L.oracle_quantize_q8_act.argtypes = [P, i64, i32, i64, P, P]
         L.oracle_quantize_q8_act.restype = i32
+        L.oracle_quantize_kv_q4_0.argtypes = [P, i64, i64, P, P]
+        L.oracle_quantize_kv_q4_0.restype = i32
         L.oracle_qgemv_q8_0.argtypes = [P, i64, i64, P, i64, P, i64, i32, P, i64,
                                         P, i64, P, P, P, i64]
         L.oracle_rope_posvec.argtypes = [P, i32, i32, i32, i64, i64, P, f64, i32]
@@ -176,6 +178,43 @@ def dequant_kv_q8_0(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
     return codes.astype(np.float64) * np.repeat(d, 32, axis=-1)
 
 
+def quantize_kv_q4_0(x: np.ndarray):
+    """q4_0 blocks of cache rows x [..., D] fp32 (the Q4 cache type of the Q4/Q8
+    and Q8/Q4 cases in "feat(qwen36): complete concurrent serving implementation
+    with speculation", "Validation"): per run of 32 dims, d = amax / 7 and codes
+    c = round-half-away(x / d) in [-8, 7], stored as nibbles c + 8, two per byte
+    (low nibble: the even dim); the stored scale is fp16(d), nearest even.
+    Returns (packed uint8 [..., D/2], scale bits uint16 [..., D/32])."""
+    x = _req(x, np.float32)
+    D = x.shape[-1]
+    flat = x.reshape(-1, D)
+    packed = np.empty((flat.shape[0], D // 2), np.uint8)
+    d = np.empty((flat.shape[0], D // 32), np.float32)
+    rc = lib().oracle_quantize_kv_q4_0(_ptr(flat), flat.shape[0], D, _ptr(packed), _ptr(d))
+    if rc != 0:
+        raise ValueError("quantize_kv_q4_0: D must be a multiple of 32 and x finite")
+    return (packed.reshape(x.shape[:-1] + (D // 2,)),
+            f32_to_f16_bits(d).reshape(x.shape[:-1] + (D // 32,)))
+
+
+def dequant_kv_q4_0(packed: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """The values d * (n - 8) of q4_0 cache rows, in fp64 (exact)."""
+    packed = np.asarray(packed, np.uint8)
+    n = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.int64)
+    n[..., 0::2] = packed & 0x0F
+    n[..., 1::2] = packed >> 4
+    d = np.asarray(scale_bits, np.uint16).view(np.float16).astype(np.float64)
+    return (n - 8).astype(np.float64) * np.repeat(d, 32, axis=-1)
+
+
+def dequant_kv(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """dequant_kv_q8_0 for int8 codes [..., D], dequant_kv_q4_0 for packed
+    uint8 nibbles [..., D/2]."""
+    if np.asarray(codes).dtype == np.uint8:
+        return dequant_kv_q4_0(codes, scale_bits)
+    return dequant_kv_q8_0(codes, scale_bits)
+
+
 def attn_decode_one_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_len: int,
                         scale: float) -> np.ndarray:
     """attn_decode_one over fp64 keys and values [cap][H_kv][D]."""
@@ -214,14 +253,16 @@ def attn_verify(q_rows: np.ndarray, caches, ctx_lens, n_new, scale: float, windo
     implementation with speculation", "Summary"), position j stored in row
     tables[s][j // block_size] * block_size + j % block_size.
     caches[s] = (k_bits, v_bits) of an fp16 cache, or (kq, kd_bits, vq, vd_bits)
-    of a q8_0 cache, attended over its dequantized values.
+    of a quantized cache, attended over its dequantized values; K and V each
+    q8_0 (int8 codes [..., D]) or q4_0 (uint8 nibbles [..., D/2]), so mixed
+    Q4/Q8 and Q8/Q4 caches too.
     q_rows [sum(n_new)][H_q][D] -> same shape."""
     out = []
     r = 0
     for s, T in enumerate(n_new):
         if len(caches[s]) == 4:
             kq, kd, vq, vd = caches[s]
-            k_bits, v_bits = dequant_kv_q8_0(kq, kd), dequant_kv_q8_0(vq, vd)
+            k_bits, v_bits = dequant_kv(kq, kd), dequant_kv(vq, vd)
             one = attn_decode_one_f64
         else:
             k_bits, v_bits = caches[s]

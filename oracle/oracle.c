@@ -117,6 +117,53 @@ int oracle_quantize_q8_act(const float* x, int64_t ldx, int n_tok, int64_t K,
 }
 
 /*
+ * q4_0 KV rows, the Q4 cache type of the Q4/Q8 and Q8/Q4 attention cases of
+ * "feat(qwen36): complete concurrent serving implementation with speculation",
+ * "Validation".  The pages name the type only; the reading used here is the
+ * 4-bit analogue of the q8_0 rows above, per row and block b of 32 values:
+ *   amax = max |x_i|;  d = amax / 7 (fp32 IEEE division);
+ *   c_i  = round_half_away(x_i / d) (fp32 division, C roundf), clamped to
+ *          [-8, 7]; when d == 0 every c_i is 0;
+ *   stored nibble n_i = c_i + 8, two per byte: byte j of the block holds
+ *   n_{2j} in its low and n_{2j+1} in its high four bits.
+ * Outputs: packed[r*(D/2) + b*16 + j], d_out[r*(D/32) + b] (fp32; the cache
+ * stores it rounded to fp16).  Value of a stored element: fp16(d) * (n - 8).
+ * Returns 0, or -1 when D is not a multiple of 32 or an input is not finite.
+ */
+int oracle_quantize_kv_q4_0(const float* x, int64_t n_rows, int64_t D, uint8_t* packed,
+                            float* d_out) {
+  if (D % 32 != 0) return -1;
+  int64_t nb = D / 32;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* xb = x + r * D + b * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) {
+        if (!isfinite(xb[i])) return -1;
+        float a = fabsf(xb[i]);
+        if (a > amax) amax = a;
+      }
+      float d = amax / 7.0f;
+      d_out[r * nb + b] = d;
+      int nib[32];
+      for (int i = 0; i < 32; ++i) {
+        int c = 0;
+        if (d != 0.0f) {
+          float q = roundf(xb[i] / d);
+          if (q > 7.0f) q = 7.0f;
+          if (q < -8.0f) q = -8.0f;
+          c = (int)q;
+        }
+        nib[i] = c + 8;
+      }
+      for (int j = 0; j < 16; ++j)
+        packed[r * (D / 2) + b * 16 + j] = (uint8_t)(nib[2 * j] | (nib[2 * j + 1] << 4));
+    }
+  }
+  return 0;
+}
+
+/*
  * q8_0 matrix-vector product for n_tok token rows [P5 CUDA kernels: narrow-batch
  * q8_0 matmul].  W holds N rows of K/32 blocks, each block 34 bytes: an fp16
  * scale d_w (little-endian) then 32 int8 weights.  For token t and row n:

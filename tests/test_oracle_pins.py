@@ -573,3 +573,83 @@ def test_attn_q8_0_equals_fp16_on_exact_values(oracle_mod):
     a8b = oracle_mod.attn_verify(q, [(kc, kd, vc, vd2)], [L], [3], 0.7)
     assert not np.array_equal(a8b[:, :2, 32:], a8[:, :2, 32:])
     assert np.array_equal(a8b[:, :2, :32], a8[:, :2, :32]) and np.array_equal(a8b[:, 2:], a8[:, 2:])
+
+
+# ------------------------------------------------------------------ q4_0 KV cache
+
+def test_kv_q4_0_quantizer_hand_values(oracle_mod):
+    """amax 0.875: d = 0.875 / 7 = 0.125 exactly, stored as fp16 0x3000; codes of
+    0.875, -0.875, 0.5, 0.3125, -0.3125, 0.0625 are 7, -7, 4, round(2.5) = 3,
+    -3, round(0.5) = 1 (half away from zero), stored as nibbles c + 8 with the
+    even dim in the low four bits: bytes 0x1F, 0xBC, 0x95, then 0x88 (code 0 and
+    code 0).  An all-zero block gets nibbles 8 (bytes 0x88) and scale +0."""
+    x = np.zeros((2, 64), np.float32)
+    x[0, :6] = [0.875, -0.875, 0.5, 0.3125, -0.3125, 0.0625]
+    x[0, 33] = -1.75
+    packed, sb = oracle_mod.quantize_kv_q4_0(x)
+    assert packed.shape == (2, 32) and packed.dtype == np.uint8
+    assert sb.shape == (2, 2) and sb.dtype == np.uint16
+    assert sb[0, 0] == 0x3000 and sb[0, 1] == np.float16(0.25).view(np.uint16)
+    assert list(packed[0, :4]) == [0x1F, 0xBC, 0x95, 0x88]
+    assert np.all(packed[0, 4:16] == 0x88)
+    # block 1: dim 33 (odd: high nibble of byte 0 of the block) is -7
+    assert packed[0, 16] == (8 | (1 << 4)) and np.all(packed[0, 17:] == 0x88)
+    assert np.all(packed[1] == 0x88) and sb[1, 0] == 0 and sb[1, 1] == 0
+    back = oracle_mod.dequant_kv_q4_0(packed, sb)
+    assert list(back[0, :6]) == [0.875, -0.875, 0.5, 0.375, -0.375, 0.125]
+    assert back[0, 33] == -1.75 and not back[1].any()
+
+
+def test_kv_q4_0_round_trip_bounds(oracle_mod):
+    """Values c * 2^-3 with a 7 in every block come back exactly; N(0,1) rows come
+    back within d/2 + 7 |d - fp16(d)| per element."""
+    g = synth.rng(92)
+    c = g.integers(-7, 8, size=(5, 2, 64)).astype(np.float32)
+    c[..., 0] = 7.0
+    c[..., 33] = -7.0
+    x = c * np.float32(2.0 ** -3)
+    packed, sb = oracle_mod.quantize_kv_q4_0(x)
+    assert np.all(sb == np.float16(2.0 ** -3).view(np.uint16))
+    assert np.array_equal(oracle_mod.dequant_kv_q4_0(packed, sb), x.astype(np.float64))
+    y = g.standard_normal((40, 3, 128), dtype=np.float32)
+    packed, sb = oracle_mod.quantize_kv_q4_0(y)
+    back = oracle_mod.dequant_kv_q4_0(packed, sb)
+    amax = np.abs(y.astype(np.float64)).reshape(40, 3, 4, 32).max(axis=-1)
+    d = amax / 7.0
+    d16 = sb.view(np.float16).astype(np.float64)
+    bound = np.repeat(0.5 * d + 7.0 * np.abs(d - d16) + 1e-12, 32, axis=-1)
+    assert np.all(np.abs(back - y) <= bound)
+    # every code is within [-7, 7]: nibble 0 (code -8) never appears
+    lo, hi = packed & 0x0F, packed >> 4
+    assert lo.min() >= 1 and hi.min() >= 1
+
+
+def test_attn_mixed_q4_q8_equals_fp16_on_exact_values(oracle_mod):
+    """Q4/Q8 and Q8/Q4 caches (K one type, V the other) whose values are exactly
+    fp16 numbers give the bits of the fp16-cache attention over those numbers,
+    and so do Q4/Q4 caches."""
+    g = synth.rng(93)
+    L, H_q, H_kv, Dh = 41, 4, 2, 64
+    kc4 = g.integers(-7, 8, size=(L, H_kv, Dh))
+    vc4 = g.integers(-7, 8, size=(L, H_kv, Dh))
+    kc8 = g.integers(-127, 128, size=(L, H_kv, Dh), dtype=np.int8)
+    vc8 = g.integers(-127, 128, size=(L, H_kv, Dh), dtype=np.int8)
+
+    def pack(c):
+        n = (c + 8).astype(np.uint8)
+        return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+    def scales(v):
+        return np.full((L, H_kv, Dh // 32), np.float16(v).view(np.uint16), np.uint16)
+
+    def f16(c, v):
+        return (c.astype(np.float32) * np.float32(v)).astype(np.float16).view(np.uint16)
+
+    q = g.standard_normal((2, H_q, Dh), dtype=np.float32)
+    cases = [((pack(kc4), scales(2.0 ** -3), vc8, scales(2.0 ** -6)), (f16(kc4, 2.0 ** -3), f16(vc8, 2.0 ** -6))),
+             ((kc8, scales(2.0 ** -7), pack(vc4), scales(2.0 ** -2)), (f16(kc8, 2.0 ** -7), f16(vc4, 2.0 ** -2))),
+             ((pack(kc4), scales(2.0 ** -3), pack(vc4), scales(2.0 ** -2)), (f16(kc4, 2.0 ** -3), f16(vc4, 2.0 ** -2)))]
+    for quant, exact in cases:
+        aq = oracle_mod.attn_verify(q, [quant], [L], [2], 0.6)
+        af = oracle_mod.attn_verify(q, [exact], [L], [2], 0.6)
+        assert np.array_equal(aq, af)

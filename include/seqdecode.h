@@ -49,7 +49,7 @@ typedef enum sd_status {
 const char* sd_status_string(int status);
 
 /* ABI revision of this header; bumps on any signature change. */
-#define SD_ABI_VERSION 9
+#define SD_ABI_VERSION 10
 int sd_abi_version(void);
 
 /* Largest batch of token rows a GEMV call takes (speculative-verify width, see
@@ -170,9 +170,21 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
  * offsets divided by 32.  Quantization of a new row (the append and the step)
  * takes, per block, d = amax / 127 in fp32, c = clamp(round-half-away(x / d),
  * -127, 127) (0 when d = 0), and stores fp16(d) rounded to nearest even.
+ * SD_KV_Q4_0, SD_KV_Q4_Q8, SD_KV_Q8_Q4: the Q4 type and the mixed Q4/Q8 and
+ * Q8/Q4 caches of the same "Validation" (K type / V type).  A q4_0 block is 32
+ * four-bit codes with one fp16 scale d, value d * (n - 8) for the stored
+ * nibble n; the nibbles of dims 2j and 2j + 1 of a block share byte j (the
+ * even dim in the low four bits), so a row's codes take half the bytes of its
+ * dims: codes at the element offsets of an fp16 cache divided by 2, scales (as
+ * for q8_0) divided by 32.  Quantization takes d = amax / 7 in fp32 and
+ * c = clamp(round-half-away(x / d), -8, 7) (0 when d = 0), stores n = c + 8
+ * and fp16(d) rounded to nearest even.
  */
 #define SD_KV_F16 0
 #define SD_KV_Q8_0 1
+#define SD_KV_Q4_0 2  /* K and V q4_0 */
+#define SD_KV_Q4_Q8 3 /* K q4_0, V q8_0 */
+#define SD_KV_Q8_Q4 4 /* K q8_0, V q4_0 */
 
 /*
  * One sequence's key and value caches, element (row r, head g, dim d) at
@@ -187,9 +199,10 @@ int sd_rope_posvec(float* x, int n_tok, int n_heads, int head_dim,
  *           1: the cache is a ring, position j in row j % capacity (needs
  *           window >= 1 and room for every position still attended to).
  *   kv_type SD_KV_F16: k and v hold fp16 bits and k_q8 .. v_d are unused;
- *           SD_KV_Q8_0: k and v are unused, codes in k_q8 / v_q8 (16-byte
- *           aligned), scales in k_d / v_d (8-byte aligned); D % 32 == 0 and
- *           ld_tok, ld_head multiples of 32 (of 128 for attention).
+ *           the quantized types: k and v are unused, codes in k_q8 / v_q8
+ *           (16-byte aligned; q4_0 nibbles at half the byte offsets), scales
+ *           in k_d / v_d (8-byte aligned); D % 32 == 0 and ld_tok, ld_head
+ *           multiples of 32 (of 128 for attention).
  *   block_table  NULL, or a paged cache ("feat(qwen36): complete concurrent
  *           serving implementation with speculation", "Summary": a shared
  *           paged KV pool with per-sequence block tables): k and v are a pool
@@ -216,10 +229,11 @@ typedef struct sd_seqview {
   int32_t ring;
   const int32_t* block_table;
   int32_t block_size;
-  int32_t kv_type;      /* SD_KV_F16 (k, v) or SD_KV_Q8_0 (k_q8, v_q8, k_d, v_d) */
-  int8_t* k_q8;         /* q8_0 codes [capacity][H_kv][D] at ld_tok, ld_head (bytes) */
+  int32_t kv_type;      /* SD_KV_F16 (k, v) or a quantized type (k_q8, v_q8, k_d, v_d) */
+  int8_t* k_q8;         /* q8_0 codes [capacity][H_kv][D] at ld_tok, ld_head (bytes), or
+                           q4_0 nibble pairs [capacity][H_kv][D/2] at ld_tok/2, ld_head/2 */
   int8_t* v_q8;
-  uint16_t* k_d;        /* q8_0 fp16 scales: block b of (r, g) at r*(ld_tok/32) + g*(ld_head/32) + b */
+  uint16_t* k_d;        /* fp16 scales: block b of (r, g) at r*(ld_tok/32) + g*(ld_head/32) + b */
   uint16_t* v_d;
 } sd_seqview;
 
@@ -241,11 +255,12 @@ int sd_kv_append_f16(const float* k_new, const float* v_new, int64_t ld_new,
                      sd_stream_t stream);
 
 /*
- * sd_kv_append_q8_0 -- the same append into SD_KV_Q8_0 views: the row of
- * position ctx_len_s - 1 receives the q8_0 blocks of k_new[s] and v_new[s]
- * (codes and fp16 scales, quantized as stated above); no other row is touched.
- * Requires what sd_kv_append_f16 does, with every view SD_KV_Q8_0 and
- * D % 32 == 0; k_new, v_new finite.
+ * sd_kv_append_q8_0 -- the same append into quantized views: the row of
+ * position ctx_len_s - 1 receives the blocks of k_new[s] and v_new[s] in the
+ * view's K and V types (codes and fp16 scales, quantized as stated above); no
+ * other row is touched.  Requires what sd_kv_append_f16 does, with every view
+ * of one quantized kv_type (SD_KV_Q8_0, SD_KV_Q4_0, SD_KV_Q4_Q8 or
+ * SD_KV_Q8_Q4) and D % 32 == 0; k_new, v_new finite.
  */
 int sd_kv_append_q8_0(const float* k_new, const float* v_new, int64_t ld_new,
                       const sd_seqview* views, int n_seq, int H_kv, int D,
@@ -279,8 +294,9 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  * chunks are aligned to absolute positions, so a windowed result is the same
  * in a ring as in a plain cache holding the same rows.  A paged view (see
  * sd_seqview) gives the same bits as a plain cache holding the same keys.
- * SD_KV_Q8_0 views: keys and values are the dequantized d * c (exact in fp32);
- * all views of one call share one kv_type (else SD_EUNSUPPORTED).
+ * Quantized views: keys and values are the dequantized d * c of q8_0 and
+ * d * (n - 8) of q4_0 blocks (exact in fp32); all views of one call share one
+ * kv_type (else SD_EUNSUPPORTED).
  */
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views,
                             int n_seq, int H_q, int H_kv, int D, float scale,
@@ -451,9 +467,10 @@ typedef struct sd_step_seq {
                                   are pools [n_layers][capacity][H_kv][D] in blocks of
                                   block_size rows (64, 128 or 256), as in sd_seqview */
   int32_t block_size;
-  int32_t kv_type;    /* SD_KV_F16 (k_cache, v_cache) or SD_KV_Q8_0: codes
-                         k_q8 / v_q8 [n_layers][capacity][H_kv][D] int8 and scales
-                         k_d / v_d [n_layers][capacity][H_kv][D/32] fp16; all
+  int32_t kv_type;    /* SD_KV_F16 (k_cache, v_cache) or a quantized type: codes
+                         k_q8 / v_q8 [n_layers][capacity][H_kv][D] int8 (q8_0) or
+                         [n_layers][capacity][H_kv][D/2] nibble pairs (q4_0), and
+                         scales k_d / v_d [n_layers][capacity][H_kv][D/32] fp16; all
                          sequences of a step share one kv_type */
   int8_t* k_q8;
   int8_t* v_q8;

@@ -16,8 +16,8 @@ __all__ = [
     "decode_attn_multiseq_noalloc", "ATTN_SCRATCH_BYTES",
     "decode_attn_verify", "ATTN_MAX_NEW",
     "rmsnorm_q8", "swiglu_q8", "qgemv_q8_0_swiglu_q8", "embed_f16", "argmax_rows", "MAX_TOKENS", "MAX_SEQS",
-    "ATTN_CHUNK", "ATTN_SMALL_CHUNK", "ATTN_SMALL_SPAN", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "kv_append_q8_0",
-    "KV_F16", "KV_Q8_0",
+    "ATTN_CHUNK", "ATTN_SMALL_CHUNK", "ATTN_SMALL_SPAN", "GEMV_AUTO", "GEMV_NARROW", "GEMV_MFMA", "seqview_q8", "seqview_quant", "kv_append_q8_0",
+    "KV_F16", "KV_Q8_0", "KV_Q4_0", "KV_Q4_Q8", "KV_Q8_Q4", "kv_type_of",
 ]
 
 MAX_TOKENS = 16
@@ -28,7 +28,16 @@ ATTN_SMALL_SPAN = 2048
 ATTN_MAX_NEW = 4
 ATTN_SCRATCH_BYTES = 16 << 20
 GEMV_AUTO, GEMV_NARROW, GEMV_MFMA = 0, 1, 2
-KV_F16, KV_Q8_0 = 0, 1
+KV_F16, KV_Q8_0, KV_Q4_0, KV_Q4_Q8, KV_Q8_Q4 = 0, 1, 2, 3, 4
+
+
+def kv_type_of(k_type: str, v_type: str) -> int:
+    """The sd_seqview kv_type of quantized K and V types ("q8_0" or "q4_0")."""
+    types = {("q8_0", "q8_0"): KV_Q8_0, ("q4_0", "q4_0"): KV_Q4_0, ("q4_0", "q8_0"): KV_Q4_Q8,
+             ("q8_0", "q4_0"): KV_Q8_Q4}
+    if (k_type, v_type) not in types:
+        raise ValueError(f"unknown K/V types {k_type}/{v_type}")
+    return types[(k_type, v_type)]
 
 
 class SdError(RuntimeError):
@@ -139,10 +148,23 @@ def seqview_q8(kq, kd, vq, vd, ctx_len, window=0, ring=False, block_table=None, 
     """View of one sequence's q8_0 caches: codes kq, vq [capacity][H_kv][D] int8
     and fp16 block scales kd, vd [capacity][H_kv][D/32] (or int16 bits); the
     other arguments as in seqview."""
+    return seqview_quant(kq, kd, vq, vd, ctx_len, "q8_0", "q8_0", window, ring, block_table, block_size)
+
+
+def seqview_quant(kq, kd, vq, vd, ctx_len, k_type="q8_0", v_type="q8_0", window=0, ring=False,
+                  block_table=None, block_size=0):
+    """View of one sequence's quantized caches, K and V each "q8_0" (codes int8
+    [capacity][H_kv][D]) or "q4_0" (nibble pairs uint8 [capacity][H_kv][D/2]),
+    with fp16 block scales kd, vd [capacity][H_kv][D/32] (or int16 bits); the
+    other arguments as in seqview."""
     import torch
-    cap, H_kv, D = kq.shape
-    for t, n, dt in ((kq, "kq", torch.int8), (vq, "vq", torch.int8)):
-        _need(t, dt, n)
+    kv_type = kv_type_of(k_type, v_type)
+    cap, H_kv, nsc = kd.shape
+    D = 32 * nsc
+    for t, n, ty in ((kq, "kq", k_type), (vq, "vq", v_type)):
+        _need(t, torch.int8 if ty == "q8_0" else torch.uint8, n)
+        if tuple(t.shape) != (cap, H_kv, D if ty == "q8_0" else D // 2):
+            raise TypeError(f"{n} has the wrong shape for {ty} codes")
     for t, n in ((kd, "kd"), (vd, "vd")):
         if t.dtype not in (torch.float16, torch.int16):
             raise TypeError(f"{n} must be float16 (or int16 bits)")
@@ -153,7 +175,7 @@ def seqview_q8(kq, kd, vq, vd, ctx_len, window=0, ring=False, block_table=None, 
         _need(block_table, torch.int32, "block_table")
         bt = block_table.data_ptr()
     return SeqView(0, 0, int(ctx_len), int(cap), H_kv * D, D, int(window), 1 if ring else 0, bt,
-                   int(block_size), KV_Q8_0, kq.data_ptr(), vq.data_ptr(), kd.data_ptr(),
+                   int(block_size), kv_type, kq.data_ptr(), vq.data_ptr(), kd.data_ptr(),
                    vd.data_ptr())
 
 

@@ -37,20 +37,27 @@ int check_gemv(const void* w, int64_t N, int64_t K, const int8_t* xq, const floa
   return SD_OK;
 }
 
-// kv_type: the element type every view must have, or -1 (attention: any, but
-// the same for all views of the call).
+// kv_type: the element type every view must have, -1 (attention: any, but
+// the same for all views of the call) or kAnyQuant (any quantized type, the
+// same for all views).
+constexpr int kAnyQuant = -2;
+bool is_kv_type(int t) { return t >= SD_KV_F16 && t <= SD_KV_Q8_Q4; }
+bool k_is_q4(int t) { return t == SD_KV_Q4_0 || t == SD_KV_Q4_Q8; }
+bool v_is_q4(int t) { return t == SD_KV_Q4_0 || t == SD_KV_Q8_Q4; }
+
 int check_views(const sd_seqview* views, int n_seq, int D, bool attn,
                 const int32_t* n_new = nullptr, int kv_type = -1) {
   if (!views || n_seq < 1 || n_seq > SD_MAX_SEQS) return SD_EINVAL;
   for (int s = 0; s < n_seq; ++s) {
     const sd_seqview& v = views[s];
-    if (v.kv_type != SD_KV_F16 && v.kv_type != SD_KV_Q8_0) return SD_EINVAL;
+    if (!is_kv_type(v.kv_type)) return SD_EINVAL;
     if (kv_type >= 0 && v.kv_type != kv_type) return SD_EINVAL;
+    if (kv_type == kAnyQuant && v.kv_type == SD_KV_F16) return SD_EINVAL;
     if (v.kv_type != views[0].kv_type) return SD_EUNSUPPORTED;
     if (v.kv_type == SD_KV_F16) {
       if (!v.k || !v.v) return SD_EINVAL;
     } else {
-      // q8_0: codes and scales, whole 32-dim blocks
+      // q8_0 / q4_0: codes and scales, whole 32-dim blocks
       if (!v.k_q8 || !v.v_q8 || !v.k_d || !v.v_d) return SD_EINVAL;
       if (D % 32 != 0) return SD_EINVAL;
       const int64_t m = attn ? 128 : 32;
@@ -110,8 +117,10 @@ void fill_seqargs(const sd_seqview* views, int n_seq, SeqArgs* a, const int32_t*
     x.n_new = n_new ? n_new[s] : 1;
     x.window = views[s].window;
     x.ring_cap = views[s].ring ? views[s].capacity : 0;
-    if (views[s].kv_type == SD_KV_Q8_0) {
+    if (views[s].kv_type != SD_KV_F16) {
       x.q8 = 1;
+      x.k4 = k_is_q4(views[s].kv_type);
+      x.v4 = v_is_q4(views[s].kv_type);
       x.kq = views[s].k_q8;
       x.vq = views[s].v_q8;
       x.kd = views[s].k_d;
@@ -205,7 +214,7 @@ int sd_kv_append_q8_0(const float* k_new, const float* v_new, int64_t ld_new,
                       const sd_seqview* views, int n_seq, int H_kv, int D, sd_stream_t stream) {
   if (!k_new || !v_new || H_kv < 1 || D < 32 || D > 4096 || D % 32 != 0) return SD_EINVAL;
   if (ld_new < (int64_t)H_kv * D) return SD_EINVAL;
-  int rc = check_views(views, n_seq, D, false, nullptr, SD_KV_Q8_0);
+  int rc = check_views(views, n_seq, D, false, nullptr, kAnyQuant);
   if (rc != SD_OK) return rc;
   if (!aligned(k_new, 4) || !aligned(v_new, 4)) return SD_EALIGN;
   SeqArgs a;

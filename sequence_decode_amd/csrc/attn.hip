@@ -132,6 +132,36 @@ __device__ __forceinline__ h8 codes_to_h8(uint32_t w0, uint32_t w1) {
   return h8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
 }
 
+// q4_0 caches: a 32-bit word of eight nibbles (dims 2j and 2j + 1 in byte j,
+// the even dim low) as its bytes in dim order: {n0, n1, n2, n3}, {n4 .. n7}.
+__device__ __forceinline__ void nibbles_to_bytes(uint32_t w, uint32_t& b0, uint32_t& b1) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  b0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  b1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// Eight q4_0 nibbles n as the exact fp16 values n - 8: bits 0x6400 | n is
+// 1024 + n, minus 1032.
+__device__ __forceinline__ h8 nibbles_to_h8(uint32_t w) {
+  uint32_t b0, b1;
+  nibbles_to_bytes(w, b0, b1);
+  const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 e0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, b0, 0x04010400u)) - bias;
+  const h2 e1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, b0, 0x04030402u)) - bias;
+  const h2 e2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, b1, 0x04010400u)) - bias;
+  const h2 e3 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, b1, 0x04030402u)) - bias;
+  return h8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+}
+
+// Eight nibbles as the int8 codes n - 8 (per byte: n + 0x78 stays below 0x100,
+// and flipping its top bit gives n - 8 in two's complement).
+__device__ __forceinline__ void nibbles_to_codes(uint32_t w, uint32_t& c0, uint32_t& c1) {
+  uint32_t b0, b1;
+  nibbles_to_bytes(w, b0, b1);
+  c0 = (b0 + 0x78787878u) ^ 0x80808080u;
+  c1 = (b1 + 0x78787878u) ^ 0x80808080u;
+}
+
 // One workgroup = (sequence, KV head g, chunk); wave w owns keys 64w .. 64w+63
 // of the chunk (a chunk of at most 64 keys is one wave's).  Both contractions run on v_mfma_f32_16x16x32_f16
 // with the four query heads of the group as the first 4 of 16 columns:
@@ -150,10 +180,14 @@ __device__ __forceinline__ h8 codes_to_h8(uint32_t w0, uint32_t w1) {
 // value scales fold into the weights: the B operand of dim tile dt is the
 // fp32 product p_j * d_j[dt/2] as fp16 hi + lo.  V^T comes from the codes in
 // LDS by ds_read_b64_tr_b8 (each 16-lane group gathers 8 keys x 16 dims).
+// q4_0 keys (K4) enter the same MFMAs through nibbles_to_h8 (lane (col, kg)
+// loads the 4 bytes of dims 8kg .. 8kg+7 of each block); q4_0 values (V4) are
+// loaded into registers and written to the wave's LDS region as the int8 codes
+// n - 8 in the q8_0 layout, so the value contraction is that of q8_0 caches.
 // The four wave partials are added in wave order.  Keys past the end of the
 // sequence get weight 0; their V rows (and scales) are clamped to the last key,
 // so every product that enters a sum is finite.
-template <bool Q8>
+template <bool Q8, bool K4 = false, bool V4 = false>
 __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q, int64_t ld_q,
                                                     SeqArgs seqs, int H_q, float scale,
                                                     float* __restrict__ part) {
@@ -244,7 +278,16 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       return krow((j0 + jlo) % A.ring_cap, min(max(jl, jlo), nk - 1));
     };
     uint8_t* vw = s_v + wave * kVB;
-    if constexpr (Q8) {
+    // q4_0 values: lane l loads the 64 nibble bytes of the wave's key l (to LDS
+    // as codes before the value contraction), issued first
+    u32x4a v4r[4];
+    if constexpr (V4) {
+      const uint8_t* vr = reinterpret_cast<const uint8_t*>(A.vq) + (int64_t)g * (A.ld_head >> 1) +
+                          vrow(wk + lane) * (A.ld_tok >> 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4r[i] = *reinterpret_cast<const u32x4a*>(vr + 16 * i);
+    }
+    if constexpr (Q8 && !V4) {
       // ---- V code rows of this wave -> LDS by DMA, issued first (the scores
       // wait for every load of the wave): instruction i fills rows
       // 8i .. 8i+7; lane l writes row 8i + l/8 at 16-byte position l%8, which
@@ -282,6 +325,28 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
           const uint16_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * A.ld_tok;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) ka[t][kk] = *reinterpret_cast<const u32x4a*>(kr + 32 * kk);
+        }
+      }
+    } else if constexpr (K4) {
+      // q4_0 keys: the 4 bytes of dims 8kg .. 8kg+7 of block kk (in kc[t][kk].x)
+      const uint8_t* kb = reinterpret_cast<const uint8_t*>(A.kq) + (int64_t)g * (A.ld_head >> 1) + 4 * kg;
+      const int64_t kst = A.ld_tok >> 1;
+      if (__builtin_expect(lin, 1)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+          const uint8_t* kr = kb + (jl < nk ? jrow + jl : jlast) * kst;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) kc[t][kk] = u32x2a{*reinterpret_cast<const uint32_t*>(kr + 16 * kk), 0u};
+        }
+      } else {
+        const int prow0 = (j0 + jlo) % A.ring_cap;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int jl = jk + 32 * (t >> 1) + 4 * (t & 1);
+          const uint8_t* kr = kb + (int64_t)krow(prow0, min(max(jl, jlo), nk - 1)) * kst;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) kc[t][kk] = u32x2a{*reinterpret_cast<const uint32_t*>(kr + 16 * kk), 0u};
         }
       }
     } else {
@@ -405,7 +470,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
         f32x4v dk[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const h8 av = codes_to_h8(kc[t][kk].x, kc[t][kk].y);
+          const h8 av = K4 ? nibbles_to_h8(kc[t][kk].x) : codes_to_h8(kc[t][kk].x, kc[t][kk].y);
           dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi[kk], f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
           dk[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo[kk], dk[kk], 0, 0, 0);
         }
@@ -468,6 +533,21 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 
     // ---- weighted values: this wave's V rows have landed in LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (V4) {
+      // lane l's key: its 128 codes n - 8 as eight 16-byte segments, segment q
+      // at 16-byte position q ^ vswz8(l) of row l (the q8_0 DMA layout)
+      const uint32_t nb[16] = {v4r[0].x, v4r[0].y, v4r[0].z, v4r[0].w, v4r[1].x, v4r[1].y, v4r[1].z, v4r[1].w,
+                               v4r[2].x, v4r[2].y, v4r[2].z, v4r[2].w, v4r[3].x, v4r[3].y, v4r[3].z, v4r[3].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t c0, c1, c2, c3;
+        nibbles_to_codes(nb[2 * q], c0, c1);
+        nibbles_to_codes(nb[2 * q + 1], c2, c3);
+        *reinterpret_cast<u32x4a*>(vw + lane * kRowBytes8 + 16 * (q ^ vswz8(lane))) = u32x4a{c0, c1, c2, c3};
+      }
+      // every lane's codes are in LDS before the transposed reads below
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     f32x4v o[8];
     if constexpr (!Q8) {
       // lane (col, kg) reads row 32b + 8kg + 4h + col/4, dims 16dt + 4(col%4) .. +3
@@ -843,7 +923,16 @@ hipError_t launch_attn(const float* q, int64_t ld_q, const SeqArgs& seqs, int H_
                        hipStream_t st) {
   const int units = seqs.units_total;
   (void)H_kv;
-  if (seqs.s[0].q8)
+  if (seqs.s[0].q8 && seqs.s[0].k4 && seqs.s[0].v4)
+    hipLaunchKernelGGL((k_attn_chunk<true, true, true>), dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q,
+                       scale, partials);
+  else if (seqs.s[0].q8 && seqs.s[0].k4)
+    hipLaunchKernelGGL((k_attn_chunk<true, true, false>), dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q,
+                       scale, partials);
+  else if (seqs.s[0].q8 && seqs.s[0].v4)
+    hipLaunchKernelGGL((k_attn_chunk<true, false, true>), dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q,
+                       scale, partials);
+  else if (seqs.s[0].q8)
     hipLaunchKernelGGL(k_attn_chunk<true>, dim3(units), dim3(256), 0, st, q, ld_q, seqs, H_q, scale,
                        partials);
   else

@@ -77,7 +77,9 @@ struct SeqArg {
   const int32_t* btab;    // paged cache: block table (device), else null
   int32_t bshift;         // log2 of the block size (paged)
   int32_t n_blocks;       // blocks in the pool (paged)
-  int32_t q8;             // 1: q8_0 caches (codes kq / vq, fp16 scales kd / vd at offsets / 32)
+  int32_t q8;             // 1: quantized caches (codes kq / vq, fp16 scales kd / vd at offsets / 32)
+  int32_t k4;             // with q8: 1 when K is q4_0 (nibble pairs at offsets / 2), 0 for q8_0
+  int32_t v4;             // the same for V
   int8_t* kq;
   int8_t* vq;
   uint16_t* kd;

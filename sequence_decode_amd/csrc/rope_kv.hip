@@ -66,6 +66,33 @@ __device__ __forceinline__ void put_q8_0(float x, int d, int8_t* codes, uint16_t
   if ((d & 31) == 0) scales[d >> 5] = f32_to_f16_bits(dd);
 }
 
+// One element of a q4_0 block: lane d of an aligned group of 32 holds x; the
+// block's scale d = amax / 7 and the code c = clamp(round-half-away(x / d),
+// -8, 7) (0 when d = 0) are those of the library's q4_0 convention; the even
+// lane of each pair stores the byte of nibbles c + 8 (its own in the low four
+// bits), the block's first lane stores fp16(d) (nearest even).
+__device__ __forceinline__ void put_q4_0(float x, int d, uint8_t* packed, uint16_t* scales) {
+  const float amax = group_max<32>(fabsf(x));
+  const float dd = fdiv(amax, 7.0f);
+  int c = 0;
+  if (dd != 0.0f) c = (int)fminf(fmaxf(roundf(fdiv(x, dd)), -8.0f), 7.0f);
+  const int n = c + 8;
+  const int odd = __shfl_xor(n, 1);  // the partner dim's nibble (lane d ^ 1)
+  if ((d & 1) == 0) packed[d >> 1] = (uint8_t)(n | (odd << 4));
+  if ((d & 31) == 0) scales[d >> 5] = f32_to_f16_bits(dd);
+}
+
+// The quantized row of (row r, head g) of a cache, K or V: q4_0 nibble pairs
+// at half the element offset, else q8_0 codes at the element offset.
+__device__ __forceinline__ void put_quant(float x, int d, bool q4, int8_t* codes, int64_t r, int g,
+                                          const SeqArg& a, uint16_t* scales) {
+  if (q4)
+    put_q4_0(x, d, reinterpret_cast<uint8_t*>(codes) + r * (a.ld_tok >> 1) + (int64_t)g * (a.ld_head >> 1),
+             scales);
+  else
+    put_q8_0(x, d, codes + r * a.ld_tok + (int64_t)g * a.ld_head, scales);
+}
+
 // Grid (n_seq, H_kv), 128 threads; D % 32 == 0, so every block of 32 dims is
 // one aligned group of 32 lanes.
 __global__ __launch_bounds__(128) void k_kv_append_q8(const float* __restrict__ k_new,
@@ -75,12 +102,11 @@ __global__ __launch_bounds__(128) void k_kv_append_q8(const float* __restrict__ 
   const int g = blockIdx.y;
   const SeqArg& a = seqs.s[s];
   const int64_t r = seq_row(a, a.ctx_len - 1);
-  const int64_t row = r * a.ld_tok + (int64_t)g * a.ld_head;
   const int64_t srow = r * (a.ld_tok >> 5) + (int64_t)g * (a.ld_head >> 5);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     const int64_t src = (int64_t)s * ld_new + (int64_t)g * D + d;
-    put_q8_0(k_new[src], d, a.kq + row, a.kd + srow);
-    put_q8_0(v_new[src], d, a.vq + row, a.vd + srow);
+    put_quant(k_new[src], d, a.k4, a.kq, r, g, a, a.kd + srow);
+    put_quant(v_new[src], d, a.v4, a.vq, r, g, a, a.vd + srow);
   }
 }
 
@@ -151,8 +177,8 @@ __global__ __launch_bounds__(64) void k_rope_kv_step(float* qkv, int64_t ld_qkv,
       __syncthreads();
       const int64_t sdst = crow * (a.ld_tok >> 5) + (int64_t)g * (a.ld_head >> 5);
       for (int d = threadIdx.x; d < head_dim; d += blockDim.x) {
-        put_q8_0(s_k[d], d, a.kq + dst, a.kd + sdst);
-        put_q8_0(vh[d], d, a.vq + dst, a.vd + sdst);
+        put_quant(s_k[d], d, a.k4, a.kq, crow, g, a, a.kd + sdst);
+        put_quant(vh[d], d, a.v4, a.vq, crow, g, a, a.vd + sdst);
       }
       return;
     }

@@ -87,7 +87,7 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     const int T = q.n_new == 0 ? 1 : q.n_new;
     if (T < 1 || T > SD_ATTN_MAX_NEW) return SD_EINVAL;
     if (q.capacity < 1 || q.pos < 0 || (q.ring != 0 && q.ring != 1)) return SD_EINVAL;
-    if (q.kv_type != SD_KV_F16 && q.kv_type != SD_KV_Q8_0) return SD_EINVAL;
+    if (q.kv_type < SD_KV_F16 || q.kv_type > SD_KV_Q8_Q4) return SD_EINVAL;
     if (q.kv_type != io->seqs[0].kv_type) return SD_EUNSUPPORTED;
     if (q.kv_type == SD_KV_F16) {
       if (!q.k_cache || !q.v_cache) return SD_EINVAL;
@@ -165,7 +165,10 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
     sa.s[s].n_new = T;
     sa.s[s].window = m->window;
     sa.s[s].ring_cap = io->seqs[s].ring ? io->seqs[s].capacity : 0;
-    sa.s[s].q8 = io->seqs[s].kv_type == SD_KV_Q8_0;
+    const int kt = io->seqs[s].kv_type;
+    sa.s[s].q8 = kt != SD_KV_F16;
+    sa.s[s].k4 = kt == SD_KV_Q4_0 || kt == SD_KV_Q4_Q8;
+    sa.s[s].v4 = kt == SD_KV_Q4_0 || kt == SD_KV_Q8_Q4;
     if (io->seqs[s].block_table) {
       sa.s[s].btab = io->seqs[s].block_table;
       sa.s[s].bshift = __builtin_ctz((unsigned)io->seqs[s].block_size);
@@ -199,8 +202,8 @@ int sd_decode_step(const sd_model* m, const sd_step_io* io, sd_stream_t stream) 
       const sd_step_seq& q = io->seqs[s];
       const int64_t off = (int64_t)l * q.capacity * layer_elems_per_tok;
       if (sa.s[s].q8) {
-        sa.s[s].kq = q.k_q8 + off;
-        sa.s[s].vq = q.v_q8 + off;
+        sa.s[s].kq = q.k_q8 + (sa.s[s].k4 ? off / 2 : off);
+        sa.s[s].vq = q.v_q8 + (sa.s[s].v4 ? off / 2 : off);
         sa.s[s].kd = q.k_d + off / 32;
         sa.s[s].vd = q.v_d + off / 32;
       } else {

@@ -10,7 +10,7 @@ import ctypes
 import numpy as np
 
 from . import _lib, synth
-from . import _check, _stream
+from . import _check, _stream, kv_type_of
 
 
 class DecodeModel:
@@ -104,12 +104,17 @@ class SeqCache:
 
 
 class SeqCacheQ8:
-    """One sequence's q8_0 caches: codes kq, vq int8 [n_layers][capacity][H_kv][D]
-    and fp16 block scales kd, vd [n_layers][capacity][H_kv][D/32]."""
+    """One sequence's quantized caches: K and V codes each q8_0 (int8
+    [n_layers][capacity][H_kv][D]) or q4_0 (nibble pairs, uint8
+    [n_layers][capacity][H_kv][D/2]), the type told by the dtype, and fp16
+    block scales kd, vd [n_layers][capacity][H_kv][D/32]."""
 
     def __init__(self, kq, kd, vq, vd):
+        import torch
         self.kq, self.kd, self.vq, self.vd = kq, kd, vq, vd
         self.capacity = kq.shape[1]
+        self.k_type = "q4_0" if kq.dtype == torch.uint8 else "q8_0"
+        self.v_type = "q4_0" if vq.dtype == torch.uint8 else "q8_0"
 
     @classmethod
     def from_host(cls, kq, kd_bits, vq, vd_bits, device="cuda"):
@@ -173,7 +178,8 @@ class StepRunner:
             bt = 0 if self.block_tables is None else self.block_tables[s].data_ptr()
             if isinstance(c, SeqCacheQ8):
                 self._seqs[s] = _lib.StepSeq(0, 0, c.capacity, 0, self.n_new[s], 1 if ring else 0, bt,
-                                             int(block_size) if bt else 0, 1, c.kq.data_ptr(),
+                                             int(block_size) if bt else 0,
+                                             kv_type_of(c.k_type, c.v_type), c.kq.data_ptr(),
                                              c.vq.data_ptr(), c.kd.data_ptr(), c.vd.data_ptr())
             else:
                 self._seqs[s] = _lib.StepSeq(c.k.data_ptr(), c.v.data_ptr(), c.capacity, 0,

@@ -66,6 +66,16 @@ def kv_cache_q8(g: np.random.Generator, capacity: int, H_kv: int, D: int):
     return codes, d.astype(np.float16).view(np.uint16)
 
 
+def kv_cache_q4(g: np.random.Generator, capacity: int, H_kv: int, D: int):
+    """(nibble pairs uint8 [capacity][H_kv][D/2], fp16 scale bits
+    [capacity][H_kv][D/32]): nibbles uniform on 1..15 (codes -7..7), scales
+    those of N(0,1) blocks under amax / 7."""
+    packed = g.integers(1, 16, size=(capacity, H_kv, D // 2), dtype=np.uint8)
+    packed |= g.integers(1, 16, size=(capacity, H_kv, D // 2), dtype=np.uint8) << 4
+    d = g.uniform(2.0 / 7.0, 3.0 / 7.0, size=(capacity, H_kv, D // BLOCK))
+    return packed, d.astype(np.float16).view(np.uint16)
+
+
 def queries(g: np.random.Generator, n_seq: int, H_q: int, D: int) -> np.ndarray:
     return g.standard_normal(size=(n_seq, H_q, D), dtype=np.float32)
 

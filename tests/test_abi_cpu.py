@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sd_abi_version() == 9
+    assert L.sd_abi_version() == 10
     for code in (0, -1, -2, -3, -4, -5):
         assert L.sd_status_string(code).startswith(b"SD_")
     assert L.sd_status_string(7) == b"unknown sd_status"
@@ -217,7 +217,8 @@ def test_q8_0_view_rejections(L):
     assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
     for bad, rc in ((view(kq=ctypes.c_void_p(0)), SD_EINVAL),     # missing codes
                     (view(kd=ctypes.c_void_p(0)), SD_EINVAL),     # missing scales
-                    (view(kv_type=2), SD_EINVAL),                 # unknown type
+                    (view(kv_type=5), SD_EINVAL),                 # unknown type
+                    (view(kv_type=-1), SD_EINVAL),
                     (view(kq=ODD), SD_EALIGN),
                     (view(kd=ctypes.c_void_p(0x10004)), SD_EALIGN),  # scales need 8 bytes
                     (view(ld_tok=1056), SD_EALIGN)):              # strides: multiples of 128
@@ -232,6 +233,36 @@ def test_q8_0_view_rejections(L):
     assert kv8(FAKE, FAKE, 1024, plain, 1, 8, 128, None) == SD_EINVAL
     assert kv8(FAKE, FAKE, 1024, ok, 1, 8, 100, None) == SD_EINVAL        # D % 32
     assert kv8(FAKE, FAKE, 1024, one(view(ld_tok=1040)), 1, 8, 128, None) == SD_EALIGN
+
+
+def test_q4_and_mixed_view_rejections_and_workspace(L):
+    """q4_0 and the mixed Q4/Q8, Q8/Q4 views take the q8_0 view's checks; their
+    workspace is that of any view of the same contexts; one kv_type per call."""
+    a = L.sd_decode_attn_multiseq
+    def view(kv_type, ctx=100, kq=FAKE, kd=FAKE, ld_tok=1024):
+        return _lib.SeqView(0, 0, ctx, 128, ld_tok, 128, 0, 0, None, 0, kv_type,
+                            kq.value, FAKE.value, kd.value, FAKE.value)
+    one = lambda v: (_lib.SeqView * 1)(v)
+    for t in (2, 3, 4):
+        ok = one(view(t))
+        need = L.sd_decode_attn_workspace_bytes(ok, 1, 32, 128)
+        assert need == 2 * 32 * 132 * 4
+        assert a(FAKE, 4096, ok, 1, 32, 8, 128, 0.088, FAKE, FAKE, need - 4, None) == SD_EWORKSPACE
+        for bad, rc in ((view(t, kq=ctypes.c_void_p(0)), SD_EINVAL),
+                        (view(t, kd=ctypes.c_void_p(0)), SD_EINVAL),
+                        (view(t, kq=ODD), SD_EALIGN),
+                        (view(t, ld_tok=1056), SD_EALIGN)):
+            assert a(FAKE, 4096, one(bad), 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == rc
+        for u in (1, 2, 3, 4):
+            if u != t:
+                pair = (_lib.SeqView * 2)(view(t), view(u))
+                assert a(FAKE, 4096, pair, 2, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 30, None) == SD_EUNSUPPORTED
+        # the quantized append takes every quantized type, one per call
+        kv8 = L.sd_kv_append_q8_0
+        assert kv8(FAKE, FAKE, 1024, ok, 1, 8, 100, None) == SD_EINVAL      # D % 32
+        assert L.sd_kv_append_f16(FAKE, FAKE, 1024, ok, 1, 8, 128, None) == SD_EINVAL
+        pair = (_lib.SeqView * 2)(view(t), view(1))
+        assert kv8(FAKE, FAKE, 1024, pair, 2, 8, 128, None) == SD_EUNSUPPORTED
 
 
 def test_rope_kv_and_glue_rejections(L):
@@ -294,6 +325,10 @@ def test_step_rejections(L):
     assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EWORKSPACE
     q8[1].kv_type = 0                 # one kv_type per step
     assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EUNSUPPORTED
+    q8[1].kv_type = 3                 # Q4/Q8 beside Q8/Q8
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EUNSUPPORTED
+    q8[1].kv_type = 5                 # unknown type
+    assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EINVAL
     q8[1].kv_type = 1
     q8[1].k_d = 0x10004               # scales need 8-byte alignment
     assert L.sd_decode_step(ctypes.byref(m), ctypes.byref(io8), None) == SD_EALIGN

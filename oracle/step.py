@@ -39,12 +39,21 @@ class Model:
         #                                       attn_norm, ffn_norm)
 
 
+def _quant_like(codes, x):
+    """The new rows x in the cache type of `codes`: q4_0 nibble pairs (uint8),
+    else q8_0 codes (int8)."""
+    if codes.dtype == np.uint8:
+        return O.quantize_kv_q4_0(x)
+    return O.quantize_kv_q8_0(x)
+
+
 def decode_step(m: Model, caches, tokens, pos):
     """One step for n = len(tokens) sequences.
 
     caches[s] = (k_bits, v_bits), each uint16 [n_layers][capacity][H_kv][D],
-    or q8_0 caches (kq, kd_bits, vq, vd_bits) with codes int8 [..][D] and scale
-    bits uint16 [..][D/32]; updated in place at row pos[s] of every layer.  Returns (logits [n][vocab]
+    or quantized caches (kq, kd_bits, vq, vd_bits) with codes int8 [..][D]
+    (q8_0) or nibble pairs uint8 [..][D/2] (q4_0), K and V each either, and
+    scale bits uint16 [..][D/32]; updated in place at row pos[s] of every layer.  Returns (logits [n][vocab]
     fp32, next tokens int32 [n]).
     """
     tokens = np.asarray(tokens, np.int64)
@@ -63,9 +72,9 @@ def decode_step(m: Model, caches, tokens, pos):
         q = O.rope_posvec(q, pos, m.theta, m.n_rot)
         k = O.rope_posvec(k, pos, m.theta, m.n_rot)
         for s in range(n):
-            if len(caches[s]) == 4:  # q8_0 cache: codes and fp16 scales of the new rows
-                kq, kd = O.quantize_kv_q8_0(k[s])
-                vq, vd = O.quantize_kv_q8_0(v[s])
+            if len(caches[s]) == 4:  # quantized cache: codes and fp16 scales of the new rows
+                kq, kd = _quant_like(caches[s][0], k[s])
+                vq, vd = _quant_like(caches[s][2], v[s])
                 caches[s][0][li, pos[s]], caches[s][1][li, pos[s]] = kq, kd
                 caches[s][2][li, pos[s]], caches[s][3][li, pos[s]] = vq, vd
             else:

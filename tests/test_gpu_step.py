@@ -291,30 +291,35 @@ def test_paged_pool_step_equals_plain(sd, model):
         assert np.array_equal(pkh[:, rows[s]], kh) and np.array_equal(pvh[:, rows[s]], vh), s
 
 
-def _q8_caches_host(n, seed):
-    """q8_0 caches [n_layers][CAP][H_kv][D] codes and [..][D/32] fp16 scale bits."""
+def _q8_caches_host(n, seed, kt="q8_0", vt="q8_0"):
+    """Quantized caches [n_layers][CAP][H_kv][D] codes (q8_0) or [..][D/2] nibble
+    pairs (q4_0), K and V each, and [..][D/32] fp16 scale bits."""
     g = synth.rng(seed)
     L_, Hkv, Dh = DIMS["n_layers"], DIMS["n_kv_heads"], DIMS["head_dim"]
+    half = lambda ty: synth.kv_cache_q4 if ty == "q4_0" else synth.kv_cache_q8
     out = []
     for _ in range(n):
-        kq, kd = synth.kv_cache_q8(g, L_ * CAP, Hkv, Dh)
-        vq, vd = synth.kv_cache_q8(g, L_ * CAP, Hkv, Dh)
+        kq, kd = half(kt)(g, L_ * CAP, Hkv, Dh)
+        vq, vd = half(vt)(g, L_ * CAP, Hkv, Dh)
         out.append(tuple(a.reshape((L_, CAP) + a.shape[1:]) for a in (kq, kd, vq, vd)))
     return out
 
 
-def test_q8_kv_step_oracle_invariance_and_verify(sd, model, model_host):
-    """Steps over q8_0 caches: agreement with the oracle's step over the same
-    caches; each sequence alone gives the batched bits (logits and cache rows);
-    a verify step equals the sequential one-token steps."""
+@pytest.mark.parametrize("kt,vt", [("q8_0", "q8_0"), ("q4_0", "q8_0"), ("q8_0", "q4_0")])
+def test_q8_kv_step_oracle_invariance_and_verify(sd, model, model_host, kt, vt):
+    """Steps over quantized caches (q8_0, and the mixed Q4/Q8 and Q8/Q4 types of
+    "feat(qwen36): complete concurrent serving implementation with speculation",
+    "Validation"): agreement with the oracle's step over the same caches; each
+    sequence alone gives the batched bits (logits and cache rows); a verify step
+    equals the sequential one-token steps."""
     import torch
     from sequence_decode_amd.step import SeqCacheQ8
-    say("q8 KV step")
+    say(f"{kt}/{vt} KV step")
     h = model_host
     m = ostep.Model(h["hidden"], h["n_heads"], h["n_kv_heads"], h["head_dim"], h["ffn"],
                     h["vocab"], h["eps"], h["theta"], h["tok_embd_bits"], h["out_norm"],
                     h["w_lm"], h["layers"])
-    ch = _q8_caches_host(4, 3600)
+    ch = _q8_caches_host(4, 3600, kt, vt)
     toks, pos = [4, 77, 600, 999], [0, 63, 256, 319]
 
     def run(caches_h, tokens, positions, n_new=None):
@@ -329,7 +334,7 @@ def test_q8_kv_step_oracle_invariance_and_verify(sd, model, model_host):
     ocache = [tuple(a.copy() for a in c) for c in ch]
     olg, ont = ostep.decode_step(m, ocache, toks, pos)
     rel = np.linalg.norm(lg - olg) / np.linalg.norm(olg)
-    say(f"  q8 logits normwise relative error vs oracle: {rel:.3e}")
+    say(f"  {kt}/{vt} logits normwise relative error vs oracle: {rel:.3e}")
     assert rel <= 1e-3
     for s in range(4):
         l1, n1, c1 = run([ch[s]], [toks[s]], [pos[s]])

@@ -334,6 +334,24 @@ def decode_bench(torch, steps, warmup):
         res[f"q8kv_ragged_n{n}"] = {"tok_s": round(n / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
         log(f"decode q8_0 KV ragged n_seq={n}: {n / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
     del r, q8c
+    # mixed Q4/Q8 KV caches (K q4_0, V q8_0) for the four ragged contexts
+    q48 = [SeqCacheQ8.random_device(g, 32, ctx + span, 8, 128, k_type="q4_0") for ctx in ragged]
+    r = StepRunner(model, q48, max_ctx=max(ragged) + span)
+    r.tokens.copy_(torch.arange(4, dtype=torch.int32) + 7)
+    r.set_positions([c - 1 for c in ragged])
+    for _ in range(warmup):
+        r.step()
+        r.advance()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.step()
+        r.advance()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    res["q4q8kv_ragged_n4"] = {"tok_s": round(4 / dt, 2), "ms_per_step": round(dt * 1e3, 3)}
+    log(f"decode Q4/Q8 KV ragged n_seq=4: {4 / dt:.1f} tok/s ({dt * 1e3:.3f} ms/step)")
+    del r, q48
     # serial baseline: the four ragged sequences one at a time (one-token steps back to back)
     runners = [StepRunner(model, [caches[s]], max_ctx=ragged[s] + span) for s in range(4)]
     for s in range(4):
@@ -365,18 +383,32 @@ def launch_floor_us(torch, n=64):
     return time_graph(torch, run, 20, 2) * 1e6 / n
 
 
+# cache kinds of the attention pass: fp16, q8_0, the mixed Q4/Q8 and Q8/Q4
+# types (K type first), fp16 in a paged pool
+ATTN_KINDS = ("f16", "q8_0", "q4_q8", "q8_q4", "f16_paged64")
+
+
+def attn_key_bytes(kind):
+    """Cache bytes per position (8 KV heads of 128 dims, K and V): fp16 2 B per
+    value; a q8_0 half 128 + 8 B per head, a q4_0 half 64 + 8 B."""
+    half = {"q8": 8 * (128 + 8), "q4": 8 * (64 + 8)}
+    if kind in ("q4_q8", "q8_q4"):
+        return half[kind[:2]] + half[kind[3:]]
+    return 2 * half["q8"] if kind == "q8_0" else 4096
+
+
 def attn_sets(lens, kind):
     """Cache sets the attention pass cycles through: at least 4, and enough that
     together they exceed 512 MB (at most 64)."""
-    per_key = 2176 if kind == "q8_0" else 4096
+    per_key = attn_key_bytes(kind)
     set_bytes = sum(lens) * per_key
     return min(64, max(4, -(-512 * 2**20 // set_bytes)))
 
 
 def attention_bench(torch, reps=20):
     """Graph-timed sd_decode_attn_multiseq (chunk + combine kernels) at the decode
-    contexts: fp16 and q8_0 caches, plain and in a paged pool (64-row blocks).
-    GB/s counts the cache bytes the call must read."""
+    contexts: fp16, q8_0 and mixed Q4/Q8, Q8/Q4 caches, and fp16 in a paged pool
+    (64-row blocks).  GB/s counts the cache bytes the call must read."""
     import sequence_decode_amd as sd
     g = torch.Generator(device="cuda")
     g.manual_seed(21)
@@ -385,15 +417,35 @@ def attention_bench(torch, reps=20):
              "n1_32768": [32768]}
     out = {}
     for cname, lens in cases.items():
-        for kind in ("f16", "q8_0", "f16_paged64"):
+        for kind in ATTN_KINDS:
             keep, sets = [], []
             # cache sets, cycled, enough of them to exceed twice the 256 MB
             # Infinity Cache: like a decode step (which reads the rest of the
             # model between two reads of a layer's cache), no call finds its
             # cache in any cache level
             n_sets = attn_sets(lens, kind)
+            def half(ty, L):
+                """Codes and fp16 scales of one quantized half ("q8" or "q4")."""
+                if ty == "q8":
+                    c = torch.randint(-127, 128, (L, H_kv, D), generator=g, device="cuda",
+                                      dtype=torch.int32).to(torch.int8)
+                    d = ((torch.rand((L, H_kv, D // 32), generator=g, device="cuda") + 2) / 127).half()
+                else:
+                    lo = torch.randint(1, 16, (L, H_kv, D // 2), generator=g, device="cuda", dtype=torch.int32)
+                    hi = torch.randint(1, 16, (L, H_kv, D // 2), generator=g, device="cuda", dtype=torch.int32)
+                    c = (lo | (hi << 4)).to(torch.uint8)
+                    d = ((torch.rand((L, H_kv, D // 32), generator=g, device="cuda") + 2) / 7).half()
+                return c, d
             for _ in range(n_sets):
-                if kind == "q8_0":
+                if kind in ("q4_q8", "q8_q4"):
+                    cs = []
+                    for L in lens:
+                        kq, kd = half(kind[:2], L)
+                        vq, vd = half(kind[3:], L)
+                        cs.append((kq, kd, vq, vd))
+                    types = {"q8": "q8_0", "q4": "q4_0"}
+                    views = [sd.seqview_quant(*c, L, types[kind[:2]], types[kind[3:]]) for c, L in zip(cs, lens)]
+                elif kind == "q8_0":
                     cs = []
                     for L in lens:
                         kq = torch.randint(-127, 128, (L, H_kv, D), generator=g, device="cuda",
@@ -428,8 +480,7 @@ def attention_bench(torch, reps=20):
                 for v in sets:
                     sd.decode_attn_multiseq(q, v, H_kv, 0.08838835, out=o, ws=ws)
             us = time_graph(torch, cycle, reps, 2) * 1e6 / n_sets
-            per_key = 2176 if kind == "q8_0" else 4096
-            gbs = sum(lens) * per_key / us / 1e3
+            gbs = sum(lens) * attn_key_bytes(kind) / us / 1e3
             out[f"{cname}_{kind}"] = {"us": round(us, 2), "GB_s": round(gbs, 1),
                                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                       "cache_sets": n_sets}
@@ -853,7 +904,7 @@ def attn_trace_summary(trace_db, fetch_db=None, write_db=None, reps=20):
         comb = [v for n, v in rows if _short_kernel(n).startswith("k_attn_combine")]
         out, i = {}, 0
         for cname, lens in ATTN_CASES.items():
-            for kind in ("f16", "q8_0", "f16_paged64"):
+            for kind in ATTN_KINDS:
                 sets = attn_sets(lens, kind)
                 n = (3 + reps) * sets
                 out[f"{cname}_{kind}"] = (chunk[i + 3 * sets:i + n], comb[i + 3 * sets:i + n])
@@ -877,7 +928,7 @@ def attn_trace_summary(trace_db, fetch_db=None, write_db=None, reps=20):
     for key, (ch, cb) in cases.items():
         cname, kind = key.split("_", 2)[0] + "_" + key.split("_", 2)[1], key.split("_", 2)[2]
         lens = ATTN_CASES[cname]
-        cache = sum(lens) * (2176 if kind == "q8_0" else 4096)
+        cache = sum(lens) * attn_key_bytes(kind)
         row = f"| {key} | {statistics.mean(ch):.2f} | {statistics.mean(cb):.2f} | {cache:,} |"
         if have_pmc:
             fb = statistics.mean(fc[key][0]) * 1024 * ff

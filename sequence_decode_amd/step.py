@@ -124,16 +124,22 @@ class SeqCacheQ8:
         return cls(t(kq), f(kd_bits), t(vq), f(vd_bits))
 
     @classmethod
-    def random_device(cls, gen, n_layers, capacity, H_kv, D, device="cuda"):
-        """Codes uniform in [-127, 127], scales those of N(0,1) blocks (about 2.5/127)."""
+    def random_device(cls, gen, n_layers, capacity, H_kv, D, device="cuda", k_type="q8_0",
+                      v_type="q8_0"):
+        """q8_0 halves: codes uniform in [-127, 127], scales those of N(0,1) blocks
+        (about 2.5/127); q4_0 halves: nibbles uniform in 1..15, scales about 2.5/7."""
         import torch
-        def codes():
+        def codes(ty):
+            if ty == "q4_0":
+                n = lambda: torch.randint(1, 16, (n_layers, capacity, H_kv, D // 2), generator=gen,
+                                          device=device, dtype=torch.int32)
+                return (n() | (n() << 4)).to(torch.uint8)
             return torch.randint(-127, 128, (n_layers, capacity, H_kv, D), generator=gen,
                                  device=device, dtype=torch.int32).to(torch.int8)
-        def scales():
+        def scales(ty):
             u = torch.rand((n_layers, capacity, H_kv, D // 32), generator=gen, device=device)
-            return ((u + 2.0) / 127.0).to(torch.float16)
-        return cls(codes(), scales(), codes(), scales())
+            return ((u + 2.0) / (7.0 if ty == "q4_0" else 127.0)).to(torch.float16)
+        return cls(codes(k_type), scales(k_type), codes(v_type), scales(v_type))
 
 
 class StepRunner:

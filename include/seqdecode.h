@@ -127,7 +127,7 @@ int sd_qgemv_q8_0_batch(const void* w, int64_t N, int64_t K,
  *   path  SD_GEMV_AUTO   the kernel sd_qgemv_q8_0_batch uses (the narrow
  *                        kernel up to 8 tokens and K <= 16384, else MFMA);
  *         SD_GEMV_NARROW v_dot4 kernels (one lane per block pair);
- *         SD_GEMV_MFMA   matrix-core kernel (v_mfma_i32_16x16x64_i8 on tiles
+ *         SD_GEMV_MFMA   matrix-core kernel (v_mfma_i32_16x16x32_i8 on tiles
  *                        of 16 rows x 16 tokens).
  * All paths compute the same cells in the same fixed order, so y is bitwise
  * identical whichever path runs, for any n_tok.  Other arguments, layouts and

@@ -702,270 +702,294 @@ __global__ __launch_bounds__(kGemvThreads) void k_qgemv_q8_0_lds(
 }
 
 // ---------------------------------------------------------------------------
-// Any batch width on the matrix cores (v_mfma_i32_16x16x64_i8), with the
-// same cells, tree and chunk order as the two kernels above, hence the same
-// bits.
+// Any batch width up to 16 on the matrix cores, with the same cells, tree and
+// chunk order as the two kernels above, hence the same bits.
 //
-// A workgroup (8 waves) owns tiles of 16 rows.  For K chunk c it stages the
-// activations of pairs 64c .. 64c+63 for all tokens in LDS in the padded pair
-// layout: dwords 1..16 of each (pair, token) as one 64-byte entry; dword 0
-// and the two block scales go to a per-pair table of 16-token vectors.  Wave
-// w takes pairs 64c + 8w + j, j = 0..7, of the tile.  Lane (col, kq) loads
-// pair bytes 4 + 16kq .. 19 + 16kq of row col (global_load_dwordx4) and pair
-// dword 0; the 16-byte pieces of lanes kq = 0, 1 lie in block A (weights 2..31
-// and the scale of B, which meets activation zeros), those of kq = 2, 3 in
-// block B.  Against token col's activation piece at the same bytes, one MFMA
-// sums block A (lanes kq >= 2 feed zeros, read from a zero region of LDS) and
-// one sums block B (lanes kq <= 1 feed zeros); weights 0, 1 of block A (pair
-// dword 0, whose scale bytes meet zeros) join the first sum through v_dot4.
-// The accumulator of lane (col, kq) holds tokens 4kq .. 4kq+3 of row col; the
-// lane forms those four cells (0 + s_A) + s_B exactly as the narrow kernels
-// do and runs the 8-leaf tree of its pairs in registers.  The eight wave
-// subtrees meet in LDS as ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)), the last
-// three levels of the 64-leaf tree, and the chunk sums are added in chunk
-// order.  A wave loads the next tile's weights while it works on the current
-// one (two register sets), and the per-tile sums alternate between two LDS
-// tables, so a tile costs one barrier.
+// Work: tiles of 16 rows.  A workgroup of 8 waves takes tiles blockIdx.x +
+// k * gridDim.x and, for each, the K chunks in order (unit = (tile, chunk)).
+// Wave w owns pairs 8w .. 8w+7 of every chunk, as two items of 4 pairs; an
+// item's weights (16 rows x 4 pairs, 272 contiguous bytes per row) stream into
+// the wave's two-slot LDS ring by DMA as whole 16-byte pieces of each row;
+// item m + 2 goes out as soon as item m has been read.
+//
+// Integer sums: one v_mfma_i32_16x16x32_i8 per q8_0 block, A = the 16 tokens'
+// activation codes, B = the 16 rows' weight codes, so lane (col, kq) ends with
+// the exact block sums of row col for tokens 4kq .. 4kq+3.  The 32 codes of a
+// block may be dealt to the four k-groups in any way the two operands share:
+// k-group kq takes codes 4kq .. 4kq+3 and 16+4kq .. 19+4kq.  Of block B those
+// are weight dwords 9+kq and 13+kq of the pair; block A's codes sit 2 bytes
+// into the pair (behind its scale), so they are dwords kq, kq+1 and kq+4, kq+5
+// shifted by 16 bits (dword 0 brings codes 0, 1 in its high half, dword 8
+// codes 30, 31 in its low half).  Rows sit 272 bytes (68 dwords) apart, so
+// each of these reads puts the 64 lanes on 64 distinct banks.
+//
+// Activations: per chunk each wave loads the codes and block scales of its own
+// 8 pairs (contiguous runs of each token's row) and stores them to its own part
+// of LDS (a token's 16-byte pieces rotated by the token, so that the reads
+// below hit distinct banks); each lane then keeps its token's codes and the
+// scales of tokens 4kq .. 4kq+3 in registers for the chunk.  No other wave
+// touches that part, so no barrier is needed.  (By DMA instead, or with the
+// loads overlapping the first weight DMAs, the launches measured slower.)
+//
+// Each lane forms its four cells (0 + (dA xA) iA) + (dB xB) iB exactly as the
+// streaming kernels do and runs the 8-leaf tree of its pairs in registers;
+// the eight wave subtrees meet in LDS as ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)),
+// the top three levels of the 64-leaf tree, and the chunk sums are added in
+// chunk order.  The residual rows also come by DMA, and the wave tracks how
+// many DMAs it has issued, so each wait names exactly the DMAs that may stay
+// in flight (loads and stores issued meanwhile only make a wait longer).
 typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kMfmaThreads = 512;
 constexpr int kMfmaWaves = 8;
-constexpr int kMfmaPairs = 8;   // pairs per wave per chunk
-constexpr int kMfmaGroup = 8;   // tiles whose running totals a thread keeps across chunks
-// LDS (bytes): activations [64 pairs][16 tokens][16 dwords]; per-pair vectors
-// [64][3][16] (scale A, scale B, dword 0); zeros covering one wave's read span;
-// two tables [8 waves][16 rows][16 tokens]
-constexpr int kMfmaActBytes = 64 * 16 * 64;
-constexpr int kMfmaScBytes = 64 * 3 * 16 * 4;
-constexpr int kMfmaZeroBytes = kMfmaPairs * 1024 + 1024;
-constexpr int kMfmaTabBytes = 2 * kMfmaWaves * 256 * 4;
-
-struct MfmaW {  // one wave's weights of one tile: 16 bytes at 4 + 16kq and dword 0 of 8 pairs
-  u32x4a q[kMfmaPairs];
-  uint32_t d0[kMfmaPairs];
-};
+constexpr int kMfmaRowBytes = 4 * kPairBytes;                      // one row of an item
+constexpr int kMfmaItemBytes = 16 * kMfmaRowBytes;                 // 4352
+constexpr int kMfmaItemPieces = kMfmaItemBytes / 16;               // 272
+constexpr int kMfmaItemDmas = (kMfmaItemPieces + 63) / 64;         // 5
+constexpr int kMfmaRingBytes = kMfmaWaves * 2 * kMfmaItemBytes;    // 69632
+constexpr int kMfmaActBytes = 64 * 16 * 64;                        // [pair][token][64 B]
+constexpr int kMfmaXsBytes = 128 * 16 * 4;                         // [block][token] fp32
+constexpr int kMfmaTabBytes = 2 * kMfmaWaves * 256 * 4;            // two [wave][row][token] tables
+constexpr int kMfmaResBytes = 256 * 4;                             // [row][token] residual
+constexpr int kMfmaLdsBytes = kMfmaRingBytes + kMfmaActBytes + kMfmaXsBytes + kMfmaTabBytes + kMfmaResBytes;
+static_assert(kMfmaLdsBytes <= 160 * 1024, "fits the LDS of a CU");
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
     const uint8_t* __restrict__ w, int N, int P, int64_t row_bytes,
     const int8_t* __restrict__ xq, int64_t K, const float* __restrict__ xd, int n_tok,
     const float* residual, float* y, int64_t ldy, int n_tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  uint32_t* s_act = reinterpret_cast<uint32_t*>(lds_dyn);
-  float* s_sc = reinterpret_cast<float*>(lds_dyn + kMfmaActBytes);
-  uint32_t* s_zero = reinterpret_cast<uint32_t*>(lds_dyn + kMfmaActBytes + kMfmaScBytes);
-  float* s_tab = reinterpret_cast<float*>(lds_dyn + kMfmaActBytes + kMfmaScBytes + kMfmaZeroBytes);
+  uint8_t* ring = lds_dyn;
+  uint8_t* s_act = lds_dyn + kMfmaRingBytes;
+  float* s_xs = reinterpret_cast<float*>(s_act + kMfmaActBytes);
+  float* s_tab = s_xs + kMfmaXsBytes / 4;
+  float* s_res = s_tab + kMfmaTabBytes / 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop bounds
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar bounds
   const int col = lane & 15;
   const int kq = lane >> 4;
-  const int chunks = (P + 63) / 64;
+  const int C = (P + 63) / 64;
   const int nb = 2 * P;
   const int my_tiles = (int)blockIdx.x < n_tiles ? (n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-  // combine: 32 lanes of every wave -> output (row, token)
-  const bool comb = lane < 32;
-  const int cidx = wave * 32 + (lane & 31);
-  const int trow = cidx >> 4;
-  const int ttok = cidx & 15;
-  for (int e = tid; e < kMfmaZeroBytes / 4; e += kMfmaThreads) s_zero[e] = 0u;
-  // this lane's activation piece of pair j: act_l + 256 j dwords (tokens >= n_tok
-  // and the other block's lanes read zeros at the same offsets)
-  const uint32_t* act_l = s_act + (wave * kMfmaPairs * 16 + col) * 16 + 4 * kq;
-  const uint32_t* zero_l = s_zero + col * 16 + 4 * kq;
-  const uint32_t* srcA = (kq <= 1 && col < n_tok) ? act_l : zero_l;
-  const uint32_t* srcB = (kq >= 2 && col < n_tok) ? act_l : zero_l;
-  const float* sc_l = s_sc + wave * kMfmaPairs * 48 + 4 * kq;
-  const int bperm_b = (col + 16) * 4;  // lane holding pair dword 8 (the scale of B) for this row
+  const int n_units = my_tiles * C;
+  const int n_items = 2 * n_units;
+  auto unit_tile = [&](int u) { return (int)blockIdx.x + (u / C) * (int)gridDim.x; };
+  // DMA instructions this wave has issued: every wait below names how many of
+  // them may still be outstanding, and only instructions that some lane
+  // executes are counted
+  int nv = 0;
 
-  // weights of item (chunk c, tile) for this wave
-  auto load_w = [&](MfmaW& B, int c, int tile) {
-    const int np = min(64, P - 64 * c);
-    // rows past N read row N-1; their sums stay in their own column and are never stored
-    const int n = min(tile * 16 + col, N - 1);
-    const uint8_t* pb = w + (int64_t)n * row_bytes + (int64_t)kPairBytes * (64 * (int64_t)c + kMfmaPairs * wave);
-    if (kMfmaPairs * wave + kMfmaPairs <= np) {
+  // item m = half m % 2 of unit m / 2: rows 16T .. 16T+15 (past N: row N-1,
+  // never stored), pairs 64c + 8 wave + 4 (m % 2) .. +3 (P % 4 == 0, so an
+  // item is whole or past the end); instruction k moves pieces 64k + lane:
+  // row piece / 17, bytes 16 (piece % 17) of the row's 272
+  // byte offset of this lane's piece of instruction k within a whole tile's item
+  uint32_t doff[kMfmaItemDmas];
 #pragma unroll
-      for (int j = 0; j < kMfmaPairs; ++j) {
-        B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 4 + 16 * kq);
-        B.d0[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j);
-      }
+  for (int k = 0; k < kMfmaItemDmas; ++k) {
+    const int q = min(64 * k + lane, kMfmaItemPieces - 1);
+    doff[k] = (uint32_t)(q / 17) * (uint32_t)row_bytes + 16u * (uint32_t)(q % 17);
+  }
+  auto issue_w = [&](int m) -> int {
+    if (m >= n_items) return 0;
+    const int u = m >> 1;
+    const int c = u % C;
+    const int T = unit_tile(u);
+    const int p0 = 64 * c + 8 * wave + 4 * (m & 1);
+    if (p0 >= P) return 0;
+    uint8_t* slot = ring + (wave * 2 + (m & 1)) * kMfmaItemBytes;
+    const int r0 = 16 * T;
+    const uint8_t* base = w + (int64_t)r0 * row_bytes + (int64_t)p0 * kPairBytes;
+    if (r0 + 16 <= N) {
+#pragma unroll
+      for (int k = 0; k < kMfmaItemDmas; ++k)
+        if (64 * k + lane < kMfmaItemPieces)
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + doff[k]), (lds_ptr)(slot + 1024 * k), 16, 0,
+                                           kWeightCpol);
     } else {
-      // last chunk of a row: pairs past the end are zero cells
+      const int rmax = N - 1 - r0;  // last row of the tile in the matrix
 #pragma unroll
-      for (int j = 0; j < kMfmaPairs; ++j) {
-        B.q[j] = u32x4a{0u, 0u, 0u, 0u};
-        B.d0[j] = 0u;
-        if (kMfmaPairs * wave + j < np) {
-          B.q[j] = *reinterpret_cast<const u32x4a*>(pb + kPairBytes * j + 4 + 16 * kq);
-          B.d0[j] = *reinterpret_cast<const uint32_t*>(pb + kPairBytes * j);
-        }
+      for (int k = 0; k < kMfmaItemDmas; ++k) {
+        const int q = 64 * k + lane;
+        if (q < kMfmaItemPieces)
+          __builtin_amdgcn_global_load_lds(
+              static_cast<const void*>(base + (int64_t)min(q / 17, rmax) * row_bytes + 16 * (q % 17)),
+              (lds_ptr)(slot + 1024 * k), 16, 0, kWeightCpol);
       }
     }
+    return kMfmaItemDmas;
   };
-
-  // this wave's 8-leaf subtree for the 4 tokens of its lane
-  auto wave_sub = [&](const MfmaW& B, float (&sub)[4]) {
-    struct PairOps {
-      v4i DA, DB;
-      f32x4 xa, xb;
-      u32x4a a0;
-      uint32_t dwb;
-    };
-    auto issue = [&](int j, PairOps& o) {
-      const v4i opA = __builtin_bit_cast(v4i, *reinterpret_cast<const u32x4a*>(srcA + j * 256));
-      const v4i opB = __builtin_bit_cast(v4i, *reinterpret_cast<const u32x4a*>(srcB + j * 256));
-      const v4i wop = __builtin_bit_cast(v4i, B.q[j]);
-      const v4i zero = {0, 0, 0, 0};
-      o.DA = __builtin_amdgcn_mfma_i32_16x16x64_i8(opA, wop, zero, 0, 0, 0);
-      o.DB = __builtin_amdgcn_mfma_i32_16x16x64_i8(opB, wop, zero, 0, 0, 0);
-      o.xa = *reinterpret_cast<const f32x4*>(sc_l + j * 48);
-      o.xb = *reinterpret_cast<const f32x4*>(sc_l + j * 48 + 16);
-      o.a0 = *reinterpret_cast<const u32x4a*>(sc_l + j * 48 + 32);
-      o.dwb = (uint32_t)__builtin_amdgcn_ds_bpermute(bperm_b, (int)B.q[j].w);
-      // keep program order: a pair's math must not wait for every pair's sums
-      asm volatile("" : "+v"(o.DA), "+v"(o.DB));
-    };
-    float st[3][4];
-    auto math = [&](int j, const PairOps& o) {
-      const float dwA = f16_bits_to_f32(B.d0[j]);
-      const float dwB = f16_bits_to_f32(o.dwb >> 16);
-      const float xar[4] = {o.xa.x, o.xa.y, o.xa.z, o.xa.w};
-      const float xbr[4] = {o.xb.x, o.xb.y, o.xb.z, o.xb.w};
-      const uint32_t a0r[4] = {o.a0.x, o.a0.y, o.a0.z, o.a0.w};
+  // the activations of chunk c for this wave's 8 pairs (64c + 8 wave + p,
+  // p < 8), in its own part of the stage: the codes of token t at 512 t, piece
+  // q of pair p at 16 ((4p + q + t) % 32); the block scales of token t at
+  // [16 t .. 16 t + 15] of its 256 floats.  Plain 16-byte loads of
+  // contiguous runs of each token's row (tokens 2i and 2i + 1 per code load,
+  // all 16 tokens' scales in one), stored to LDS; indices past n_tok or P read
+  // valid rows whose values are never used.
+  uint8_t* st_codes = s_act + 8192 * wave;
+  float* st_scales = s_xs + 256 * wave;
+  auto stage_act = [&](int c) {
+    const int pw = 64 * c + 8 * wave;  // first pair of the wave in the chunk
+    if (pw >= P) return;
+    const int v = ((lane & 31) - (lane >> 5)) & 31;  // with t = 2i + lane / 32: (pos - t) % 32
+    u32x4 cv[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int iA = __builtin_amdgcn_sdot4((int)B.d0[j], (int)a0r[r], o.DA[r], false);
-        const int iB = o.DB[r];
-        const float sA = fmul(fmul(dwA, xar[r]), (float)iA);
-        const float sB = fmul(fmul(dwB, xbr[r]), (float)iB);
-        float v = fadd(fadd(0.0f, sA), sB);
-        // 8-leaf tree over j, built as leaves arrive
-        if ((j & 1) == 0) {
-          st[0][r] = v;
-        } else {
-          v = fadd(st[0][r], v);
-          if ((j & 2) == 0) {
-            st[1][r] = v;
-          } else {
-            v = fadd(st[1][r], v);
-            if ((j & 4) == 0) st[2][r] = v;
-            else sub[r] = fadd(st[2][r], v);
-          }
-        }
-      }
-      asm volatile("" : "+v"(st[0][0]), "+v"(st[0][1]), "+v"(st[0][2]), "+v"(st[0][3]));
-    };
-    PairOps ops[2];
-    issue(0, ops[0]);
-#pragma unroll
-    for (int j = 0; j < kMfmaPairs; ++j) {
-      if (j + 1 < kMfmaPairs) issue(j + 1, ops[(j + 1) & 1]);
-      math(j, ops[j & 1]);
+    for (int i = 0; i < 8; ++i) {
+      const int t = min(2 * i + (lane >> 5), n_tok - 1);
+      const int vv = (v - 2 * i) & 31;
+      const int pr = vv >> 2, q = vv & 3;
+      cv[i] = *reinterpret_cast<const u32x4*>(xq + (int64_t)t * K + 64 * (int64_t)min(pw + pr, P - 1) + 16 * q);
     }
+    const int ts = min(lane >> 2, n_tok - 1);
+    // (a wave with only 4 pairs left reads its last 16 blocks ending at the row's end)
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(xd + (int64_t)ts * nb + min(2 * pw + 4 * (lane & 3), nb - 4));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(st_codes + 1024 * i + 16 * lane) = cv[i];
+    *reinterpret_cast<u32x4*>(st_scales + 4 * lane) = sv;
   };
 
-  int staged = -1;
-  MfmaW wA, wB;
-  for (int g0 = 0; g0 < my_tiles; g0 += kMfmaGroup) {
-    const int ng = min(kMfmaGroup, my_tiles - g0);
-    const int n_items = chunks * ng;  // item i = (chunk i / ng, tile g0 + i % ng)
-    float tot[kMfmaGroup];
+  int r_end = 0;
+  int w_end[2] = {0, 0};
+  // chunk 0's activations first (their loads are waited for at once; a load
+  // issued behind the weights would wait for them), then both ring slots fill;
+  // afterwards item m + 2 goes out as soon as item m's slot has been read
+  if (n_units > 0) stage_act(0);
+  nv += issue_w(0);
+  w_end[0] = nv;
+  nv += issue_w(1);
+  w_end[1] = nv;
+
+  long actA[8], actB[8];   // this lane's token: codes of the wave's pairs (k-group kq)
+  float xa[8][4], xb[8][4];  // block scales of tokens 4kq .. 4kq+3
+  float tot = 0.0f;          // threads < 256: running total of (row tid / 16, token tid % 16)
+  for (int u = 0; u < n_units; ++u) {
+    const int c = u % C;
+    const int T = unit_tile(u);
+    if (u == 0 || C > 1) {
+      // this chunk's activations to registers: a wave reads back only the part
+      // of the stage that it wrote itself, so no barrier is needed
+      if (u > 0) stage_act(c);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int kk = 0; kk < kMfmaGroup; ++kk) tot[kk] = 0.0f;
-    auto tile_of = [&](int i) { return (int)blockIdx.x + (g0 + i % ng) * (int)gridDim.x; };
-    auto item = [&](int i, MfmaW& cur, MfmaW& nxt) {
-      const int c = i / ng;
-      const int kk = i - c * ng;
-      if (staged != c) {
-        __syncthreads();
-        const int np = min(64, P - 64 * c);
-        for (int e = tid; e < 64 * 16; e += kMfmaThreads) {
-          const int pl = e >> 4;
-          const int t = e & 15;
-          const int64_t pp = 64 * (int64_t)c + pl;
-          uint32_t o[17];
-          float da = 0.0f, db = 0.0f;
-          if (pl < np && t < n_tok) {
-            const u32x4a* src = reinterpret_cast<const u32x4a*>(xq + (int64_t)t * K + 64 * pp);
-            uint32_t a[16];
+      for (int j = 0; j < 8; ++j) {
+        const int p = 8 * wave + j;
+        const bool ok = col < n_tok && 64 * c + p < P;
+        const uint32_t* e = reinterpret_cast<const uint32_t*>(st_codes + 512 * col) + kq;
+        const uint32_t a0 = e[4 * ((4 * j + 0 + col) & 31)], a1 = e[4 * ((4 * j + 1 + col) & 31)];
+        const uint32_t b0 = e[4 * ((4 * j + 2 + col) & 31)], b1 = e[4 * ((4 * j + 3 + col) & 31)];
+        actA[j] = ok ? (long)(((uint64_t)a1 << 32) | a0) : 0;
+        actB[j] = ok ? (long)(((uint64_t)b1 << 32) | b0) : 0;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const u32x4a q = src[v];
-              a[4 * v + 0] = q.x;
-              a[4 * v + 1] = q.y;
-              a[4 * v + 2] = q.z;
-              a[4 * v + 3] = q.w;
-            }
-            o[0] = a[0] << 16;
-#pragma unroll
-            for (int q = 1; q < 8; ++q) o[q] = (a[q - 1] >> 16) | (a[q] << 16);
-            o[8] = a[7] >> 16;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) o[9 + q] = a[8 + q];
-            da = xd[(int64_t)t * nb + 2 * pp];
-            db = xd[(int64_t)t * nb + 2 * pp + 1];
-          } else {
-#pragma unroll
-            for (int q = 0; q < 17; ++q) o[q] = 0u;
-          }
-          if (t < n_tok) {
-            u32x4a* dst = reinterpret_cast<u32x4a*>(s_act + (pl * 16 + t) * 16);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              dst[v] = u32x4a{o[4 * v + 1], o[4 * v + 2], o[4 * v + 3], o[4 * v + 4]};
-          }
-          s_sc[(pl * 3 + 0) * 16 + t] = da;
-          s_sc[(pl * 3 + 1) * 16 + t] = db;
-          s_sc[(pl * 3 + 2) * 16 + t] = __uint_as_float(o[0]);
-        }
-        __syncthreads();
-        staged = c;
-      }
-      // wait for this tile's weights here, once, before the next tile's loads
-      // queue up behind them (the memory counter retires loads in order)
-#pragma unroll
-      for (int j = 0; j < kMfmaPairs; ++j) asm volatile("" ::"v"(cur.q[j]), "v"(cur.d0[j]));
-      if (i + 1 < n_items) load_w(nxt, (i + 1) / ng, tile_of(i + 1));
-      float sub[4];
-      wave_sub(cur, sub);
-      float* tab = s_tab + (i & 1) * (kMfmaWaves * 256);
-      *reinterpret_cast<f32x4*>(tab + (wave * 16 + col) * 16 + 4 * kq) = f32x4{sub[0], sub[1], sub[2], sub[3]};
-      __syncthreads();
-      if (comb) {
-        const float* tb = tab + trow * 16 + ttok;
-        const float cs = fadd(fadd(fadd(tb[0], tb[256]), fadd(tb[512], tb[768])),
-                              fadd(fadd(tb[1024], tb[1280]), fadd(tb[1536], tb[1792])));
-#pragma unroll
-        for (int q = 0; q < kMfmaGroup; ++q)
-          if (q == kk) tot[q] = c == 0 ? cs : fadd(tot[q], cs);
-        if (c == chunks - 1) {
-          const int n = tile_of(i) * 16 + trow;
-          if (n < N && ttok < n_tok) {
-            float v = 0.0f;
-#pragma unroll
-            for (int q = 0; q < kMfmaGroup; ++q)
-              if (q == kk) v = tot[q];
-            store_out(v, n, ttok, residual, y, ldy);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const bool okr = 4 * kq + r < n_tok && 64 * c + p < P;
+          const float2 ab = *reinterpret_cast<const float2*>(st_scales + 16 * (4 * kq + r) + 2 * j);
+          xa[j][r] = okr ? ab.x : 0.0f;
+          xb[j][r] = okr ? ab.y : 0.0f;
         }
       }
-    };
-    load_w(wA, 0, tile_of(0));
-    for (int i = 0; i < n_items; i += 2) {
-      item(i, wA, wB);
-      if (i + 1 < n_items) item(i + 1, wB, wA);
+      // the reads are done before a later chunk's stores refill the stage
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    const bool last = c == C - 1;
+    if (last && residual && wave < 4) {
+      // the residual of the tile's outputs (row tid / 16, token tid % 16) to s_res[tid]
+      const int row = tid >> 4, tok = tid & 15;
+      if (16 * T + 4 * wave < N) {
+        if (tok < n_tok && 16 * T + row < N)
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(residual + (int64_t)tok * ldy + 16 * T + row),
+                                           (lds_ptr)(s_res + 64 * wave), 4, 0, 0);
+        ++nv;
+      }
+      r_end = nv;
+    }
+
+    float sub[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = 2 * u + h;
+      wait_vmcnt_wave(nv - w_end[m & 1]);
+      float qs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (64 * c + 8 * wave + 4 * h < P) {
+        const uint8_t* slot = ring + (wave * 2 + (m & 1)) * kMfmaItemBytes + col * kMfmaRowBytes;
+        // all reads of the item, then its eight MFMAs, then the cells
+        uint32_t wd[4][8];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t* rp = reinterpret_cast<const uint32_t*>(slot + kPairBytes * jj);
+          const uint32_t* rk = rp + kq;
+          wd[jj][0] = rk[0];
+          wd[jj][1] = rk[1];
+          wd[jj][2] = rk[4];
+          wd[jj][3] = rk[5];
+          wd[jj][4] = rk[9];
+          wd[jj][5] = rk[13];
+          wd[jj][6] = rp[0];
+          wd[jj][7] = rp[8];
+        }
+        v4i DA[4], DB[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * h + jj;
+          const uint32_t w0 = __builtin_amdgcn_alignbit(wd[jj][1], wd[jj][0], 16);
+          const uint32_t w1 = __builtin_amdgcn_alignbit(wd[jj][3], wd[jj][2], 16);
+          const long wa = (long)(((uint64_t)w1 << 32) | w0);
+          const long wb = (long)(((uint64_t)wd[jj][5] << 32) | wd[jj][4]);
+          const v4i zero = {0, 0, 0, 0};
+          DA[jj] = __builtin_amdgcn_mfma_i32_16x16x32_i8(actA[j], wa, zero, 0, 0, 0);
+          DB[jj] = __builtin_amdgcn_mfma_i32_16x16x32_i8(actB[j], wb, zero, 0, 0, 0);
+        }
+        float lf[4][4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * h + jj;
+          const float dwA = f16_bits_to_f32(wd[jj][6]);
+          const float dwB = f16_bits_to_f32(wd[jj][7] >> 16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sA = fmul(fmul(dwA, xa[j][r]), (float)DA[jj][r]);
+            const float sB = fmul(fmul(dwB, xb[j][r]), (float)DB[jj][r]);
+            lf[jj][r] = fadd(fadd(0.0f, sA), sB);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qs[r] = fadd(fadd(lf[0][r], lf[1][r]), fadd(lf[2][r], lf[3][r]));
+      }
+      // the slot's reads are done (their values are in the sums): refill it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      nv += issue_w(m + 2);
+      w_end[m & 1] = nv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sub[r] = h == 0 ? qs[r] : fadd(sub[r], qs[r]);
+    }
+
+    // the wave subtrees of (row col, tokens 4kq .. 4kq+3), then the top levels
+    float* tab = s_tab + (u & 1) * (kMfmaWaves * 256);
+    *reinterpret_cast<f32x4*>(tab + (wave * 16 + col) * 16 + 4 * kq) = f32x4{sub[0], sub[1], sub[2], sub[3]};
+    if (last && residual && wave < 4) wait_vmcnt_wave(nv - r_end);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < 256) {
+      const float* tb = tab + tid;  // (row tid / 16, token tid % 16) of wave 0's table
+      const float cs = fadd(fadd(fadd(tb[0], tb[256]), fadd(tb[512], tb[768])),
+                            fadd(fadd(tb[1024], tb[1280]), fadd(tb[1536], tb[1792])));
+      tot = c == 0 ? cs : fadd(tot, cs);
+      if (last) {
+        const int n = 16 * T + (tid >> 4);
+        const int tok = tid & 15;
+        if (n < N && tok < n_tok) y[(int64_t)tok * ldy + n] = residual ? fadd(s_res[tid], tot) : tot;
+      }
     }
   }
 }
 
-// Raises a kernel's dynamic LDS limit to kGemvLdsMax, once per kernel and
-// process (thread-safe: concurrent first calls wait for the one that sets it).
-template <auto Kern>
+// Raises a kernel's dynamic LDS limit to Bytes, once per kernel and process
+// (thread-safe: concurrent first calls wait for the one that sets it).
+template <auto Kern, int Bytes = kGemvLdsMax>
 hipError_t raise_lds_once() {
   static std::once_flag once;
   static hipError_t err = hipSuccess;
   std::call_once(once, [] {
     err = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kGemvLdsMax);
+                              Bytes);
   });
   return err;
 }
@@ -973,8 +997,7 @@ hipError_t raise_lds_once() {
 hipError_t launch_mfma(const GemvPlan& pl, const void* w, int64_t N, int64_t K, const int8_t* xq,
                        const float* xd, int n_tok, const float* residual, float* y, int64_t ldy,
                        hipStream_t st) {
-  // up to 80 KiB of dynamic LDS
-  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_mfma>(); e != hipSuccess) return e;
+  if (hipError_t e = raise_lds_once<&k_qgemv_q8_0_mfma, kMfmaLdsBytes>(); e != hipSuccess) return e;
   hipLaunchKernelGGL(k_qgemv_q8_0_mfma, dim3(pl.grid), dim3(kMfmaThreads), pl.lds_bytes, st,
                      static_cast<const uint8_t*>(w), (int)N, pl.pairs, (int64_t)(K / 32 * kBlockBytes),
                      xq, K, xd, n_tok, residual, y, ldy, pl.n_blocks);
@@ -1029,7 +1052,7 @@ hipError_t launch_dma_nt(const GemvPlan& pl, const void* w, int64_t N, int64_t K
 
 }  // namespace
 
-size_t mfma_lds_bytes() { return (size_t)kMfmaActBytes + kMfmaScBytes + kMfmaZeroBytes + kMfmaTabBytes; }
+size_t mfma_lds_bytes() { return (size_t)kMfmaLdsBytes; }
 
 bool plan_qgemv(int64_t N, int64_t K, int n_tok, int path, GemvPlan* plan) {
   if (N < 1 || K < 256 || K % 256 != 0 || n_tok < 1 || n_tok > SD_MAX_TOKENS) return false;

@@ -83,6 +83,22 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
   }
 }
 
+// The same for a count held per wave (made scalar here, so the choice is a
+// scalar branch), up to 31; a larger n waits for at most 31: longer, never
+// shorter.
+__device__ __forceinline__ void wait_vmcnt_wave(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+#define SD_WAIT(i) \
+  case i: wait_vmcnt<i>(); break;
+    SD_WAIT(0) SD_WAIT(1) SD_WAIT(2) SD_WAIT(3) SD_WAIT(4) SD_WAIT(5) SD_WAIT(6) SD_WAIT(7)
+    SD_WAIT(8) SD_WAIT(9) SD_WAIT(10) SD_WAIT(11) SD_WAIT(12) SD_WAIT(13) SD_WAIT(14) SD_WAIT(15)
+    SD_WAIT(16) SD_WAIT(17) SD_WAIT(18) SD_WAIT(19) SD_WAIT(20) SD_WAIT(21) SD_WAIT(22) SD_WAIT(23)
+    SD_WAIT(24) SD_WAIT(25) SD_WAIT(26) SD_WAIT(27) SD_WAIT(28) SD_WAIT(29) SD_WAIT(30)
+#undef SD_WAIT
+    default: wait_vmcnt<31>(); break;
+  }
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Cache policy of the weight DMAs: non-temporal (nt).  Each weight byte is

@@ -1,6 +1,6 @@
 """The widened verify batch: n_tok up to 16 on both q8_0 GEMV kernels.
 
-The v_dot4 ("narrow") kernels and the matrix-core kernel (v_mfma_i32_16x16x64_i8)
+The v_dot4 ("narrow") kernels and the matrix-core kernel (v_mfma_i32_16x16x32_i8)
 form the same cells in the same fixed order, so their outputs must agree
 bitwise for every shape and width; both are also held to the oracle (1e-5 of
 sum|s_b| per element).  Shapes cover ragged N (not a multiple of the 16-row

@@ -779,17 +779,18 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void k_qgemv_q8_0_mfma(
   // executes are counted
   int nv = 0;
 
-  // item m = half m % 2 of unit m / 2: rows 16T .. 16T+15 (past N: row N-1,
-  // never stored), pairs 64c + 8 wave + 4 (m % 2) .. +3 (P % 4 == 0, so an
-  // item is whole or past the end); instruction k moves pieces 64k + lane:
-  // row piece / 17, bytes 16 (piece % 17) of the row's 272
-  // byte offset of this lane's piece of instruction k within a whole tile's item
+  // byte offset of this lane's piece of DMA k within an item of a whole tile
+  // (pieces as in issue_w below)
   uint32_t doff[kMfmaItemDmas];
 #pragma unroll
   for (int k = 0; k < kMfmaItemDmas; ++k) {
     const int q = min(64 * k + lane, kMfmaItemPieces - 1);
     doff[k] = (uint32_t)(q / 17) * (uint32_t)row_bytes + 16u * (uint32_t)(q % 17);
   }
+  // item m = half m % 2 of unit m / 2: rows 16T .. 16T+15 (past N: row N-1,
+  // never stored), pairs 64c + 8 wave + 4 (m % 2) .. +3 (P % 4 == 0, so an
+  // item is whole or past the end); DMA k moves pieces 64k + lane: row
+  // piece / 17, bytes 16 (piece % 17) of the row's 272.  Returns the DMAs issued.
   auto issue_w = [&](int m) -> int {
     if (m >= n_items) return 0;
     const int u = m >> 1;

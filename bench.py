@@ -882,6 +882,65 @@ def _kernel_stats(rows, top=24):
     return "\n".join(lines)
 
 
+def wide_trace_summary(trace_db, fetch_db=None, write_db=None, n_tok=16):
+    """Summary of rocprofv3 results databases of `bench.py --wide-only` (and,
+    for the counter runs, `--wide-only --calibrate-copy`): the matrix-core
+    GEMV's launches of the roofline pass at n_tok 16 (per shape, in launch order
+    QKV, O, gate|up, down, the 128 timed ones of its 192), their average trace
+    duration, and from the counter runs their HBM bytes per launch (FETCH_SIZE
+    and WRITE_SIZE scaled by what the counters read for the 1 GiB calibration
+    copy)."""
+    import hashlib
+    import statistics
+    kern = "k_qgemv_q8_0_mfma"
+    per_shape_n = (ROOF_WARM_ROUNDS + ROOF_REPS) * N_LAYERS
+    skip = ROOF_WARM_ROUNDS * N_LAYERS
+    shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
+
+    def launches(rows):
+        a = [v for n, v in rows if _short_kernel(n) == kern][-4 * per_shape_n:]
+        if len(a) < 4 * per_shape_n:
+            raise RuntimeError("the database does not hold the matrix-core roofline pass")
+        return {k: a[i * per_shape_n + skip:(i + 1) * per_shape_n] for i, k in enumerate(shapes)}
+
+    tr = _rocpd_dispatches(trace_db)
+    roof = launches(tr)
+    out = {"kernel_stats": _kernel_stats(tr), "n_tok": n_tok, "per_shape": {}}
+    tot_us, tot_b, n_all = 0.0, 0, 0
+    for k, v in roof.items():
+        b = gemv_bytes(*shapes[k], n_tok)
+        out["per_shape"][k] = {"trace_avg_us": round(statistics.mean(v), 3),
+                               "GB_s": round(b / statistics.mean(v) / 1e3, 1)}
+        tot_us += sum(v)
+        tot_b += b * len(v)
+        n_all += len(v)
+    out["trace_avg_us_per_launch"] = round(tot_us / n_all, 3)
+    out["achieved_GB_s"] = round(tot_b / tot_us / 1e3, 1)
+    out["gemv_us_per_sweep"] = round(sum(statistics.mean(v) for v in roof.values()) * N_LAYERS, 1)
+    if fetch_db and write_db:
+        f = _rocpd_dispatches(fetch_db, "FETCH_SIZE")
+        w = _rocpd_dispatches(write_db, "WRITE_SIZE")
+        ff = (1 << 30) / ([v for n, v in f if "copyBuffer" in n][-1] * 1024)
+        wf = (1 << 30) / ([v for n, v in w if "copyBuffer" in n][-1] * 1024)
+        rf, rw = launches(f), launches(w)
+        out["fetch_factor"], out["write_factor"] = round(ff, 4), round(wf, 4)
+        out["traffic_per_shape"] = {}
+        for k in shapes:
+            fb = statistics.mean(rf[k]) * 1024 * ff
+            wb = statistics.mean(rw[k]) * 1024 * wf
+            alg = gemv_bytes(*shapes[k], n_tok)
+            out["traffic_per_shape"][k] = {"fetched": int(round(fb)), "written": int(round(wb)),
+                                           "algorithmic": alg, "ratio": round((fb + wb) / alg, 4)}
+        fetched = sum(sum(v) for v in rf.values()) * 1024 * ff / n_all
+        written = sum(sum(v) for v in rw.values()) * 1024 * wf / n_all
+        out["traffic_bytes_per_launch"] = int(round(fetched + written))
+        out["algorithmic_bytes_per_launch"] = int(round(tot_b / n_all))
+        out["traffic_over_algorithmic"] = round((fetched + written) / (tot_b / n_all), 4)
+    src = os.path.join(ROOT, "sequence_decode_amd", "csrc", "qgemv.hip")
+    out["kernel_source_sha256"] = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return out
+
+
 ATTN_CASES = {"n1_2050": [2050], "n4_2050": [2050] * 4, "n4_ragged": [2050, 3072, 16384, 32768],
               "n1_32768": [32768]}
 
@@ -1009,6 +1068,10 @@ def main():
                          "trace [FETCH_SIZE WRITE_SIZE]")
     ap.add_argument("--step-trace-summary", metavar="DB",
                     help="print the per-step kernel breakdown of a rocprofv3 database of --step-only N")
+    ap.add_argument("--wide-only", action="store_true",
+                    help="only the matrix-core GEMV's per-shape roofline pass at 16 tokens (for profiling)")
+    ap.add_argument("--wide-trace-summary", nargs="+", metavar="DB",
+                    help="summarize rocprofv3 databases of --wide-only: trace [fetch write]")
     ap.add_argument("--trace-summary", nargs="+", metavar="DB",
                     help="summarize rocprofv3 results databases of a --sweep-only run: the kernel-trace "
                          "database, then optionally the FETCH_SIZE and WRITE_SIZE ones (no GPU used)")
@@ -1023,6 +1086,9 @@ def main():
     if args.trace_summary:
         print(json.dumps(trace_summary(*args.trace_summary[:3], n_tok=args.n_tok), indent=1))
         return
+    if args.wide_trace_summary:
+        print(json.dumps(wide_trace_summary(*args.wide_trace_summary[:3]), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode step here is built and measured on a "
               "single MI355X; run it with --gpus 1", file=sys.stderr)
@@ -1034,7 +1100,8 @@ def main():
     # the decode tok/s come from fresh processes started before this one
     # touches the GPU: 8 warmups, 64 timed steps, median of the processes
     decode = None
-    if (not args.no_decode and not args.step_only and not args.attention_only and not args.sweep_only):
+    if (not args.no_decode and not args.step_only and not args.attention_only and not args.sweep_only
+            and not args.wide_only):
         decode = decode_children(args.decode_procs, 64, 8)
 
     import torch
@@ -1061,6 +1128,14 @@ def main():
     log("generating 7.42 GB of q8_0 projection weights on the device")
     sweep = Sweep(sd, torch, seed=1, max_tok=16)
     torch.cuda.synchronize()
+    if args.wide_only:
+        # the 16-token sweep (graph-timed) and its per-shape roofline pass, on
+        # the matrix-core kernel that sd_qgemv_q8_0_batch picks at 16 tokens
+        dt, runs = sweep_median(torch, sweep, 16, max(3, args.steps // 2), 2)
+        _, _, _, roof_shapes = roofline_pass(torch, sweep, 16, ROOF_REPS)
+        print(json.dumps({"n_tok": 16, "GB_s": round(sweep.bytes_per_step(16) / dt / 1e9, 1),
+                          "ms_per_step": round(dt * 1e3, 4), "per_shape": roof_shapes}), flush=True)
+        return
 
     per_n = {}
     for n in (1, 2, 3, 4):

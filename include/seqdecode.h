@@ -285,8 +285,10 @@ size_t sd_decode_attn_workspace_bytes(const sd_seqview* views, int n_seq, int H_
  *   out  [n_seq][H_q][D] fp32 contiguous, 16-byte aligned.
  *   ws   workspace of at least sd_decode_attn_workspace_bytes(), 16-byte aligned.
  *   views [host]: 16-byte aligned bases, ld_tok and ld_head multiples of 8.
- * Requires 1 <= n_seq <= SD_MAX_SEQS, D == 128, H_q % H_kv == 0,
- * H_q / H_kv == 4 (grouped-query attention with four query heads per KV head),
+ * Requires 1 <= n_seq <= SD_MAX_SEQS, D == 128, H_q % H_kv == 0 (any number G
+ * of query heads per KV head: a workgroup takes a head group, the hpw query
+ * heads of one KV head with hpw the largest divisor of G up to 4, so for G of
+ * 8, 16, 5, ... each of a KV head's G / hpw groups reads its keys and values),
  * ctx_len >= 1 and, for a plain view, ctx_len <= capacity; a ring needs
  * window >= 1 and min(ctx_len, window + n_new - 1) <= capacity (n_new = 1
  * here).  The keys attended to span at most SD_MAX_CTX positions (else
@@ -508,7 +510,7 @@ size_t sd_decode_step_workspace_bytes(const sd_model* m, int rows, int max_ctx);
  * causally.  Every row's logits and token are bitwise those of one-token steps
  * of that sequence alone, run one after another over the same tokens.
  * Requires 1 <= n_seq <= SD_MAX_SEQS, rows <= SD_MAX_TOKENS, head_dim == 128,
- * n_heads == 4*n_kv_heads, hidden % 256 == 0, ffn % 256 == 0,
+ * n_heads % n_kv_heads == 0, hidden % 256 == 0, ffn % 256 == 0,
  * n_heads*head_dim % 256 == 0, 0 <= pos and, for plain caches,
  * pos + n_new <= capacity (rings and paged pools as in sd_seqview).
  */

@@ -141,7 +141,7 @@ int attn_common(const float* q, int64_t ld_q, const sd_seqview* views, const int
                 int n_seq, int H_q, int H_kv, int D, float scale, float* out, void* ws,
                 size_t ws_bytes, sd_stream_t stream) {
   if (!q || !out || !ws || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SD_EINVAL;
-  if (D != kAttnHeadDim || H_q / H_kv != kAttnGroup) return SD_EUNSUPPORTED;
+  if (D != kAttnHeadDim) return SD_EUNSUPPORTED;
   if (ld_q < (int64_t)H_q * D || !isfinite(scale)) return SD_EINVAL;
   int rc = check_views(views, n_seq, D, true, n_new);
   if (rc != SD_OK) return rc;
@@ -244,7 +244,8 @@ size_t sd_decode_attn_verify_workspace_bytes(const sd_seqview* views, const int3
   SeqArgs a;
   if (check_views(views, n_seq, D, true, n_new) != SD_OK) return 0;
   fill_seqargs(views, n_seq, &a, n_new);
-  return attn_layout(&a, H_q, H_q / kAttnGroup) * sizeof(float);
+  // (the partials do not depend on how the query heads share KV heads)
+  return attn_layout(&a, H_q, H_q) * sizeof(float);
 }
 
 int sd_decode_attn_multiseq(const float* q, int64_t ld_q, const sd_seqview* views, int n_seq,
@@ -257,7 +258,7 @@ int sd_decode_attn_multiseq_noalloc(const float* q, int64_t ld_q, const sd_seqvi
                                     int H_q, int H_kv, int D, float scale, float* out,
                                     sd_stream_t stream) {
   if (!q || !out || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SD_EINVAL;
-  if (D != kAttnHeadDim || H_q / H_kv != kAttnGroup) return SD_EUNSUPPORTED;
+  if (D != kAttnHeadDim) return SD_EUNSUPPORTED;
   if (ld_q < (int64_t)H_q * D || !isfinite(scale)) return SD_EINVAL;
   int rc = check_views(views, n_seq, D, true);
   if (rc != SD_OK) return rc;

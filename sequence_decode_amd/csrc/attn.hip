@@ -198,22 +198,26 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   __shared__ float s_m[4][16], s_l[4][16];  // per wave and MFMA column (token, head)
 
   // The grid holds every sequence's 256-key units first (the long-running
-  // ones start first), then its 64-key units; within each, KV head by KV head.
+  // ones start first), then its 64-key units; within each, head group by head
+  // group (a head group: seqs.hpw query heads of one KV head; seqs.vg groups
+  // share each KV head).
   const bool large = (int)blockIdx.x < seqs.large_total;
   const int s = find_seq(seqs, blockIdx.x, large);
   const SeqArg& A = seqs.s[s];
-  const int n_su = (A.ns + A.pk - 1) / A.pk;  // 64-key units per KV head
-  const int n_lu = A.n_chunks - A.ns;         // 256-key units per KV head
-  int g, u;  // KV head, and unit within it (64-key units first)
+  const int n_su = (A.ns + A.pk - 1) / A.pk;  // 64-key units per head group
+  const int n_lu = A.n_chunks - A.ns;         // 256-key units per head group
+  int hg, u;  // head group, and unit within it (64-key units first)
   if (large) {
     const int local = blockIdx.x - A.large_begin;
-    g = local / n_lu;
-    u = n_su + (local - g * n_lu);
+    hg = local / n_lu;
+    u = n_su + (local - hg * n_lu);
   } else {
     const int local = blockIdx.x - A.small_begin;
-    g = local / n_su;
-    u = local - g * n_su;
+    hg = local / n_su;
+    u = local - hg * n_su;
   }
+  const int hpw = seqs.hpw;    // query heads of the group (columns 4 tk + hh, hh < hpw)
+  const int g = hg / seqs.vg;  // its KV head
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // The chunk of this wave.  Units 0 .. n_su-1 hold the chunks of the 64-key
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
     const int T = A.n_new;
     const int tk = col >> 2;
     const int hh = col & (kAttnGroup - 1);
-    const bool colv = tk < T;
+    const bool colv = tk < T && hh < hpw;
     const int p_col = A.ctx_len - T + tk;
     const int nk_col = colv ? min(csz, p_col + 1 - j0) : 0;
     const int jlo_col = A.window ? max(0, p_col - A.window + 1) - j0 : 0;
@@ -380,13 +384,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       ksc = *reinterpret_cast<const u32x2a*>(A.kd + so);
       vsc = *reinterpret_cast<const u32x2a*>(A.vd + so);
     }
-    // ---- q (score B operands): column col = (token tk, head g*4 + hh), dims 32kk + 8kg ..
-    // (a column past the sequence's tokens reads its last token: all its keys are
-    // masked and its partial is not stored)
+    // ---- q (score B operands): column col = (token tk, head hg*hpw + hh), dims 32kk + 8kg ..
+    // (a column past the sequence's tokens or the group's heads reads its last
+    // token or head: all its keys are masked and its partial is not stored)
     f32x4 qv[4][2];
     {
       const f32x4* qp = reinterpret_cast<const f32x4*>(
-          q + (int64_t)(A.row0 + min(tk, T - 1)) * ld_q + (int64_t)(g * kAttnGroup + hh) * HD + 8 * kg);
+          q + (int64_t)(A.row0 + min(tk, T - 1)) * ld_q + (int64_t)(hg * hpw + min(hh, hpw - 1)) * HD + 8 * kg);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         qv[kk][0] = qp[8 * kk];
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       // later tokens make the same chunk a four-wave one), so the bits agree.
       const int p2 = A.ctx_len - T + tk;
       if (colv && j0 <= p2 && !(A.window && j0 + csz <= p2 - A.window + 1)) {
-        const int h = g * kAttnGroup + hh;
+        const int h = hg * hpw + hh;
         float* dst = part + ((int64_t)A.partial_begin + ((int64_t)tk * H_q + h) * A.n_chunks + ci) * PF;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
@@ -685,6 +689,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
       const int d = idx - cc * HD;
       const int t2 = cc >> 2;
       const int p2 = A.ctx_len - T + t2;
+      if ((cc & (kAttnGroup - 1)) >= hpw) continue;  // no head of the group
       if (j0 > p2) continue;  // chunk past this token's position
       if (A.window && j0 + csz <= p2 - A.window + 1) continue;  // chunk before its window
       float O = 0.0f, L = 0.0f;
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
         L = fadd(L, s_l[w][cc]);
       }
       const float Mh = fmaxf(fmaxf(s_m[0][cc], s_m[1][cc]), fmaxf(s_m[2][cc], s_m[3][cc]));
-      const int h = g * kAttnGroup + (cc & (kAttnGroup - 1));
+      const int h = hg * hpw + (cc & (kAttnGroup - 1));
       float* dst = part + ((int64_t)A.partial_begin + ((int64_t)t2 * H_q + h) * A.n_chunks + ci) * PF;
       dst[4 + d] = O;
       if (d == 0) {
@@ -873,6 +878,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(SeqArgs seqs, int H_q,
 }  // namespace
 
 size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
+  // head groups: the largest divisor of the group size H_q / H_kv that fills at
+  // most the 4 head columns of a workgroup (four: one group per KV head)
+  const int G = H_q / H_kv;
+  a->hpw = G >= 4 && G % 4 == 0 ? 4 : (G % 3 == 0 ? 3 : (G % 2 == 0 ? 2 : 1));
+  a->vg = G / a->hpw;
+  const int n_hg = H_q / a->hpw;
   int parts = 0, rows = 0;
   int64_t small_keys = 0, large_keys = 0;
   for (int s = 0; s < a->n_seq; ++s) {
@@ -892,7 +903,7 @@ size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
   // most of its keys sit in 256-key chunks, four per workgroup (one per wave)
   // do better (graph-timed, us, one vs four per workgroup: {2050, 3072} 14.9
   // vs 13.8; four 2050s 16.5 vs 15.0; one 32768-key sequence 34.7 vs 32.6).
-  const int pk = small_keys / kAttnSmallChunk * H_kv > kAttnSpreadUnits || large_keys > small_keys ? 4 : 1;
+  const int pk = small_keys / kAttnSmallChunk * n_hg > kAttnSpreadUnits || large_keys > small_keys ? 4 : 1;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.pk = pk;
@@ -906,13 +917,13 @@ size_t attn_layout(SeqArgs* a, int H_q, int H_kv) {
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.large_begin = units;
-    units += (x.n_chunks - x.ns) * H_kv;
+    units += (x.n_chunks - x.ns) * n_hg;
   }
   a->large_total = units;
   for (int s = 0; s < a->n_seq; ++s) {
     SeqArg& x = a->s[s];
     x.small_begin = units;
-    units += (x.ns + pk - 1) / pk * H_kv;
+    units += (x.ns + pk - 1) / pk * n_hg;
   }
   a->units_total = units;
   return (size_t)parts * PF;

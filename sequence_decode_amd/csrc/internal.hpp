@@ -101,6 +101,8 @@ struct SeqArgs {
   int32_t n_seq;
   int32_t large_total;  // workgroups holding 256-key units (they come first)
   int32_t units_total;  // all workgroups of the chunk kernel
+  int32_t hpw;          // query heads per head group (a workgroup's columns): 1..4
+  int32_t vg;           // head groups per KV head (H_q / H_kv / hpw)
 };
 
 // Angle pos * theta^(-2i/n_rot) of RoPE pair i, its cosine and sine in fp64,

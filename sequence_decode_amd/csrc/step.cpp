@@ -30,7 +30,7 @@ struct StepLayout {
 bool model_ok(const sd_model* m) {
   if (!m || !m->layers || !m->tok_embd || !m->out_norm || !m->w_lm_head) return false;
   if (m->n_layers < 1 || m->hidden < 256 || m->vocab < 1 || m->ffn < 256) return false;
-  if (m->head_dim != kAttnHeadDim || m->n_kv_heads < 1 || m->n_heads != kAttnGroup * m->n_kv_heads)
+  if (m->head_dim != kAttnHeadDim || m->n_kv_heads < 1 || m->n_heads < 1 || m->n_heads % m->n_kv_heads != 0)
     return false;
   if (m->hidden % 256 != 0 || m->ffn % 256 != 0 || (m->n_heads * m->head_dim) % 256 != 0) return false;
   if (m->hidden > 32768 || m->ffn > 32768) return false;

@@ -110,7 +110,10 @@ def test_attention_rejections(L):
     v1 = (_lib.SeqView * 1)(_view(10, 16))
     assert a(FAKE, 4096, v1, 0, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
     assert a(FAKE, 4096, v1, 1, 32, 8, 64, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EUNSUPPORTED
-    assert a(FAKE, 4096, v1, 1, 32, 16, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EUNSUPPORTED
+    # any H_q / H_kv is accepted (two query heads per KV head here); a workspace
+    # too small is refused before any HIP call
+    assert a(FAKE, 4096, v1, 1, 32, 16, 128, 0.088, FAKE, FAKE, 16, None) == SD_EWORKSPACE
+    assert a(FAKE, 4096, v1, 1, 32, 32, 128, 0.088, FAKE, FAKE, 16, None) == SD_EWORKSPACE
     assert a(FAKE, 4096, v1, 1, 30, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL
     over = (_lib.SeqView * 1)(_view(17, 16))
     assert a(FAKE, 4096, over, 1, 32, 8, 128, 0.088, FAKE, FAKE, 1 << 20, None) == SD_EINVAL

@@ -1,0 +1,102 @@
+"""Decode attention for any number of query heads per KV head (H_q % H_kv == 0).
+
+A workgroup takes a head group: hpw query heads of one KV head, hpw the largest
+divisor of G = H_q / H_kv up to 4 (G = 1, 2, 3, 4 take one group per KV head;
+G = 5, 6, 8 take 5, 2, 2 groups, each reading the KV head's keys and values).
+Against the oracle (2e-3 absolute, 1e-4 normwise) on ragged contexts with
+verify bursts, fp16 and q8_0 caches; bitwise: burst tokens equal one-token
+calls over their prefixes, a sequence alone equals it inside the batch, and
+the allocation-free entry point equals the workspace one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import bits, dev, host, say
+from sequence_decode_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+SCALE = np.float32(1.0) / np.sqrt(np.float32(D))
+GROUPS = [(8, 8), (16, 8), (12, 4), (10, 2), (24, 4), (32, 4)]  # G = 1, 2, 3, 5, 6, 8
+
+
+def _check_parity(o, ref):
+    assert np.max(np.abs(o - ref)) <= 2e-3
+    rel = np.linalg.norm((o - ref).ravel()) / np.linalg.norm(ref.ravel())
+    assert rel <= 1e-4, rel
+
+
+def _fp16_caches(seed, lens, H_kv):
+    g = synth.rng(seed)
+    return [(synth.kv_cache(g, L + 2, H_kv, D), synth.kv_cache(g, L + 2, H_kv, D)) for L in lens]
+
+
+@pytest.mark.parametrize("H_q,H_kv", GROUPS)
+def test_groups_fp16_parity_prefix_and_solo(sd, H_q, H_kv):
+    import torch
+    say(f"attention head groups H_q={H_q} H_kv={H_kv}")
+    lens, news = [2050, 65, 4097, 300], [4, 1, 3, 2]
+    kv = _fp16_caches(7000 + H_q * 10 + H_kv, lens, H_kv)
+    dkv = [(dev(k, torch.float16), dev(v, torch.float16)) for k, v in kv]
+    views = [sd.seqview(k, v, L) for (k, v), L in zip(dkv, lens)]
+    q = synth.queries(synth.rng(7100 + H_q), sum(news), H_q, D)
+    o = host(sd.decode_attn_verify(dev(q), views, news, H_kv, SCALE))
+    _check_parity(o, oracle.attn_verify(q, kv, lens, news, SCALE))
+    # each burst token: a one-token call over its own prefix
+    r = 0
+    for s, (L, n) in enumerate(zip(lens, news)):
+        for i in range(n):
+            p = L - n + i
+            one = host(sd.decode_attn_multiseq(dev(q[r][None]), [sd.seqview(dkv[s][0], dkv[s][1], p + 1)],
+                                               H_kv, SCALE))[0]
+            assert np.array_equal(bits(o[r]), bits(one)), (s, i)
+            r += 1
+    # one token per sequence: batched == alone == the allocation-free entry point
+    q1 = synth.queries(synth.rng(7200 + H_q), len(lens), H_q, D)
+    ob = host(sd.decode_attn_multiseq(dev(q1), views, H_kv, SCALE))
+    _check_parity(ob, oracle.attn_decode_multiseq(q1, kv, lens, SCALE))
+    on = host(sd.decode_attn_multiseq_noalloc(dev(q1), views, H_kv, SCALE))
+    assert np.array_equal(bits(ob), bits(on))
+    for s in range(len(lens)):
+        solo = host(sd.decode_attn_multiseq(dev(q1[s][None]), [views[s]], H_kv, SCALE))[0]
+        assert np.array_equal(bits(ob[s]), bits(solo)), s
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(16, 8), (32, 4)])
+def test_groups_q8_parity(sd, H_q, H_kv):
+    import torch
+    say(f"q8 attention head groups H_q={H_q} H_kv={H_kv}")
+    lens, news = [2051, 700, 17], [2, 4, 1]
+    g = synth.rng(7300 + H_q)
+    caches, views, keep = [], [], []
+    for L in lens:
+        kq, kd = synth.kv_cache_q8(g, L, H_kv, D)
+        vq, vd = synth.kv_cache_q8(g, L, H_kv, D)
+        caches.append((kq, kd, vq, vd))
+        t = [dev(kq), dev(kd, torch.float16), dev(vq), dev(vd, torch.float16)]
+        keep += t
+        views.append(sd.seqview_q8(t[0], t[1], t[2], t[3], L))
+    q = synth.queries(synth.rng(7400 + H_q), sum(news), H_q, D)
+    o = host(sd.decode_attn_verify(dev(q), views, news, H_kv, SCALE))
+    _check_parity(o, oracle.attn_verify(q, caches, lens, news, SCALE))
+
+
+def test_groups_of_four_unchanged(sd):
+    """G = 4 keeps one head group per KV head: a 32/8 call equals the same call
+    split into its four 8/2 quarters (heads 8k .. 8k+7 over KV heads 2k, 2k+1)."""
+    import torch
+    say("attention G=4 quarters")
+    lens = [2050, 3000]
+    kv = _fp16_caches(7500, lens, 8)
+    dkv = [(dev(k, torch.float16), dev(v, torch.float16)) for k, v in kv]
+    views = [sd.seqview(k, v, L) for (k, v), L in zip(dkv, lens)]
+    q = synth.queries(synth.rng(7501), len(lens), 32, D)
+    full = host(sd.decode_attn_multiseq(dev(q), views, 8, SCALE))
+    for k in range(4):
+        sub = [(dev(np.ascontiguousarray(c[0][:, 2 * k:2 * k + 2]), torch.float16),
+                dev(np.ascontiguousarray(c[1][:, 2 * k:2 * k + 2]), torch.float16)) for c in kv]
+        sv = [sd.seqview(a, b, L) for (a, b), L in zip(sub, lens)]
+        part = host(sd.decode_attn_multiseq(dev(np.ascontiguousarray(q[:, 8 * k:8 * k + 8])), sv, 2, SCALE))
+        assert np.array_equal(bits(part), bits(full[:, 8 * k:8 * k + 8])), k

@@ -4,9 +4,10 @@ A workgroup takes a head group: hpw query heads of one KV head, hpw the largest
 divisor of G = H_q / H_kv up to 4 (G = 1, 2, 3, 4 take one group per KV head;
 G = 5, 6, 8 take 5, 2, 2 groups, each reading the KV head's keys and values).
 Against the oracle (2e-3 absolute, 1e-4 normwise) on ragged contexts with
-verify bursts, fp16 and q8_0 caches; bitwise: burst tokens equal one-token
-calls over their prefixes, a sequence alone equals it inside the batch, and
-the allocation-free entry point equals the workspace one.
+verify bursts, fp16, q8_0 and mixed q4_0/q8_0 caches and windows; bitwise:
+burst tokens equal one-token calls over their prefixes, a sequence alone
+equals it inside the batch, the allocation-free entry point equals the
+workspace one, and ring and paged storage equal plain storage.
 """
 import numpy as np
 import pytest
@@ -100,3 +101,95 @@ def test_groups_of_four_unchanged(sd):
         sv = [sd.seqview(a, b, L) for (a, b), L in zip(sub, lens)]
         part = host(sd.decode_attn_multiseq(dev(np.ascontiguousarray(q[:, 8 * k:8 * k + 8])), sv, 2, SCALE))
         assert np.array_equal(bits(part), bits(full[:, 8 * k:8 * k + 8])), k
+
+
+def _ring_of(k, v, ctx, cap):
+    """The last `cap` positions of a plain cache, stored at row j % cap."""
+    rk, rv = np.zeros((cap,) + k.shape[1:], k.dtype), np.zeros((cap,) + v.shape[1:], v.dtype)
+    for j in range(max(0, ctx - cap), ctx):
+        rk[j % cap], rv[j % cap] = k[j], v[j]
+    return rk, rv
+
+
+def _pool_of(kvs, lens, bs, H_kv, seed, spare=3):
+    """Every sequence's positions in blocks of bs rows at shuffled places of
+    one pool, noise in the spare blocks.  Returns (pool_k, pool_v, tables)."""
+    g = synth.rng(seed)
+    nb = [(L + bs - 1) // bs for L in lens]
+    n_pool = sum(nb) + spare
+    place = g.permutation(n_pool)
+    pk = synth.kv_cache(g, n_pool * bs, H_kv, D)
+    pv = synth.kv_cache(g, n_pool * bs, H_kv, D)
+    tables, nxt = [], 0
+    for (k, v), L, n in zip(kvs, lens, nb):
+        tab = place[nxt:nxt + n].astype(np.int32)
+        nxt += n
+        for j in range(L):
+            r = tab[j // bs] * bs + j % bs
+            pk[r], pv[r] = k[j], v[j]
+        tables.append(tab)
+    return pk, pv, tables
+
+
+def _verify(sd, q, views, news, H_kv):
+    return host(sd.decode_attn_verify(dev(q), views, news, H_kv, SCALE))
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(8, 8), (16, 8), (24, 4)])  # G = 1, 2, 6
+def test_groups_window_ring_paged(sd, H_q, H_kv):
+    """Head groups over windowed, ring and paged storage: windowed parity with
+    the oracle, ring == plain and paged == plain bitwise."""
+    import torch
+    say(f"head groups window/ring/paged H_q={H_q} H_kv={H_kv}")
+    lens, news, window, bs = [3000, 700, 4100, 300], [4, 1, 2, 3], 257, 64
+    g = synth.rng(7600 + H_q + H_kv)
+    kvs = [(synth.kv_cache(g, L, H_kv, D), synth.kv_cache(g, L, H_kv, D)) for L in lens]
+    q = synth.queries(synth.rng(7700 + H_q), sum(news), H_q, D)
+    keep = [(dev(k, torch.float16), dev(v, torch.float16)) for k, v in kvs]
+    plain_w = _verify(sd, q, [sd.seqview(k, v, L, window=window) for (k, v), L in zip(keep, lens)], news, H_kv)
+    _check_parity(plain_w, oracle.attn_verify(q, kvs, lens, news, SCALE, window=window))
+    caps = [min(L, window + T - 1) + 5 for L, T in zip(lens, news)]
+    rings = [_ring_of(k, v, L, cap) for (k, v), L, cap in zip(kvs, lens, caps)]
+    rdev = [(dev(k, torch.float16), dev(v, torch.float16)) for k, v in rings]
+    ring_w = _verify(sd, q, [sd.seqview(k, v, L, window=window, ring=True) for (k, v), L in zip(rdev, lens)],
+                     news, H_kv)
+    assert np.array_equal(bits(ring_w), bits(plain_w))
+    plain = _verify(sd, q, [sd.seqview(k, v, L) for (k, v), L in zip(keep, lens)], news, H_kv)
+    pk, pv, tabs = _pool_of(kvs, lens, bs, H_kv, 7800 + H_q)
+    dpk, dpv = dev(pk, torch.float16), dev(pv, torch.float16)
+    dt = [dev(t) for t in tabs]
+    paged = _verify(sd, q, [sd.seqview(dpk, dpv, L, block_table=t, block_size=bs) for t, L in zip(dt, lens)],
+                    news, H_kv)
+    assert np.array_equal(bits(paged), bits(plain))
+    _check_parity(plain, oracle.attn_verify(q, kvs, lens, news, SCALE))
+
+
+@pytest.mark.parametrize("kt,vt", [("q4_0", "q8_0"), ("q8_0", "q4_0")])
+@pytest.mark.parametrize("H_q,H_kv", [(16, 8), (32, 4)])  # G = 2, 8
+def test_groups_mixed_quant_parity_and_prefix(sd, H_q, H_kv, kt, vt):
+    """Head groups over the mixed q4_0 / q8_0 caches: parity with the oracle over
+    the dequantized caches, and each burst token equal to a one-token call."""
+    import torch
+    say(f"head groups {kt}/{vt} H_q={H_q} H_kv={H_kv}")
+    lens, news = [2051, 700, 17], [3, 4, 1]
+    g = synth.rng(7900 + H_q + H_kv)
+    half = lambda n, ty: synth.kv_cache_q4(g, n, H_kv, D) if ty == "q4_0" else synth.kv_cache_q8(g, n, H_kv, D)
+    caches, views, keep = [], [], []
+    for L in lens:
+        kq, kd = half(L, kt)
+        vq, vd = half(L, vt)
+        caches.append((kq, kd, vq, vd))
+        t = [dev(kq), dev(kd, torch.float16), dev(vq), dev(vd, torch.float16)]
+        keep.append(t)
+        views.append(sd.seqview_quant(t[0], t[1], t[2], t[3], L, kt, vt))
+    q = synth.queries(synth.rng(7950 + H_q), sum(news), H_q, D)
+    o = _verify(sd, q, views, news, H_kv)
+    _check_parity(o, oracle.attn_verify(q, caches, lens, news, SCALE))
+    r = 0
+    for s, (L, T) in enumerate(zip(lens, news)):
+        t = keep[s]
+        for i in range(T):
+            v1 = sd.seqview_quant(t[0], t[1], t[2], t[3], L - T + i + 1, kt, vt)
+            one = _verify(sd, q[r:r + 1], [v1], [1], H_kv)
+            assert np.array_equal(bits(one[0]), bits(o[r])), (s, i)
+            r += 1

@@ -6,9 +6,13 @@
  * without synchronizing.  Pointers are DEVICE pointers unless marked [host].
  * The caller owns every buffer; the library allocates no device memory and
  * keeps no device state between calls, so concurrent calls on different
- * streams are independent.  Its only process state is each kernel's raised
- * LDS limit, set once on a kernel's first launch under std::call_once (safe
- * when several host threads make their first calls at once).
+ * streams are independent.  The one exception is
+ * sd_decode_attn_multiseq_noalloc, whose partials live in a file-scope device
+ * array that every call on a GPU shares (calls of it that overlap on one GPU
+ * race).  Its only process state is each kernel's raised LDS limit, set once on
+ * a kernel's first launch under std::call_once (safe when several host threads
+ * make their first calls at once), and that array's device address, looked up
+ * once per device the same way.
  *
  * Errors: arguments are validated on the host before any HIP call.  On failure
  * a negative sd_status is returned, nothing is launched and no output is

@@ -193,3 +193,27 @@ def test_groups_mixed_quant_parity_and_prefix(sd, H_q, H_kv, kt, vt):
             one = _verify(sd, q[r:r + 1], [v1], [1], H_kv)
             assert np.array_equal(bits(one[0]), bits(o[r])), (s, i)
             r += 1
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(16, 8), (32, 4), (12, 4)])  # G = 2, 8, 3
+def test_groups_batch_order(sd, H_q, H_kv):
+    """The same sequences in reversed order give the same rows, bit for bit
+    (one-token and verify calls)."""
+    import torch
+    say(f"head groups batch order H_q={H_q} H_kv={H_kv}")
+    lens, news = [2050, 65, 4097, 300], [4, 1, 3, 2]
+    kv = _fp16_caches(8100 + H_q + H_kv, lens, H_kv)
+    dkv = [(dev(k, torch.float16), dev(v, torch.float16)) for k, v in kv]
+    views = [sd.seqview(k, v, L) for (k, v), L in zip(dkv, lens)]
+    rev = views[::-1]
+    q1 = synth.queries(synth.rng(8200 + H_q), len(lens), H_q, D)
+    a = host(sd.decode_attn_multiseq(dev(q1), views, H_kv, SCALE))
+    b = host(sd.decode_attn_multiseq(dev(np.ascontiguousarray(q1[::-1])), rev, H_kv, SCALE))
+    assert np.array_equal(bits(a), bits(b[::-1]))
+    q = synth.queries(synth.rng(8300 + H_q), sum(news), H_q, D)
+    starts = np.cumsum([0] + news[:-1])
+    qr = np.concatenate([q[s:s + n] for s, n in zip(starts[::-1], news[::-1])])
+    o = host(sd.decode_attn_verify(dev(q), views, news, H_kv, SCALE))
+    orv = host(sd.decode_attn_verify(dev(qr), rev, news[::-1], H_kv, SCALE))
+    back = np.concatenate([orv[s:s + n] for s, n in zip(np.cumsum([0] + news[::-1][:-1])[::-1], news)])
+    assert np.array_equal(bits(o), bits(back))
